@@ -1,0 +1,220 @@
+"""Benchmark of the fp8 MoE hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config 2] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic input,
+all inputs resident in HBM: quantize the tokens, sort/gather them by expert,
+the grouped matmuls (gate, up, SiLU*mul requantize, down), and the weighted
+gather-reduce -- the gated MoE FFN forward with T=4096 tokens, H=2048,
+E=64 experts, top-8, I=768 (config 2).  Prints one JSON line:
+
+  value      whole-step throughput: algorithmic GMM flops of a step / step time
+  roofline   for the dominant kernel (the grouped matmul): algorithmic bytes of
+             its launches / their HIP-event durations against 8 TB/s HBM (its
+             shapes sit below the fp8 ridge, 5.0 PFLOP/s / 8 TB/s = 629 flop/B)
+  kernels    per-kernel average durations, GB/s and TFLOP/s of every step stage
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+
+Per-kernel durations come from torch.cuda events recorded around each call
+on the stream the kernels run on (torch's current stream).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp8 MoE GMM TFLOP/s (% fp8 MFMA peak) + sort/gather HBM GB/s, 1×MI355X"
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 MFMA, MI355X
+PEAK_HBM_GBPS = 8000.0        # HBM3E
+
+
+def step_accounting(path, n, U):
+    """Algorithmic bytes / flops of each call of one step (per launch)."""
+    cfg = path.cfg
+    T, H, k, E, I = cfg.T, cfg.H, cfg.k, cfg.E, cfg.I
+    M_cap = path.m_cap
+    acc = {}
+    acc["quantize"] = {"bytes": (T // path.share) * H * 3 + (T // path.share) * 4, "flops": 0}
+    acc["sort"] = {"bytes": T * k * 4 + 2 * T * k * 4 + E * 4 + U * H + n * H + 8 * n, "flops": 0}
+    gm = []
+    nonempty = int(path.nonempty_local)
+    for name in (["wi_0", "wi_1", "wo"] if cfg.pipeline == "ffn" else ["w_up"]):
+        w = path.w[name]
+        K, N = w.K, w.N
+        by = n * K + nonempty * K * N + n * N * 2 + (M_cap - n) * N * 2 + n * 4 + nonempty * w.kb * w.nb * 4
+        gm.append({"name": name, "bytes": by, "flops": 2 * n * K * N})
+    acc["gmm"] = gm
+    if cfg.pipeline == "ffn":
+        acc["silu_quant"] = {"bytes": M_cap * I * 5 + M_cap * 4, "flops": 0}
+    N_out = path.N_out
+    acc["gather_reduce"] = {"bytes": n * N_out * 2 + T * N_out * 2 + T * k * 8, "flops": 0}
+    return acc
+
+
+def run_gpu(cfg_id, steps, warmup):
+    import moe_fp8_grouped_amd as m
+    from moe_fp8_grouped_amd.pipeline import ForwardPath
+    from workloads import CONFIGS, generate, m_cap_for
+
+    m.load_library()
+    cfg = CONFIGS[cfg_id]
+    data = generate(cfg)
+    ids = data["ids"]
+    local = (ids >= cfg.group_offset) & (ids < cfg.group_offset + cfg.E_loc)
+    n = int(local.sum())
+    U = int(local.any(axis=1).sum())
+    share = 8 if cfg.E_loc < cfg.E else 1
+    path = ForwardPath(cfg, data, m_cap=m_cap_for(cfg, n), share=share)
+    gs = np.bincount(ids.ravel(), minlength=cfg.E)[cfg.group_offset:cfg.group_offset + cfg.E_loc]
+    path.nonempty_local = int((gs > 0).sum())
+    del data
+    acc = step_accounting(path, n, U)
+
+    names = ["quantize", "sort"] + [f"gmm_{g['name']}" for g in acc["gmm"]] + \
+        (["silu_quant"] if cfg.pipeline == "ffn" else []) + ["gather_reduce"]
+    ev = {nm: [] for nm in names}
+
+    def timed(nm, fn, record):
+        if record:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[nm].append((a, b))
+        else:
+            fn()
+
+    def one_step(record):
+        timed("quantize", path.quantize, record)
+        timed("sort", path.sort, record)
+        ls = path.ss if path.act_mode == m.MOE_SCALE_ROW_DYNAMIC else path.xscale
+        if cfg.pipeline == "up":
+            timed("gmm_w_up", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["w_up"], path.y), record)
+        else:
+            timed("gmm_wi_0", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_0"], path.a), record)
+            timed("gmm_wi_1", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_1"], path.b), record)
+            timed("silu_quant", lambda: m.moe_quantize_rows(path.a, path.b, m.MOE_ACT_SILU_MUL, path.m_cap, cfg.I,
+                                                            m.MOE_SCALE_ROW_DYNAMIC, 0.0, path.hq, path.hs, None, None),
+                  record)
+            timed("gmm_wo", lambda: path.gmm(path.hq, path.hs, m.MOE_SCALE_ROW_DYNAMIC, path.w["wo"], path.y), record)
+        timed("gather_reduce", path.combine, record)
+
+    for _ in range(warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+
+    kern = {}
+    for nm in names:
+        durs = [a.elapsed_time(b) for a, b in ev[nm]]
+        avg_ms = float(np.mean(durs))
+        if nm.startswith("gmm_"):
+            info = next(g for g in acc["gmm"] if "gmm_" + g["name"] == nm)
+        else:
+            info = acc[nm]
+        kern[nm] = {"avg_us": round(avg_ms * 1e3, 2), "min_us": round(float(np.min(durs)) * 1e3, 2),
+                    "alg_bytes": int(info["bytes"]), "GB_s": round(info["bytes"] / (avg_ms * 1e-3) / 1e9, 1)}
+        if info["flops"]:
+            tf = info["flops"] / (avg_ms * 1e-3) / 1e12
+            kern[nm]["alg_flops"] = int(info["flops"])
+            kern[nm]["TFLOP_s"] = round(tf, 1)
+            kern[nm]["frac_fp8_peak"] = round(tf / PEAK_FP8_TFLOPS, 4)
+    gmm_names = [nm for nm in names if nm.startswith("gmm_")]
+    gmm_flops = sum(g["flops"] for g in acc["gmm"])
+    gmm_bytes = sum(g["bytes"] for g in acc["gmm"])
+    gmm_us = sum(kern[nm]["avg_us"] for nm in gmm_names)
+    achieved_gbps = gmm_bytes / (gmm_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+            "kernel": "moe_gmm_fp8 (gmm_kernel)",
+            "alg_intensity_flop_per_byte": round(gmm_flops / gmm_bytes, 1),
+            "mfma_TFLOP_s": round(gmm_flops / (gmm_us * 1e-6) / 1e12, 1),
+            "mfma_frac_fp8_peak": round(gmm_flops / (gmm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+    if gmm_flops / gmm_bytes > PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        tf = gmm_flops / (gmm_us * 1e-6) / 1e12
+        roof.update({"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4)})
+    sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "gather_reduce")}
+    value = gmm_flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3fn x fp8_e4m3fn -> f32 accumulate",
+        "data": "synthetic (seeded; random-init weights)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.k} I={cfg.I}"
+                               + (f" local experts {cfg.group_offset}..{cfg.group_offset + cfg.E_loc - 1}"
+                                  if cfg.E_loc < cfg.E else ""),
+                   "routed_local_rows": n, "m_cap": path.m_cap, "gmm_flops_per_step": gmm_flops},
+        "frac_fp8_peak_whole_step": round(value / PEAK_FP8_TFLOPS, 4),
+        "sort_gather_GB_s": sort_gather,
+        "roofline": roof,
+        "kernels": kern,
+        "device": torch.cuda.get_device_name(0),
+    }
+    return res, cfg
+
+
+def cpu_baseline(cfg, tokens=2048):
+    """The oracle's forward pipeline on the first ``tokens`` tokens."""
+    from threadpoolctl import threadpool_info
+    from oracle.pipeline import forward_pipeline, quantize_config_weights
+    from workloads import generate
+
+    data = generate(cfg)
+    sub = dict(data)
+    sub["x"] = data["x"][:tokens]
+    sub["ids"] = data["ids"][:tokens]
+    sub["topk_w"] = data["topk_w"][:tokens]
+    import dataclasses
+    scfg = dataclasses.replace(cfg, T=tokens)
+    qw = quantize_config_weights(scfg, data["weights"])      # weights are pre-quantized on both sides
+    t0 = time.perf_counter()
+    st = forward_pipeline(scfg, sub, qw)
+    t1 = time.perf_counter()
+    n = int(st["sort"]["n"])
+    flops = sum(2 * n * w.shape[1] * w.shape[2] for w in data["weights"].values())
+    blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": round(flops / (t1 - t0) / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {tokens} of {cfg.T} tokens ({n} routed rows): the whole forward step "
+                      f"(quantize, sort, gmm x3, SiLU requantize, gather-reduce) on pre-quantized weights, "
+                      f"{t1 - t0:.1f} s, numpy float64",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {a.gpus}); expert parallelism is modelled "
+              f"as one GPU's expert slice", file=sys.stderr)
+        sys.exit(2)
+    res, cfg = run_gpu(a.config, a.steps, a.warmup)
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, a.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

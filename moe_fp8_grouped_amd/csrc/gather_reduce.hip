@@ -1,0 +1,92 @@
+// moe_gather_reduce: un-sort plus top-k weighted combine ("Quantize
+// activations before EP all gather", review comments on
+// ragged_gather_reduce_v2.py: reduce the sorted expert outputs back to token
+// rows over the valid rows; bf16 output when the dtype is unset or fp8).
+//
+// One wave per token row: the lanes read the token's k slot entries
+// (inverse position, router weight), then sweep the row in 16-byte chunks,
+// loading the k expert-output rows and accumulating in float32 in slot order.
+// HBM-bound: reads n*N*2 (each sorted row once) + T*k*8, writes T*N*2 bytes.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+template <int YBF16, int OBF16>
+__global__ __launch_bounds__(256) void gather_reduce_kernel(const void* __restrict__ y, const int32_t* __restrict__ inv,
+                                                            const float* __restrict__ wts, int64_t T, int k,
+                                                            int64_t N, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int my_r = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_r = inv[t * k + lane];
+    my_w = wts[t * k + lane];
+  }
+  const uint64_t m = __ballot(my_r >= 0);
+  const int64_t chunks = N >> 3;            // 8 elements per chunk
+  for (int64_t ch = lane; ch < chunks; ch += 64) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < k; ++j) {            // slot order, uniform across the wave
+      if (!((m >> j) & 1ull)) continue;
+      const int r = __builtin_amdgcn_readlane(my_r, j);
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+      if (YBF16) {
+        const uint4 v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + static_cast<int64_t>(r) * N)[ch];
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj, __uint_as_float(wv[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj, __uint_as_float(wv[i] & 0xffff0000u), acc[2 * i + 1]);
+        }
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + static_cast<int64_t>(r) * N) + 2 * ch;
+        const float4 a = p[0], b = p[1];
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+      }
+    }
+    if (OBF16) {
+      uint4 o;
+      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * N)[ch] = o;
+    } else {
+      float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + t * N) + 2 * ch;
+      p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_gather_reduce(const void* y, int y_dtype, const int32_t* inv_pos, const float* topk_weights,
+                                 int64_t T, int32_t k, int64_t N, int out_dtype, void* out, void* stream) {
+  if (T < 0 || k <= 0 || k > 64 || N <= 0 || N % 8) return MOE_ERR_SHAPE;
+  if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (out_dtype == MOE_DTYPE_DEFAULT || out_dtype == MOE_E4M3FN) out_dtype = MOE_BF16;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y || !inv_pos || !topk_weights || !out) return MOE_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(moe_cdiv(T, 4))), block(256);
+  if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
+    moe::gather_reduce_kernel<1, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+  else if (y_dtype == MOE_BF16)
+    moe::gather_reduce_kernel<1, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+  else if (out_dtype == MOE_BF16)
+    moe::gather_reduce_kernel<0, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+  else
+    moe::gather_reduce_kernel<0, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

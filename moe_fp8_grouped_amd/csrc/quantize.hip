@@ -1,0 +1,250 @@
+// moe_quantize_rows: absmax quantization of bf16 activations to e4m3fn.
+//
+// Per-token dynamic absmax ("Quantize activations before EP all gather",
+// description: quantize before the all-gather and the sort) and the fixed
+// activation scale of fp8_static_wa ("Support quantization for tokamax gmm
+// v2", tolerance discussion).  HBM-bound: 2 bytes read, 1 byte written per
+// element (3 for the SiLU*mul variant), plus 4 bytes per row.
+//
+// Layout: one wave per row.  A lane owns 16-byte chunks (8 bf16) at chunk
+// indices lane, lane + 64, ...; with CPL chunks per lane a row of up to
+// CPL * 512 elements stays in registers between the absmax pass and the
+// quantize pass, so each input byte is read once.  Longer rows use the
+// streaming variant (CPL = 0), which reads the row twice (the second time
+// from L2).
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+struct Bf16x8 {
+  uint4 raw;
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = (&raw.x)[i >> 1];
+    return (i & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+
+template <int ACT>
+__device__ __forceinline__ void load_vals(const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu,
+                                          int64_t off, float v[8]) {
+  Bf16x8 a;
+  a.raw = *reinterpret_cast<const uint4*>(x + off);
+  if constexpr (ACT == MOE_ACT_SILU_MUL) {
+    Bf16x8 b;
+    b.raw = *reinterpret_cast<const uint4*>(xu + off);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = silu_mul(a.get(i), b.get(i));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = a.get(i);
+  }
+}
+
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t off, const float v[8], float s) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= quantize_one(v[i], s) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= quantize_one(v[4 + i], s) << (8 * i);
+  *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ float scale_from_amax(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+// MODE_ROW: compute each row's scale; MODE_GIVEN: use *given_scale (tensor
+// modes; computed by the first pass for the dynamic one).
+constexpr int MODE_ROW = 0;
+constexpr int MODE_GIVEN = 1;
+
+template <int CPL, int ACT, int MODE>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu, int64_t R, int64_t C,
+    const float* __restrict__ given_scale, uint8_t* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ row_amax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;
+  const int64_t nchunks = C >> 3;
+  const int64_t base = row * C;
+  float amax = 0.0f;
+  if constexpr (CPL > 0) {
+    float v[CPL][8];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int64_t ch = lane + 64 * c;
+      if (ch < nchunks) {
+        load_vals<ACT>(x, xu, base + ch * 8, v[c]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+      }
+    }
+    amax = wave_max(amax);
+    const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int64_t ch = lane + 64 * c;
+      if (ch < nchunks) store_codes(q, base + ch * 8, v[c], s);
+    }
+    if (lane == 0) {
+      if (MODE == MODE_ROW) scale[row] = s;
+      if (row_amax) row_amax[row] = amax;
+    }
+  } else {
+    for (int64_t ch = lane; ch < nchunks; ch += 64) {
+      float v[8];
+      load_vals<ACT>(x, xu, base + ch * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = wave_max(amax);
+    const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
+    for (int64_t ch = lane; ch < nchunks; ch += 64) {
+      float v[8];
+      load_vals<ACT>(x, xu, base + ch * 8, v);
+      store_codes(q, base + ch * 8, v, s);
+    }
+    if (lane == 0) {
+      if (MODE == MODE_ROW) scale[row] = s;
+      if (row_amax) row_amax[row] = amax;
+    }
+  }
+}
+
+// First pass of the tensor-dynamic mode: each block reduces the absmax of a
+// grid-strided set of rows into partial[blockIdx.x] (no atomics, so the
+// result does not depend on scheduling; max is exact in any order).
+template <int ACT>
+__global__ __launch_bounds__(256) void tensor_amax_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ xu, int64_t R,
+                                                          int64_t C, float* __restrict__ partial,
+                                                          float* __restrict__ row_amax) {
+  __shared__ float red[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t nchunks = C >> 3;
+  float bmax = 0.0f;
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + w; row < R; row += static_cast<int64_t>(gridDim.x) * 4) {
+    float amax = 0.0f;
+    for (int64_t ch = lane; ch < nchunks; ch += 64) {
+      float v[8];
+      load_vals<ACT>(x, xu, row * C + ch * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0 && row_amax) row_amax[row] = amax;
+    bmax = fmaxf(bmax, amax);
+  }
+  if (lane == 0) red[w] = bmax;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Reduce the per-block partial maxima to the tensor scale.
+__global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restrict__ partial, int n,
+                                                           float* __restrict__ scale) {
+  __shared__ float red[4];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, partial[i]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) *scale = scale_from_amax(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+}
+
+__global__ void fill_scale_kernel(float* scale, float v) { *scale = v; }
+
+template <int ACT, int MODE>
+hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, const float* given,
+                       uint8_t* q, float* scale, float* row_amax, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(moe_cdiv(R, 4))), block(256);
+  const int64_t chunks_per_lane = moe_cdiv(C / 8, 64);
+  // Keep the row in registers when it fits (the SiLU variant holds float32).
+  const int max_cpl = (ACT == MOE_ACT_SILU_MUL) ? 8 : 16;
+  if (chunks_per_lane <= 1)
+    quantize_rows_kernel<1, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+  else if (chunks_per_lane <= 2)
+    quantize_rows_kernel<2, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+  else if (chunks_per_lane <= 4)
+    quantize_rows_kernel<4, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+  else if (chunks_per_lane <= 8)
+    quantize_rows_kernel<8, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+  else if (chunks_per_lane <= max_cpl)
+    quantize_rows_kernel<(ACT == MOE_ACT_SILU_MUL ? 8 : 16), ACT, MODE>
+        <<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+  else
+    quantize_rows_kernel<0, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+  return hipGetLastError();
+}
+
+constexpr int kTensorBlocks = 1024;
+
+template <int ACT>
+int quantize_rows_impl(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, int mode,
+                       float static_scale, uint8_t* q, float* scale, float* row_amax, void* ws,
+                       hipStream_t st) {
+  if (mode == MOE_SCALE_ROW_DYNAMIC) {
+    if (R == 0) return MOE_OK;
+    return launch_rows<ACT, MODE_ROW>(x, xu, R, C, nullptr, q, scale, row_amax, st) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
+  }
+  if (mode == MOE_SCALE_TENSOR_STATIC) {
+    fill_scale_kernel<<<1, 1, 0, st>>>(scale, static_scale);
+    MOE_CHECK_LAUNCH();
+    if (R == 0) return MOE_OK;
+    return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, scale, q, scale, row_amax, st) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
+  }
+  // tensor dynamic: partial maxima in the workspace after the error word
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
+  const int nblk = static_cast<int>(R == 0 ? 1 : (moe_cdiv(R, 4) < kTensorBlocks ? moe_cdiv(R, 4) : kTensorBlocks));
+  if (R == 0) {
+    fill_scale_kernel<<<1, 1, 0, st>>>(scale, 1.0f);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
+  tensor_amax_kernel<ACT><<<nblk, 256, 0, st>>>(x, xu, R, C, partial, row_amax);
+  MOE_CHECK_LAUNCH();
+  tensor_scale_kernel<<<1, 256, 0, st>>>(partial, nblk, scale);
+  MOE_CHECK_LAUNCH();
+  return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, scale, q, scale, nullptr, st) == hipSuccess
+             ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+size_t quantize_rows_ws_bytes(int64_t R, int64_t C, int mode) {
+  (void)R; (void)C;
+  return mode == MOE_SCALE_TENSOR_DYNAMIC ? 256 + kTensorBlocks * sizeof(float) : 256;
+}
+
+}  // namespace moe
+
+extern "C" int moe_quantize_rows(const void* x, const void* x_up, int act, int64_t R, int64_t C,
+                                 int scale_mode, float static_scale, uint8_t* q, float* scale,
+                                 float* row_amax, void* ws, size_t ws_bytes, void* stream) {
+  if (R < 0 || C <= 0 || C % 16 != 0) return MOE_ERR_SHAPE;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_UNSUPPORTED;
+  if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
+      scale_mode != MOE_SCALE_TENSOR_STATIC)
+    return MOE_ERR_UNSUPPORTED;
+  if (scale_mode == MOE_SCALE_TENSOR_STATIC && !(static_scale > 0.0f && static_scale < 3.0e38f))
+    return MOE_ERR_SHAPE;
+  if (!scale || (R > 0 && (!x || !q))) return MOE_ERR_NULL;
+  if (act == MOE_ACT_SILU_MUL && R > 0 && !x_up) return MOE_ERR_NULL;
+  if (act == MOE_ACT_NONE && x_up) return MOE_ERR_UNSUPPORTED;
+  if (scale_mode == MOE_SCALE_TENSOR_DYNAMIC) {
+    if (!ws) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < moe::quantize_rows_ws_bytes(R, C, scale_mode)) return MOE_ERR_WORKSPACE;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* ub = static_cast<const uint16_t*>(x_up);
+  if (act == MOE_ACT_SILU_MUL)
+    return moe::quantize_rows_impl<MOE_ACT_SILU_MUL>(xb, ub, R, C, scale_mode, static_scale, q, scale,
+                                                     row_amax, ws, st);
+  return moe::quantize_rows_impl<MOE_ACT_NONE>(xb, nullptr, R, C, scale_mode, static_scale, q, scale,
+                                               row_amax, ws, st);
+}

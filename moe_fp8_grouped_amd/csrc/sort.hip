@@ -1,0 +1,276 @@
+// moe_sort_by_expert: stable ragged sort of the routed rows by expert and the
+// gather of the quantized token rows into that order ("Quantize activations
+// before EP all gather": review comments on ragged_sort.py -- fp8 rows are
+// gathered by the sorted token indices into this shard's window, the scale
+// follows only when it is per token).
+//
+// Four launches on the caller's stream:
+//  1. hist   one block per tile of 2048 routed slots: per-tile expert counts.
+//  2. scan   one block: per-expert exclusive scan over tiles, the expert
+//            bases, group_sizes, and this shard's window (start, n).
+//  3. rank   one block per tile: the stable rank of every slot inside its
+//            tile (a wave ranks 64 slots at a time: ballots over the bits of
+//            the expert id give each lane the set of lanes holding the same
+//            expert -- the warp-level multisplit of Ashkiani et al., 2016 --
+//            and a per-wave running count per expert in LDS carries the order
+//            across chunks); writes perm and inv_pos.
+//  4. scatter one wave per token: reads the token's fp8 row once and writes
+//            it to each of its local destinations; extra waves zero rows
+//            [n, M_cap).  Coalesced 16-byte loads and stores.
+// No float atomics and no order-dependent steps: the result is deterministic.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTile = 2048;          // routed slots per tile (256 threads x 8)
+constexpr int kHdr = 256;            // workspace header bytes
+// header int32 slots
+constexpr int kErr = 0, kStart = 1, kN = 2, kValid = 3;
+
+__device__ __forceinline__ int key_of(int32_t id, int E, int32_t* err) {
+  if (id < 0 || id >= E) {
+    raise_error(err, MOE_DEVERR_EXPERT_ID);
+    return E;                         // invalid ids form a bucket after every expert
+  }
+  return id;
+}
+
+__global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
+                                                        int32_t* __restrict__ hdr, int32_t* __restrict__ tile_hist) {
+  extern __shared__ int hist[];
+  for (int e = threadIdx.x; e <= E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
+#pragma unroll
+  for (int i = 0; i < kTile / 256; ++i) {
+    const int64_t f = base + i * 256 + threadIdx.x;
+    if (f < M) atomicAdd(&hist[key_of(ids[f], E, hdr + kErr)], 1);
+  }
+  __syncthreads();
+  int32_t* out = tile_hist + static_cast<int64_t>(blockIdx.x) * (E + 1);
+  for (int e = threadIdx.x; e <= E; e += 256) out[e] = hist[e];
+}
+
+// Exclusive prefix sum of a[0..n) in LDS by the first wave (n <= 1025).
+__device__ void wave0_exclusive_scan(int* a, int n) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int carry = 0;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + lane;
+    const int v = i < n ? a[i] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (i < n) a[i] = carry + incl - v;
+    carry += __shfl(incl, 63, 64);
+  }
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ tile_hist, int ntiles, int E,
+                                                         int g0, int El, int32_t* __restrict__ group_sizes,
+                                                         int32_t* __restrict__ hdr) {
+  extern __shared__ int tot[];        // [E + 1]
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    int run = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const int c = tile_hist[static_cast<int64_t>(t) * (E + 1) + e];
+      tile_hist[static_cast<int64_t>(t) * (E + 1) + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+    if (e < E) group_sizes[e] = run;
+  }
+  __syncthreads();
+  wave0_exclusive_scan(tot, E + 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+    const int b = tot[e];
+    for (int t = 0; t < ntiles; ++t) tile_hist[static_cast<int64_t>(t) * (E + 1) + e] += b;
+  }
+  if (threadIdx.x == 0) {
+    const int start = tot[g0];
+    hdr[kStart] = start;
+    hdr[kN] = tot[g0 + El] - start;
+    hdr[kValid] = tot[E];
+  }
+}
+
+__global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E, int nbits,
+                                                        int64_t M_cap, int32_t* __restrict__ hdr,
+                                                        const int32_t* __restrict__ tile_off,
+                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv_pos) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                      // [4][E + 1] running counts per wave
+  int* off = lds + 4 * (E + 1);        // [E + 1] global base of this tile
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    cnt[e] = cnt[(E + 1) + e] = cnt[2 * (E + 1) + e] = cnt[3 * (E + 1) + e] = 0;
+    off[e] = tile_off[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
+  }
+  __syncthreads();
+  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * kTile + w * (kTile / 4);
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  int keys[kTile / 256], rank[kTile / 256];
+  int* my = cnt + w * (E + 1);
+#pragma unroll
+  for (int c = 0; c < kTile / 256; ++c) {
+    const int64_t f = wbase + c * 64 + lane;
+    const bool valid = f < M;
+    const int key = valid ? key_of(ids[f], E, nullptr) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const int r = __popcll(peers & lt_mask);
+    int prior = 0;
+    if (valid) prior = my[key];
+    __builtin_amdgcn_wave_barrier();
+    if (valid && r == 0) my[key] = prior + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    keys[c] = valid ? key : -1;
+    rank[c] = prior + r;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    int s = 0;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const int t = cnt[ww * (E + 1) + e];
+      cnt[ww * (E + 1) + e] = s;
+      s += t;
+    }
+  }
+  __syncthreads();
+  const int start = hdr[kStart], n = hdr[kN];
+#pragma unroll
+  for (int c = 0; c < kTile / 256; ++c) {
+    const int key = keys[c];
+    if (key < 0) continue;
+    const int64_t f = wbase + c * 64 + lane;
+    const int pos = off[key] + my[key] + rank[c];
+    perm[pos] = static_cast<int32_t>(f);
+    int ip = -1;
+    if (key < E && pos >= start && pos < start + n) {
+      ip = pos - start;
+      if (ip >= M_cap) {
+        raise_error(hdr + kErr, MOE_DEVERR_ROWS);
+        ip = -1;
+      }
+    }
+    inv_pos[f] = ip;
+  }
+}
+
+// One wave per token row (grid-strided), then the zero tail of xs / ss.
+__global__ __launch_bounds__(256) void sort_scatter_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
+                                                           int row_scale, const int32_t* __restrict__ inv_pos, int64_t T,
+                                                           int k, int64_t H, int64_t M_cap,
+                                                           const int32_t* __restrict__ hdr, uint8_t* __restrict__ xs,
+                                                           float* __restrict__ ss) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t segs = H >> 4;
+  if (xq) {
+    for (int64_t t = wid; t < T; t += nw) {
+      int my_r = -1;
+      if (lane < k) my_r = inv_pos[t * k + lane];
+      if (my_r >= M_cap) my_r = -1;
+      if (my_r >= 0 && row_scale && ss) ss[my_r] = xscale[t];
+      uint64_t m = __ballot(my_r >= 0);
+      if (m == 0) continue;
+      const uint4* src = reinterpret_cast<const uint4*>(xq + t * H);
+      for (int64_t s = lane; s < segs; s += 64) {
+        const uint4 v = src[s];
+        uint64_t mm = m;
+        while (mm) {
+          const int j = __builtin_ctzll(mm);
+          mm &= mm - 1;
+          const int r = __builtin_amdgcn_readlane(my_r, j);
+          reinterpret_cast<uint4*>(xs + static_cast<int64_t>(r) * H)[s] = v;
+        }
+      }
+    }
+  } else if (row_scale && ss) {
+    for (int64_t t = wid; t < T; t += nw) {
+      if (lane < k) {
+        const int r = inv_pos[t * k + lane];
+        if (r >= 0 && r < M_cap) ss[r] = xscale[t];
+      }
+    }
+  }
+  int64_t n = hdr[kN];
+  if (n > M_cap) n = M_cap;
+  for (int64_t r = n + wid; r < M_cap; r += nw) {
+    if (xs) {
+      uint4* dst = reinterpret_cast<uint4*>(xs + r * H);
+      for (int64_t s = lane; s < segs; s += 64) dst[s] = make_uint4(0, 0, 0, 0);
+    }
+    if (ss && row_scale && lane == 0) ss[r] = 0.0f;
+  }
+}
+
+}  // namespace
+
+size_t sort_ws_bytes(int64_t M, int E) {
+  const int64_t ntiles = moe_cdiv(M, kTile);
+  return kHdr + static_cast<size_t>(moe_cdiv(ntiles * (E + 1) * 4, 256) * 256);
+}
+
+}  // namespace moe
+
+extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                                  int32_t group_offset, int32_t num_local_experts, const uint8_t* xq,
+                                  const float* xscale, int xscale_mode, int64_t H, int64_t M_cap,
+                                  int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs,
+                                  float* ss, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k <= 0 || k > 64 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
+  if (group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E) return MOE_ERR_SHAPE;
+  if (M_cap < 0 || T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (xscale_mode != MOE_SCALE_ROW_DYNAMIC && xscale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
+      xscale_mode != MOE_SCALE_TENSOR_STATIC)
+    return MOE_ERR_UNSUPPORTED;
+  if (xq && (H <= 0 || H % 16)) return MOE_ERR_SHAPE;
+  const int64_t M = T * k;
+  if (!group_sizes || !ws || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
+  if (xq && M_cap > 0 && !xs) return MOE_ERR_NULL;
+  const bool row_scale = xscale_mode == MOE_SCALE_ROW_DYNAMIC;
+  if (row_scale && xscale && M_cap > 0 && !ss) return MOE_ERR_NULL;
+  if (row_scale && ss && T > 0 && !xscale) return MOE_ERR_NULL;
+  if (ws_bytes < moe::sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* hdr = static_cast<int32_t*>(ws);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + moe::kHdr);
+  const int ntiles = static_cast<int>(moe_cdiv(M, moe::kTile));
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;
+  const size_t hist_lds = (E + 1) * sizeof(int);
+  if (ntiles > 0) {
+    moe::sort_hist_kernel<<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+    MOE_CHECK_LAUNCH();
+  }
+  moe::sort_scan_kernel<<<1, 1024, hist_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
+                                                    group_sizes, hdr);
+  MOE_CHECK_LAUNCH();
+  if (ntiles > 0) {
+    moe::sort_rank_kernel<<<ntiles, 256, 5 * hist_lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr, tile_hist,
+                                                             perm, inv_pos);
+    MOE_CHECK_LAUNCH();
+  }
+  if (xs || ss) {
+    int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
+    if (waves < 4) waves = 4;
+    if (waves > 65536) waves = 65536;
+    moe::sort_scatter_kernel<<<static_cast<unsigned>(moe_cdiv(waves, 4)), 256, 0, st>>>(
+        xq, xscale, row_scale ? 1 : 0, inv_pos, T, k, H, M_cap, hdr, xs, ss);
+    MOE_CHECK_LAUNCH();
+  }
+  return MOE_OK;
+}

@@ -1,0 +1,207 @@
+"""The hot path end to end on one GPU: device buffers plus the sequence of
+C-ABI calls for the three workload shapes (up-projection, gated FFN
+forward, backward).  Buffer management and call order only -- every
+arithmetic step runs in libmoefp8's kernels.
+
+Forward ("Quantize activations before EP all gather", description and
+review comments): quantize tokens -> sort/gather fp8 rows -> gmm(s) ->
+[SiLU*mul requantize -> gmm] -> weighted gather-reduce.  Backward
+("Support quantization for tokamax gmm v2", gmm2 / tgmm2): dX = gmm(dY,
+W^T) and dW = tgmm(X, dY).
+
+Expert parallelism is modelled as one GPU's slice: experts
+[group_offset, group_offset + num_local_experts) are local; the sorted
+buffers hold only their rows (compact window).  With ``share`` the step
+quantizes only this GPU's 1/share of the tokens into its slot of the
+token buffer; the other slots stand for what the all-gather would bring and
+are quantized once at setup.
+"""
+
+import numpy as np
+import torch
+
+from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_F32, MOE_OP_GMM, MOE_OP_QUANTIZE_ROWS,
+               MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
+               MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gmm_fp8, moe_quantize_rows,
+               moe_quantize_weights, moe_sort_by_expert, moe_tgmm_fp8, workspace)
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """bfloat16 bit patterns (uint16 numpy) -> bfloat16 device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class QuantizedWeight:
+    """An expert weight [E, K, N] quantized on the GPU with [E, kb, 1, nb]
+    scales; stored [E, N, K] when ``nk`` (contraction dim contiguous)."""
+
+    def __init__(self, w_bf16: torch.Tensor, kb: int, nb: int, static_scale=None, nk=True, stream=None):
+        E, K, N = w_bf16.shape
+        self.E, self.K, self.N, self.kb, self.nb, self.nk = E, K, N, kb, nb, nk
+        dev = w_bf16.device
+        self.q = torch.empty((E, N, K) if nk else (E, K, N), dtype=torch.uint8, device=dev)
+        self.scale = torch.empty((E, kb, 1, nb), dtype=torch.float32, device=dev)
+        mode = MOE_SCALE_TENSOR_STATIC if static_scale is not None else MOE_SCALE_ROW_DYNAMIC
+        moe_quantize_weights(w_bf16, E, K, N, kb, nb, mode, static_scale or 0.0, 1 if nk else 0, self.q,
+                             self.scale, stream=stream)
+
+
+class ForwardPath:
+    """Up-projection (``cfg.pipeline == 'up'``) or gated FFN forward."""
+
+    def __init__(self, cfg, data, device="cuda", static_act=None, static_weight=None, nk=True, m_cap=None,
+                 share=1, weights_dev=None):
+        self.cfg, self.dev = cfg, device
+        T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
+        self.T, self.H, self.k, self.E = T, H, k, E
+        self.g0, self.El = cfg.group_offset, cfg.E_loc
+        self.M = T * k
+        self.m_cap = self.M if m_cap is None else m_cap
+        self.act_mode = MOE_SCALE_TENSOR_STATIC if static_act is not None else MOE_SCALE_ROW_DYNAMIC
+        self.static_act = static_act or 0.0
+        self.share = share
+        self.x = bf16_tensor(data["x"], device)
+        self.ids = torch.from_numpy(np.ascontiguousarray(data["ids"], dtype=np.int32)).to(device)
+        self.topk_w = torch.from_numpy(np.ascontiguousarray(data["topk_w"], dtype=np.float32)).to(device)
+        # weights: quantized once on the GPU (setup, not part of a step)
+        self.w = {}
+        src = weights_dev if weights_dev is not None else {n: bf16_tensor(w, device) for n, w in data["weights"].items()}
+        for name, wt in src.items():
+            _, K, N = wt.shape
+            kb, nb = cfg.scale_blocks(K, N)
+            self.w[name] = QuantizedWeight(wt, kb, nb, static_scale=static_weight, nk=nk)
+        del src
+        N_out = cfg.I if cfg.pipeline == "up" else H
+        self.N_out = N_out
+        u8, f32, i32, bf = torch.uint8, torch.float32, torch.int32, torch.bfloat16
+        self.xq = torch.empty((T, H), dtype=u8, device=device)
+        self.xscale = torch.empty((T if self.act_mode == MOE_SCALE_ROW_DYNAMIC else 1,), dtype=f32, device=device)
+        self.perm = torch.empty(self.M, dtype=i32, device=device)
+        self.inv_pos = torch.empty(self.M, dtype=i32, device=device)
+        self.group_sizes = torch.empty(E, dtype=i32, device=device)
+        self.xs = torch.empty((self.m_cap, H), dtype=u8, device=device)
+        self.ss = torch.empty((self.m_cap,), dtype=f32, device=device)
+        if cfg.pipeline == "ffn":
+            self.a = torch.empty((self.m_cap, cfg.I), dtype=bf, device=device)
+            self.b = torch.empty((self.m_cap, cfg.I), dtype=bf, device=device)
+            self.hq = torch.empty((self.m_cap, cfg.I), dtype=u8, device=device)
+            self.hs = torch.empty((self.m_cap,), dtype=f32, device=device)
+        self.y = torch.empty((self.m_cap, N_out), dtype=bf, device=device)
+        self.out = torch.empty((T, N_out), dtype=bf, device=device)
+        self.ws_q = workspace(MOE_OP_QUANTIZE_ROWS, T, H, self.act_mode, device=device)
+        self.ws_sort = workspace(MOE_OP_SORT_BY_EXPERT, self.M, 0, 0, E, device=device)
+        self.ws_gmm = workspace(MOE_OP_GMM, self.m_cap, H, N_out, E, device=device)
+        if share > 1:
+            # slots of the other GPUs: quantized once, as the all-gather would deliver them
+            self._quantize(0, T)
+
+    # -- steps -------------------------------------------------------------
+    def _quantize(self, r0, rows):
+        H = self.H
+        xs = self.xscale[r0:r0 + rows] if self.act_mode == MOE_SCALE_ROW_DYNAMIC else self.xscale
+        moe_quantize_rows(self.x[r0:r0 + rows], None, MOE_ACT_NONE, rows, H, self.act_mode, self.static_act,
+                          self.xq[r0:r0 + rows], xs, None, self.ws_q)
+
+    def quantize(self):
+        rows = self.T // self.share
+        self._quantize(0, rows)        # this GPU's share sits in slot 0
+
+    def sort(self):
+        moe_sort_by_expert(self.ids, self.T, self.k, self.E, self.g0, self.El, self.xq, self.xscale,
+                           self.act_mode, self.H, self.m_cap, self.perm, self.inv_pos, self.group_sizes,
+                           self.xs, self.ss if self.act_mode == MOE_SCALE_ROW_DYNAMIC else None, self.ws_sort)
+
+    def gmm(self, lhs, lhs_scale, lhs_mode, w: QuantizedWeight, out, out_dtype=MOE_BF16):
+        moe_gmm_fp8(lhs, lhs_scale, lhs_mode, w.q, w.scale, w.kb, w.nb, 1 if w.nk else 0, self.group_sizes,
+                    self.E, self.g0, self.El, self.m_cap, w.K, w.N, out_dtype, out, self.ws_gmm)
+
+    def experts(self):
+        ls = self.ss if self.act_mode == MOE_SCALE_ROW_DYNAMIC else self.xscale
+        if self.cfg.pipeline == "up":
+            self.gmm(self.xs, ls, self.act_mode, self.w["w_up"], self.y)
+            return
+        self.gmm(self.xs, ls, self.act_mode, self.w["wi_0"], self.a)
+        self.gmm(self.xs, ls, self.act_mode, self.w["wi_1"], self.b)
+        moe_quantize_rows(self.a, self.b, MOE_ACT_SILU_MUL, self.m_cap, self.cfg.I, MOE_SCALE_ROW_DYNAMIC, 0.0,
+                          self.hq, self.hs, None, None)
+        self.gmm(self.hq, self.hs, MOE_SCALE_ROW_DYNAMIC, self.w["wo"], self.y)
+
+    def combine(self):
+        moe_gather_reduce(self.y, MOE_BF16, self.inv_pos, self.topk_w, self.T, self.k, self.N_out, MOE_BF16,
+                          self.out)
+
+    def step(self):
+        self.quantize()
+        self.sort()
+        self.experts()
+        self.combine()
+
+    # -- accounting ----------------------------------------------------------
+    def gmm_flops(self, n_local):
+        """Algorithmic GMM flops of one step for n_local routed local rows."""
+        return sum(2 * n_local * w.K * w.N for w in self.w.values())
+
+
+class BackwardPath:
+    """Config-5 backward: dX = gmm(dY, W^T), dW = tgmm(X_sorted, dY)."""
+
+    def __init__(self, cfg, data, static_act, static_weight, device="cuda", dw_dtype=MOE_F32):
+        self.cfg, self.dev = cfg, device
+        T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+        self.T, self.H, self.E, self.k, self.I = T, H, E, k, I
+        self.M = T * k
+        self.g0, self.El = cfg.group_offset, cfg.E_loc
+        self.static_act = static_act
+        u8, f32, i32, bf = torch.uint8, torch.float32, torch.int32, torch.bfloat16
+        self.x = bf16_tensor(data["x"], device)
+        self.ids = torch.from_numpy(np.ascontiguousarray(data["ids"], dtype=np.int32)).to(device)
+        self.dy = bf16_tensor(data["dy"], device)
+        w = bf16_tensor(data["weights"]["w_up"], device)
+        # W [E, H, I] is the forward up weight; for dX it is the rhs stored [E, N=H, K=I]
+        self.w = QuantizedWeight(w, 1, 1, static_scale=static_weight, nk=False)
+        del w
+        self.xq = torch.empty((T, H), dtype=u8, device=device)
+        self.xscale = torch.empty(1, dtype=f32, device=device)
+        self.perm = torch.empty(self.M, dtype=i32, device=device)
+        self.inv_pos = torch.empty(self.M, dtype=i32, device=device)
+        self.group_sizes = torch.empty(E, dtype=i32, device=device)
+        self.xs = torch.empty((self.M, H), dtype=u8, device=device)
+        self.dyq_r = torch.empty((self.M, I), dtype=u8, device=device)
+        self.dys_r = torch.empty(self.M, dtype=f32, device=device)
+        self.dyq_t = torch.empty((self.M, I), dtype=u8, device=device)
+        self.dys_t = torch.empty(1, dtype=f32, device=device)
+        self.dx = torch.empty((self.M, H), dtype=bf, device=device)
+        self.dw_dtype = dw_dtype
+        self.dw = torch.empty((self.El, H, I), dtype=f32 if dw_dtype == MOE_F32 else bf, device=device)
+        self.ws_q = workspace(MOE_OP_QUANTIZE_ROWS, self.M, I, MOE_SCALE_TENSOR_DYNAMIC, device=device)
+        self.ws_sort = workspace(MOE_OP_SORT_BY_EXPERT, self.M, 0, 0, E, device=device)
+        self.ws_gmm = workspace(MOE_OP_GMM, self.M, I, H, E, device=device)
+        self.ws_tgmm = workspace(MOE_OP_TGMM, self.M, H, I, E, device=device)
+
+    def quantize_and_sort(self):
+        moe_quantize_rows(self.x, None, MOE_ACT_NONE, self.T, self.H, MOE_SCALE_TENSOR_STATIC, self.static_act,
+                          self.xq, self.xscale, None, None)
+        moe_sort_by_expert(self.ids, self.T, self.k, self.E, self.g0, self.El, self.xq, self.xscale,
+                           MOE_SCALE_TENSOR_STATIC, self.H, self.M, self.perm, self.inv_pos, self.group_sizes,
+                           self.xs, None, self.ws_sort)
+
+    def quantize_dy(self):
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, self.M, self.I, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r,
+                          self.dys_r, None, None)
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, self.M, self.I, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.dyq_t,
+                          self.dys_t, None, self.ws_q)
+
+    def grad_input(self):
+        moe_gmm_fp8(self.dyq_r, self.dys_r, MOE_SCALE_ROW_DYNAMIC, self.w.q, self.w.scale, 1, 1, 1,
+                    self.group_sizes, self.E, self.g0, self.El, self.M, self.I, self.H, MOE_BF16, self.dx,
+                    self.ws_gmm)
+
+    def grad_weight(self):
+        moe_tgmm_fp8(self.xs, self.xscale, 1, self.dyq_t, self.dys_t, 1, self.group_sizes, self.E, self.g0,
+                     self.El, self.M, self.H, self.I, self.dw_dtype, self.dw, self.ws_tgmm)
+
+    def step(self):
+        self.quantize_and_sort()
+        self.quantize_dy()
+        self.grad_input()
+        self.grad_weight()

@@ -1,0 +1,198 @@
+"""Match rules between the HIP path and the oracle, and numpy <-> device
+helpers for the GPU parity tests.
+
+Rules (the floating-point tolerance of the path: 1e-5 relative in float32
+before output rounding, 1 bf16 ulp after it):
+
+1. bytes, scales, permutations and group sizes: bit-exact;
+2. float32 results:  |g - o| <= 1e-5 * A + B_hw, where A is the oracle's
+   abs-sum (the same formula on absolute values, the componentwise measure
+   of a dot product's error) and B_hw is the fp8 matrix-core allowance below;
+3. bf16 results: where the float32 tolerance of rule 2 is below half a bf16
+   ulp of o, the bf16 result is within 1 ulp of bf16(o) (ordered bit
+   patterns); elsewhere (cancellation) |g - o| <= tolerance + half an ulp.
+
+B_hw: the gfx950 fp8 MFMA sums its products in aligned chunks of 8
+consecutive contraction indices.  Inside a chunk every product is aligned to
+the chunk's largest exponent sum e(a) + e(b) -- e(v) is the binary exponent
+of v, -6 for a subnormal, and a product with a zero operand takes no part --
+and bits below 2^(that sum - 13) are dropped (measured on the device for
+v_mfma_f32_16x16x128_f8f6f4 and v_mfma_f32_16x16x32_fp8_fp8).  So product i
+loses less than min(|p_i|, 2^-13 * max_j 2^(e(a_j) + e(b_j))) over its chunk;
+the allowance uses 2^-12 (a factor-2 margin) and the maximum over the window
+of the 15 products around i, which contains every aligned chunk holding i.
+"""
+
+import numpy as np
+import torch
+
+from oracle.codec import bf16_decode, bf16_rne_from_f64, e4m3_decode
+
+REL_TOL = 1e-5
+HW_FRAC = 2.0 ** -12
+
+
+# ------------------------------------------------------------ device helpers
+def dev_u8(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(device)
+
+
+def dev_i32(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+def dev_f32(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def dev_bf16(bits, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def host(t):
+    """Device tensor -> numpy (bf16 as uint16 bit patterns)."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+# ------------------------------------------------------------ allowance
+def _window_max(absp):
+    """max over [i-7, i+7] along the last axis."""
+    K = absp.shape[-1]
+    pad = np.zeros(absp.shape[:-1] + (K + 14,), dtype=absp.dtype)
+    pad[..., 7:7 + K] = absp
+    out = absp.copy()
+    for d in range(-7, 8):
+        out = np.maximum(out, pad[..., 7 + d:7 + d + K])
+    return out
+
+
+def _exp_field(codes):
+    """Alignment exponent of e4m3 codes: binary exponent, -6 for subnormals."""
+    e = (np.asarray(codes, np.int64) >> 3) & 0xF
+    return np.where(e == 0, -6, e - 7)
+
+
+def hw_allowance_products(p, ca, cb):
+    """B_hw of dot products with products p [..., K] (float64) of the codes
+    ca, cb [..., K]."""
+    nz = ((ca & 0x7F) != 0) & ((cb & 0x7F) != 0)
+    align = np.where(nz, np.ldexp(1.0, _exp_field(ca) + _exp_field(cb)), 0.0)
+    return np.minimum(np.abs(p), HW_FRAC * _window_max(align)).sum(axis=-1)
+
+
+def gmm_allowance(lhs_q, lhs_scale, rhs_q, rhs_scale, group_sizes, g0, El, rows, cols, transpose_rhs=False):
+    """B_hw of sampled gmm outputs (rows, cols), with the scales applied."""
+    gs = np.asarray(group_sizes, np.int64)[g0:g0 + El]
+    offs = np.concatenate([[0], np.cumsum(gs)])
+    K = lhs_q.shape[1]
+    rs = np.asarray(rhs_scale, np.float64)
+    kb, nb = rs.shape[1], rs.shape[3]
+    N = rhs_q.shape[1] if transpose_rhs else rhs_q.shape[2]
+    ls = np.asarray(lhs_scale, np.float64).reshape(-1)
+    out = np.zeros(len(rows))
+    grp = np.searchsorted(offs[1:], rows, side="right")
+    for g in np.unique(grp):
+        if g >= El:
+            continue
+        sel = np.nonzero(grp == g)[0]
+        Xc = lhs_q[rows[sel]]
+        Wg = rhs_q[g]
+        Wcc = Wg[cols[sel], :] if transpose_rhs else Wg[:, cols[sel]].T
+        p = e4m3_decode(Xc) * e4m3_decode(Wcc)                    # [P, K]
+        bk = K // kb
+        tot = np.zeros(len(sel))
+        for b in range(kb):
+            ks = slice(b * bk, (b + 1) * bk)
+            tot += np.abs(rs[g, b, 0, cols[sel] // (N // nb)]) * hw_allowance_products(p[:, ks], Xc[:, ks], Wcc[:, ks])
+        lsr = np.abs(ls[rows[sel]] if ls.size > 1 else np.full(len(sel), ls[0]))
+        out[sel] = lsr * tot
+    return out
+
+
+def tgmm_allowance(lhs_q, lhs_scale, rhs_q, rhs_scale, group_sizes, g0, El, gi, ki, ci):
+    gs = np.asarray(group_sizes, np.int64)[g0:g0 + El]
+    offs = np.concatenate([[0], np.cumsum(gs)])
+    ls = np.asarray(lhs_scale, np.float64).reshape(-1)
+    rs = np.asarray(rhs_scale, np.float64).reshape(-1)
+    out = np.zeros(len(gi))
+    for g in np.unique(gi):
+        sel = np.nonzero(gi == g)[0]
+        if gs[g] == 0:
+            continue
+        rows = slice(offs[g], offs[g + 1])
+        Xc = lhs_q[rows][:, ki[sel]].T                       # [P, m] codes
+        Dc = rhs_q[rows][:, ci[sel]].T
+        sc = np.abs((ls[ki[sel]] if ls.size > 1 else ls[0]) * (rs[ci[sel]] if rs.size > 1 else rs[0]))
+        out[sel] = sc * hw_allowance_products(e4m3_decode(Xc) * e4m3_decode(Dc), Xc, Dc)
+    return out
+
+
+# ------------------------------------------------------------ rules
+def _ordered(bits16):
+    b = bits16.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def _allowance_at(B, idx):
+    """B may be a scalar, an array shaped like the results, or a callable
+    returning the allowance of the flat indices ``idx``."""
+    if callable(B):
+        return np.asarray(B(idx), np.float64)
+    B = np.asarray(B, np.float64)
+    return B if B.ndim == 0 else B.reshape(-1)[idx]
+
+
+def check_f32(g, o, A, B=0.0, what=""):
+    g = np.asarray(g, np.float64).reshape(-1)
+    o = np.asarray(o, np.float64).reshape(-1)
+    A = np.asarray(A, np.float64).reshape(-1)
+    err = np.abs(g - o)
+    strict = err <= REL_TOL * A
+    idx = np.nonzero(~strict)[0]
+    if idx.size:
+        tol = REL_TOL * A[idx] + _allowance_at(B, idx)
+        bad = err[idx] > tol
+        assert not bad.any(), (f"{what}: {bad.sum()} of {g.size} float32 results outside 1e-5*A + B_hw; "
+                               f"worst excess {np.max(err[idx] - tol):.3g}")
+    return {"strict_frac": float(strict.mean()) if g.size else 1.0,
+            "max_err_over_A": float(np.max(np.where(A > 0, err / np.where(A > 0, A, 1), 0))) if g.size else 0.0}
+
+
+def check_bf16(g_bits, o, A, B=0.0, what=""):
+    g_bits = np.asarray(g_bits, np.uint16).reshape(-1)
+    o = np.asarray(o, np.float64).reshape(-1)
+    A = np.asarray(A, np.float64).reshape(-1)
+    o_bits = bf16_rne_from_f64(o)
+    d = np.abs(_ordered(g_bits) - _ordered(o_bits))
+    gv = bf16_decode(g_bits).astype(np.float64)
+    half_ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o), 1e-38))[1] - 9)
+
+    def failing(tol):
+        tight = tol < (2.0 ** -9) * np.abs(o_sel) * (1 - 2.0 ** -8)
+        return (tight & (d_sel > 1)) | ((~tight) & (np.abs(gv_sel - o_sel) > tol + hu_sel)), tight
+
+    sel = np.arange(g_bits.size)
+    o_sel, d_sel, gv_sel, hu_sel = o, d, gv, half_ulp
+    bad, tight = failing(REL_TOL * A)
+    idx = np.nonzero(bad)[0]
+    if idx.size:
+        sel = idx
+        o_sel, d_sel, gv_sel, hu_sel = o[idx], d[idx], gv[idx], half_ulp[idx]
+        bad2, _ = failing(REL_TOL * A[idx] + _allowance_at(B, idx))
+        assert not bad2.any(), (f"{what}: {bad2.sum()} bf16 results outside 1 ulp of bf16(o) "
+                                f"(or the cancellation tolerance)")
+    return {"exact_frac": float(np.mean(d == 0)) if d.size else 1.0, "max_ulp_diff": int(d.max()) if d.size else 0}
+
+
+def assert_bits_equal(g, o, what=""):
+    g = np.ascontiguousarray(g)
+    o = np.ascontiguousarray(o)
+    assert g.shape == o.shape, f"{what}: shape {g.shape} != {o.shape}"
+    if g.dtype == np.float32:
+        g = g.view(np.uint32)
+        o = o.astype(np.float32).view(np.uint32)
+    neq = g != o
+    assert not neq.any(), f"{what}: {neq.sum()} of {neq.size} differ; first at {np.argwhere(neq)[0].tolist()}"

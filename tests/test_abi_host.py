@@ -1,0 +1,153 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/*.h declares, and its host-side validation rejects bad arguments
+before any launch (only paths that return before touching the device are
+exercised here)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import moe_fp8_grouped_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for mt in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M):
+            names.add(mt.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libmoefp8.so not built")
+    return m.load_library()
+
+
+def test_header_declares_the_path_calls():
+    names = _declared_functions()
+    for fn in ["moe_quantize_rows", "moe_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
+               "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
+               "moe_version"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(m.LIB_PATH)
+    for fn in _declared_functions():
+        assert hasattr(raw, fn), fn
+    assert set(_declared_functions()) == set(m.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    assert m.status_string(m.MOE_OK) == "ok"
+    assert "workspace" in m.status_string(m.MOE_ERR_WORKSPACE)
+    assert m.status_string(99) == "unknown status"
+    assert m.version() >= 100
+
+
+def test_workspace_sizes(lib):
+    b = m.workspace_bytes(m.MOE_OP_QUANTIZE_ROWS, 100, 64, m.MOE_SCALE_ROW_DYNAMIC)
+    assert b >= 256 and b % 256 == 0
+    bt = m.workspace_bytes(m.MOE_OP_QUANTIZE_ROWS, 100, 64, m.MOE_SCALE_TENSOR_DYNAMIC)
+    assert bt > b
+    s1 = m.workspace_bytes(m.MOE_OP_SORT_BY_EXPERT, 32768, 0, 0, 64)
+    s2 = m.workspace_bytes(m.MOE_OP_SORT_BY_EXPERT, 65536, 0, 0, 256)
+    assert s2 > s1 >= 256 and s1 % 256 == 0
+    assert m.workspace_bytes(m.MOE_OP_GMM, 32768, 2048, 768, 64) >= 256
+    with pytest.raises(m.MoeError):
+        m.workspace_bytes(77)
+    with pytest.raises(m.MoeError):
+        m.workspace_bytes(m.MOE_OP_SORT_BY_EXPERT, 10, 0, 0, 2000)
+
+
+def _c(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def test_quantize_rows_validation(lib):
+    f = lambda *a: _c(lib, "moe_quantize_rows", *a)
+    one = 1  # non-null dummy pointer: never dereferenced on these paths
+    assert f(one, None, 0, 4, 24, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_SHAPE      # C % 16
+    assert f(one, None, 0, -1, 32, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_SHAPE
+    assert f(one, None, 5, 4, 32, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_UNSUPPORTED
+    assert f(one, None, 0, 4, 32, 9, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_UNSUPPORTED
+    assert f(one, None, 0, 4, 32, 2, -1.0, one, one, None, None, 0, None) == m.MOE_ERR_SHAPE     # bad static
+    assert f(None, None, 0, 4, 32, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_NULL
+    assert f(one, None, 1, 4, 32, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_NULL       # silu w/o up
+    assert f(one, one, 0, 4, 32, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_UNSUPPORTED # up w/o silu
+    assert f(one, None, 0, 4, 32, 1, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_WORKSPACE
+    assert f(one, None, 0, 4, 32, 1, 0.0, one, one, None, one, 16, None) == m.MOE_ERR_WORKSPACE
+
+
+def test_sort_validation(lib):
+    f = lambda *a: _c(lib, "moe_sort_by_expert", *a)
+    one = 1
+    def call(T=4, k=2, E=8, g0=0, El=8, xq=None, xscale=None, mode=0, H=0, M_cap=8, perm=one, inv=one,
+             gs=one, xs=None, ss=None, ws=one, wsb=1 << 20):
+        return f(one, T, k, E, g0, El, xq, xscale, mode, H, M_cap, perm, inv, gs, xs, ss, ws, wsb, None)
+    assert call(E=0) == m.MOE_ERR_SHAPE
+    assert call(E=2000) == m.MOE_ERR_SHAPE
+    assert call(k=0) == m.MOE_ERR_SHAPE
+    assert call(g0=4, El=5) == m.MOE_ERR_SHAPE
+    assert call(mode=7) == m.MOE_ERR_UNSUPPORTED
+    assert call(xq=one, H=24, xs=one) == m.MOE_ERR_SHAPE
+    assert call(gs=None) == m.MOE_ERR_NULL
+    assert call(xq=one, H=32, xs=None) == m.MOE_ERR_NULL
+    assert call(wsb=16) == m.MOE_ERR_WORKSPACE
+
+
+def test_gmm_validation(lib):
+    f = lambda *a: _c(lib, "moe_gmm_fp8", *a)
+    one = 1
+    def call(M=256, K=256, N=256, Kb=1, Nb=256, tr=1, E=8, g0=0, El=8, mode=0, od=0, ws=one, wsb=256,
+             lhs=one, out=one):
+        return f(lhs, one, mode, one, one, Kb, Nb, tr, one, E, g0, El, M, K, N, od, out, ws, wsb, None)
+    assert call(K=200) == m.MOE_ERR_SHAPE
+    assert call(N=100) == m.MOE_ERR_SHAPE
+    assert call(Kb=3) == m.MOE_ERR_SHAPE
+    assert call(K=384, Kb=2) == m.MOE_ERR_UNSUPPORTED        # 192-row K blocks
+    assert call(Nb=3) == m.MOE_ERR_SHAPE
+    assert call(tr=2) == m.MOE_ERR_UNSUPPORTED
+    assert call(mode=5) == m.MOE_ERR_UNSUPPORTED
+    assert call(od=7) == m.MOE_ERR_UNSUPPORTED
+    assert call(g0=1, El=8) == m.MOE_ERR_SHAPE
+    assert call(E=0) == m.MOE_ERR_SHAPE
+    assert call(lhs=None) == m.MOE_ERR_NULL
+    assert call(ws=None) == m.MOE_ERR_WORKSPACE
+    assert call(wsb=8) == m.MOE_ERR_WORKSPACE
+    assert call(M=0, out=None) == m.MOE_OK                  # nothing to do, no launch
+
+
+def test_tgmm_and_gather_reduce_validation(lib):
+    t = lambda *a: _c(lib, "moe_tgmm_fp8", *a)
+    one = 1
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 200, 256, 1, one, one, 256, None) == m.MOE_ERR_SHAPE
+    assert t(one, one, 3, one, one, 1, one, 8, 0, 8, 100, 256, 256, 1, one, one, 256, None) == m.MOE_ERR_UNSUPPORTED
+    assert t(one, one, 1, one, one, 7, one, 8, 0, 8, 100, 256, 256, 1, one, one, 256, None) == m.MOE_ERR_UNSUPPORTED
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 0, 100, 256, 256, 1, one, one, 256, None) == m.MOE_OK  # no experts
+    g = lambda *a: _c(lib, "moe_gather_reduce", *a)
+    assert g(one, 0, one, one, 4, 2, 12, 0, one, None) == m.MOE_ERR_SHAPE          # N % 8
+    assert g(one, 2, one, one, 4, 2, 16, 0, one, None) == m.MOE_ERR_UNSUPPORTED    # fp8 input
+    assert g(one, 0, one, one, 4, 0, 16, 0, one, None) == m.MOE_ERR_SHAPE
+    assert g(None, 0, one, one, 4, 2, 16, 0, one, None) == m.MOE_ERR_NULL
+    assert g(None, 0, None, None, 0, 2, 16, 0, None, None) == m.MOE_OK             # T = 0
+
+
+def test_weight_quantizer_validation(lib):
+    q = lambda *a: _c(lib, "moe_quantize_weights", *a)
+    one = 1
+    assert q(one, 2, 256, 250, 1, 250, 0, 0.0, 0, one, one, None) == m.MOE_ERR_SHAPE
+    assert q(one, 2, 256, 256, 3, 256, 0, 0.0, 0, one, one, None) == m.MOE_ERR_SHAPE
+    assert q(one, 2, 256, 256, 1, 256, 1, 0.0, 0, one, one, None) == m.MOE_ERR_UNSUPPORTED
+    assert q(one, 2, 256, 256, 1, 256, 0, 0.0, 2, one, one, None) == m.MOE_ERR_UNSUPPORTED
+    assert q(None, 2, 256, 256, 1, 256, 0, 0.0, 0, one, one, None) == m.MOE_ERR_NULL
+    assert q(None, 0, 256, 256, 1, 256, 0, 0.0, 0, None, None, None) == m.MOE_OK

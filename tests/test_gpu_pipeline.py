@@ -1,0 +1,218 @@
+"""GPU parity of the gather-reduce and of whole pipelines, checked stage by
+stage: the oracle of each stage is fed the GPU's actual inputs for that
+stage, so the bit-exact rules apply to every quantization on the path."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_fp8_grouped_amd as m
+from moe_fp8_grouped_amd.pipeline import BackwardPath, ForwardPath
+from oracle.gather_reduce import gather_reduce
+from oracle.gmm import gmm, tgmm
+from oracle.pipeline import dense_bf16_reference, rel_norm_diff
+from oracle.quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STATIC, quantize_rows,
+                             quantize_weights)
+from oracle.sort import sort_by_expert
+from tests.golden import accuracy_tables
+from tests.parity import (assert_bits_equal, check_bf16, check_f32, dev_bf16, dev_f32, dev_i32, gmm_allowance, host,
+                          tgmm_allowance)
+from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate, scaled_config, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_gather_reduce(y, y_bf16, inv, w, out_dtype=m.MOE_BF16):
+    T, k = inv.shape
+    N = y.shape[1]
+    yd = dev_bf16(y) if y_bf16 else dev_f32(y)
+    out = torch.full((T, N), 9.0, dtype=torch.bfloat16 if out_dtype == m.MOE_BF16 else torch.float32, device="cuda")
+    print(f"gather_reduce T={T} k={k} N={N} y_bf16={y_bf16}", flush=True)
+    m.moe_gather_reduce(yd, m.MOE_BF16 if y_bf16 else m.MOE_F32, dev_i32(inv), dev_f32(w), T, k, N, out_dtype, out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("T,k,E,g0,El,N", [(256, 2, 8, 0, 8, 1024), (4096, 8, 64, 0, 64, 2048),
+                                           (2000, 8, 256, 64, 32, 7168), (33, 3, 5, 1, 2, 8)])
+def test_gather_reduce(T, k, E, g0, El, N):
+    rng = np.random.default_rng(T + N)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    srt = sort_by_expert(ids, E, g0, El)
+    inv = srt["inv_pos"].reshape(T, k)
+    rows = max(srt["n"], 1)
+    y = to_bf16_bits(rng.standard_normal((rows, N)).astype(np.float32))
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    o = gather_reduce(y, True, inv, w)
+    g = gpu_gather_reduce(y, True, inv, w)
+    check_bf16(g, o["out"], o["abs_sum"], 0.0, "gather_reduce bf16")
+    none = np.all(inv < 0, axis=1)
+    assert not g[none].any()
+    g32 = gpu_gather_reduce(y, True, inv, w, m.MOE_F32)
+    check_f32(g32, o["out"], o["abs_sum"], 0.0, "gather_reduce f32")
+    yf = (rng.standard_normal((rows, N))).astype(np.float32)
+    o2 = gather_reduce(yf, False, inv, w)
+    g2 = gpu_gather_reduce(yf, False, inv, w, m.MOE_F32)
+    check_f32(g2, o2["out"], o2["abs_sum"], 0.0, "gather_reduce f32 in")
+
+
+def test_gather_reduce_k1_is_exact_unsort():
+    rng = np.random.default_rng(3)
+    T, E, N = 500, 7, 64
+    ids = rng.integers(0, E, (T, 1)).astype(np.int32)
+    srt = sort_by_expert(ids, E, 0, E)
+    y = to_bf16_bits(rng.standard_normal((T, N)).astype(np.float32))
+    g = gpu_gather_reduce(y, True, srt["inv_pos"].reshape(T, 1), np.ones((T, 1), np.float32))
+    assert_bits_equal(g, y[srt["inv_pos"]], "k=1 unsort")
+
+
+# ------------------------------------------------------------------ pipelines
+def _sample_gmm_stage(lhs, ls, wq_kn, ws_, gs, g0, El, got, n, seed, P, what):
+    rng = np.random.default_rng(seed)
+    N = wq_kn.shape[2]
+    rows = rng.integers(0, max(n, 1), P)
+    cols = rng.integers(0, N, P)
+    o = gmm(lhs, ls, wq_kn, ws_, gs, g0, El, sample=(rows, cols))
+    B = lambda idx: gmm_allowance(lhs, ls, wq_kn, ws_, gs, g0, El, rows[idx], cols[idx])
+    return check_bf16(got[rows, cols], o["out"], o["abs_sum"], B, what)
+
+
+def _weights_kn(path, name):
+    w = path.w[name]
+    q = host(w.q)
+    return (np.ascontiguousarray(q.transpose(0, 2, 1)) if w.nk else q), host(w.scale)
+
+
+def _forward_stagewise(cfg, data, static=False, full_gmm=False, P=4000):
+    mc = None
+    if cfg.E_loc != cfg.E:
+        n_loc = int(np.isin(data["ids"], np.arange(cfg.group_offset, cfg.group_offset + cfg.E_loc)).sum())
+        mc = ((n_loc + 255) // 256) * 256
+    path = ForwardPath(cfg, data, static_act=STATIC_ACT_SCALE if static else None,
+                       static_weight=STATIC_WEIGHT_SCALE if static else None, m_cap=mc)
+    print(f"pipeline {cfg.name} static={static} m_cap={path.m_cap}", flush=True)
+    path.step()
+    torch.cuda.synchronize()
+    assert m.moe_debug_check(path.ws_sort) == 0 and m.moe_debug_check(path.ws_gmm) == 0
+    mode = SCALE_TENSOR_STATIC if static else SCALE_ROW_DYNAMIC
+    # weights: the GPU quantizer against the oracle's (first experts of large weights)
+    for name, wb in data["weights"].items():
+        kb, nb = cfg.scale_blocks(wb.shape[1], wb.shape[2])
+        ne = wb.shape[0] if wb.size <= (1 << 26) else 2
+        wq_o, ws_o = quantize_weights(wb[:ne], kb, nb, static_scale=STATIC_WEIGHT_SCALE if static else None)
+        wq_g, ws_g = _weights_kn(path, name)
+        assert_bits_equal(wq_g[:ne], wq_o, name + " q")
+        assert_bits_equal(ws_g[:ne], ws_o, name + " scale")
+    # S1 quantize
+    xq, xsc, _ = quantize_rows(data["x"], mode, static_scale=STATIC_ACT_SCALE if static else None)
+    assert_bits_equal(host(path.xq), xq, "xq")
+    assert_bits_equal(host(path.xscale), xsc, "xscale")
+    # S2/S3 sort
+    srt = sort_by_expert(data["ids"], cfg.E, cfg.group_offset, cfg.E_loc, xq=xq, xscale=xsc, xscale_mode=mode,
+                         m_cap=path.m_cap)
+    assert_bits_equal(host(path.perm), srt["perm"], "perm")
+    assert_bits_equal(host(path.inv_pos), srt["inv_pos"], "inv_pos")
+    assert_bits_equal(host(path.group_sizes), srt["group_sizes"], "group_sizes")
+    assert_bits_equal(host(path.xs), srt["xs"], "xs")
+    if mode == SCALE_ROW_DYNAMIC:
+        assert_bits_equal(host(path.ss), srt["ss"], "ss")
+    gs, g0, El, n = srt["group_sizes"], cfg.group_offset, cfg.E_loc, srt["n"]
+    ls = srt["ss"] if mode == SCALE_ROW_DYNAMIC else xsc
+    if cfg.pipeline == "up":
+        wq, ws_ = _weights_kn(path, "w_up")
+        y = host(path.y)
+        if full_gmm:
+            o = gmm(srt["xs"], ls, wq, ws_, gs, g0, El)
+            N = o["out"].shape[1]
+            B = lambda idx: gmm_allowance(srt["xs"], ls, wq, ws_, gs, g0, El, idx // N, idx % N)
+            check_bf16(y, o["out"], o["abs_sum"], B, "up gmm")
+        else:
+            _sample_gmm_stage(srt["xs"], ls, wq, ws_, gs, g0, El, y, n, 1, P, "up gmm")
+    else:
+        for name, buf, seed in (("wi_0", path.a, 2), ("wi_1", path.b, 3)):
+            wq, ws_ = _weights_kn(path, name)
+            _sample_gmm_stage(srt["xs"], ls, wq, ws_, gs, g0, El, host(buf), n, seed, P, name)
+        a, b = host(path.a), host(path.b)
+        assert not a[n:].any() and not b[n:].any()
+        # S5: requantization of silu(a)*b from the GPU's own a and b -- bit-exact
+        hq, hs, _ = quantize_rows(a, SCALE_ROW_DYNAMIC, x_up_bits=b)
+        assert_bits_equal(host(path.hq), hq, "hq")
+        assert_bits_equal(host(path.hs), hs, "hs")
+        wq, ws_ = _weights_kn(path, "wo")
+        _sample_gmm_stage(hq, hs, wq, ws_, gs, g0, El, host(path.y), n, 4, P, "wo")
+    # S7 from the GPU's y
+    y = host(path.y)
+    o = gather_reduce(y, True, host(path.inv_pos).reshape(cfg.T, cfg.k), data["topk_w"])
+    out = host(path.out)
+    check_bf16(out, o["out"], o["abs_sum"], 0.0, "gather_reduce")
+    return out
+
+
+@pytest.mark.parametrize("cid,static", [(1, False), (3, False), (3, True)])
+def test_up_projection_pipeline_stagewise_and_context(cid, static):
+    cfg = CONFIGS[cid]
+    data = generate(cfg)
+    out = _forward_stagewise(cfg, data, static=static, full_gmm=True)
+    # fp8 vs unquantized bf16, next to the pages' TPU figures (context only)
+    rel, mx = rel_norm_diff(out, dense_bf16_reference(cfg, data))
+    tab = accuracy_tables()
+    page = tab[("rel", "megablox_fp8_static_ep1" if static else "megablox_fp8_dynamic_ep1")][0]
+    print(f"config {cid} {'static' if static else 'dynamic'}: rel_norm_diff {rel:.4f} max_abs {mx:.3g} "
+          f"(pages, TPU v5p-8 whole layer: {page})")
+    assert rel < 0.2
+
+
+@pytest.mark.timeout(600)
+def test_gated_ffn_pipeline_config2_stagewise():
+    cfg = CONFIGS[2]
+    _forward_stagewise(cfg, generate(cfg), P=3000)
+
+
+def test_gated_ffn_small_full_context():
+    cfg = scaled_config(2, T=128, H=256, E=8, k=2, I=256)
+    data = generate(cfg)
+    out = _forward_stagewise(cfg, data, P=2000)
+    rel, _ = rel_norm_diff(out, dense_bf16_reference(cfg, data))
+    assert rel < 0.2
+
+
+@pytest.mark.timeout(900)
+def test_expert_slice_pipeline_config4_stagewise():
+    cfg = CONFIGS[4]
+    data = generate(cfg)
+    out = _forward_stagewise(cfg, data, P=1500)
+    inv = (~np.isin(data["ids"], np.arange(64, 96))).all(axis=1)
+    assert inv.any() and not out[inv].any()       # tokens with no local expert: zero partial sums
+
+
+@pytest.mark.timeout(600)
+def test_backward_pipeline_config5_stagewise():
+    cfg = CONFIGS[5]
+    data = generate(cfg)
+    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE)
+    print("pipeline config 5 backward", flush=True)
+    path.step()
+    torch.cuda.synchronize()
+    wq, ws_ = quantize_weights(data["weights"]["w_up"], 1, 1, static_scale=STATIC_WEIGHT_SCALE)
+    assert_bits_equal(host(path.w.q), wq, "w q")
+    xq, xsc, _ = quantize_rows(data["x"], SCALE_TENSOR_STATIC, static_scale=STATIC_ACT_SCALE)
+    assert_bits_equal(host(path.xq), xq, "xq")
+    srt = sort_by_expert(data["ids"], cfg.E, 0, cfg.E, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_STATIC)
+    assert_bits_equal(host(path.xs), srt["xs"], "xs")
+    dq_r, ds_r, _ = quantize_rows(data["dy"], SCALE_ROW_DYNAMIC)
+    dq_t, ds_t, _ = quantize_rows(data["dy"], SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(host(path.dyq_r), dq_r, "dy row q")
+    assert_bits_equal(host(path.dys_r), ds_r, "dy row scale")
+    assert_bits_equal(host(path.dyq_t), dq_t, "dy tensor q")
+    assert_bits_equal(host(path.dys_t), ds_t, "dy tensor scale")
+    gs = srt["group_sizes"]
+    wT = np.ascontiguousarray(wq.transpose(0, 2, 1))
+    rng = np.random.default_rng(6)
+    rows, cols = rng.integers(0, cfg.M, 3000), rng.integers(0, cfg.H, 3000)
+    o = gmm(dq_r, ds_r, wT, ws_, gs, 0, cfg.E, sample=(rows, cols))
+    B = lambda idx: gmm_allowance(dq_r, ds_r, wT, ws_, gs, 0, cfg.E, rows[idx], cols[idx])
+    check_bf16(host(path.dx)[rows, cols], o["out"], o["abs_sum"], B, "dX")
+    gi, ki, ci = rng.integers(0, cfg.E, 3000), rng.integers(0, cfg.H, 3000), rng.integers(0, cfg.I, 3000)
+    o = tgmm(srt["xs"], xsc, dq_t, ds_t, gs, 0, cfg.E, sample=(gi, ki, ci))
+    B = lambda idx: tgmm_allowance(srt["xs"], xsc, dq_t, ds_t, gs, 0, cfg.E, gi[idx], ki[idx], ci[idx])
+    check_f32(host(path.dw)[gi, ki, ci], o["out"], o["abs_sum"], B, "dW")

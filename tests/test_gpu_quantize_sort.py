@@ -1,0 +1,224 @@
+"""GPU parity of the quantizers and the ragged sort against the oracle:
+bit-exact bytes, scales, permutations and group sizes."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_fp8_grouped_amd as m
+from oracle.quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STATIC, quantize_rows,
+                             quantize_weights)
+from oracle.sort import sort_by_expert
+from tests.parity import assert_bits_equal, dev_bf16, dev_f32, dev_i32, dev_u8, host
+from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate, scaled_config, to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_quantize(x_bits, mode, static=0.0, up_bits=None):
+    R, C = x_bits.shape
+    x = dev_bf16(x_bits)
+    up = dev_bf16(up_bits) if up_bits is not None else None
+    q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    s = torch.empty((R if mode == m.MOE_SCALE_ROW_DYNAMIC else 1,), dtype=torch.float32, device="cuda")
+    amax = torch.empty((R,), dtype=torch.float32, device="cuda")
+    ws = m.workspace(m.MOE_OP_QUANTIZE_ROWS, R, C, mode)
+    act = m.MOE_ACT_SILU_MUL if up is not None else m.MOE_ACT_NONE
+    print(f"quantize R={R} C={C} mode={mode} act={act}", flush=True)
+    m.moe_quantize_rows(x, up, act, R, C, mode, static, q, s, amax, ws)
+    torch.cuda.synchronize()
+    return host(q), host(s), host(amax)
+
+
+def _bits(rng, shape, scale=1.0):
+    return to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("R,C", [(1, 16), (7, 48), (256, 512), (300, 2048), (33, 7168), (5, 8192), (3, 8208)])
+def test_row_quantize_bit_exact(R, C):
+    rng = np.random.default_rng(R * 7 + C)
+    x = _bits(rng, (R, C), 3.0)
+    x[0, :5] = 0x8000                  # -0.0
+    if R > 2:
+        x[2] = 0                       # an all-zero row
+        x[1, 3] = to_bf16_bits(np.array([1e-39], np.float32))[0]   # subnormal input
+    q, s, a = gpu_quantize(x, m.MOE_SCALE_ROW_DYNAMIC)
+    qo, so, ao = quantize_rows(x, SCALE_ROW_DYNAMIC)
+    assert_bits_equal(q, qo, "q")
+    assert_bits_equal(s, so, "scale")
+    assert_bits_equal(a, ao, "row_amax")
+
+
+def test_row_quantize_config_inputs():
+    for cid in (1, 2):
+        d = generate(CONFIGS[cid], with_weights=False)
+        q, s, _ = gpu_quantize(d["x"], m.MOE_SCALE_ROW_DYNAMIC)
+        qo, so, _ = quantize_rows(d["x"], SCALE_ROW_DYNAMIC)
+        assert_bits_equal(q, qo, f"config {cid} q")
+        assert_bits_equal(s, so, f"config {cid} scale")
+    # config 4: one GPU's share (1/8 of the tokens) with its outlier rows
+    d = generate(CONFIGS[4], with_weights=False)
+    share = d["x"][:1024]
+    q, s, _ = gpu_quantize(share, m.MOE_SCALE_ROW_DYNAMIC)
+    qo, so, _ = quantize_rows(share, SCALE_ROW_DYNAMIC)
+    assert_bits_equal(q, qo, "config 4 share q")
+    assert_bits_equal(s, so, "config 4 share scale")
+
+
+def test_tensor_and_static_modes():
+    rng = np.random.default_rng(5)
+    dy = _bits(rng, (4096, 1536), 1e-3)
+    q, s, a = gpu_quantize(dy, m.MOE_SCALE_TENSOR_DYNAMIC)
+    qo, so, ao = quantize_rows(dy, SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(q, qo, "tensor q")
+    assert_bits_equal(s, so, "tensor scale")
+    assert_bits_equal(a, ao, "tensor row_amax")
+    x = _bits(rng, (512, 4096), 1.5)         # 1.5 sigma: part of it saturates at +-448
+    q, s, _ = gpu_quantize(x, m.MOE_SCALE_TENSOR_STATIC, STATIC_ACT_SCALE)
+    qo, so, _ = quantize_rows(x, SCALE_TENSOR_STATIC, static_scale=STATIC_ACT_SCALE)
+    assert np.isin(qo, [0x7E, 0xFE]).sum() > 100
+    assert_bits_equal(q, qo, "static q")
+    assert_bits_equal(s, so, "static scale")
+
+
+@pytest.mark.parametrize("R,C", [(64, 768), (37, 2048), (2, 16)])
+def test_silu_mul_requantize_bit_exact(R, C):
+    rng = np.random.default_rng(R + C)
+    a = _bits(rng, (R, C), 4.0)
+    b = _bits(rng, (R, C), 1.0)
+    a[0, :4] = to_bf16_bits(np.array([100.0, -100.0, 0.0, -0.0], np.float32))
+    q, s, _ = gpu_quantize(a, m.MOE_SCALE_ROW_DYNAMIC, up_bits=b)
+    qo, so, _ = quantize_rows(a, SCALE_ROW_DYNAMIC, x_up_bits=b)
+    assert_bits_equal(q, qo, "silu q")
+    assert_bits_equal(s, so, "silu scale")
+
+
+def test_empty_rows_tensor_dynamic():
+    ws = m.workspace(m.MOE_OP_QUANTIZE_ROWS, 0, 32, m.MOE_SCALE_TENSOR_DYNAMIC)
+    s = torch.zeros(1, dtype=torch.float32, device="cuda")
+    dummy = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    m.moe_quantize_rows(None, None, 0, 0, 32, m.MOE_SCALE_TENSOR_DYNAMIC, 0.0, None, s, None, ws)
+    torch.cuda.synchronize()
+    assert host(s)[0] == 1.0
+    del dummy
+
+
+@pytest.mark.parametrize("E,K,N,kb,nb,static,nk", [
+    (8, 512, 1024, 1, 1024, None, 0), (8, 512, 1024, 1, 1024, None, 1),      # per channel
+    (8, 512, 1024, 4, 1024, None, 1),                                         # 128-row K blocks
+    (2, 1024, 512, 8, 4, None, 1), (2, 512, 1024, 4, 8, None, 0),            # 128 x 128 blocks
+    (4, 256, 256, 1, 1, STATIC_WEIGHT_SCALE, 0), (4, 256, 256, 2, 256, STATIC_WEIGHT_SCALE, 1)])
+def test_weight_quantizer_bit_exact(E, K, N, kb, nb, static, nk):
+    rng = np.random.default_rng(E * K + N + kb)
+    w = _bits(rng, (E, K, N), 0.02)
+    w[0, :K // kb, :N // nb] = 0                                              # an all-zero block
+    qd = torch.empty((E, N, K) if nk else (E, K, N), dtype=torch.uint8, device="cuda")
+    sd = torch.empty((E, kb, 1, nb), dtype=torch.float32, device="cuda")
+    mode = m.MOE_SCALE_TENSOR_STATIC if static else m.MOE_SCALE_ROW_DYNAMIC
+    print(f"quantize_weights E={E} K={K} N={N} kb={kb} nb={nb} nk={nk}", flush=True)
+    m.moe_quantize_weights(dev_bf16(w), E, K, N, kb, nb, mode, static or 0.0, nk, qd, sd)
+    torch.cuda.synchronize()
+    qo, so = quantize_weights(w, kb, nb, static_scale=static)
+    assert_bits_equal(host(sd), so, "weight scale")
+    q = host(qd)
+    assert_bits_equal(q.transpose(0, 2, 1) if nk else q, qo, "weight q")
+
+
+# ------------------------------------------------------------------ sort
+def gpu_sort(ids, E, g0, El, xq=None, xscale=None, mode=m.MOE_SCALE_ROW_DYNAMIC, m_cap=None):
+    T, k = ids.shape
+    M = T * k
+    H = xq.shape[1] if xq is not None else 0
+    m_cap = M if m_cap is None else m_cap
+    perm = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    inv = torch.full((M,), -7, dtype=torch.int32, device="cuda")
+    gs = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    xs = torch.full((m_cap, H), 0xAB, dtype=torch.uint8, device="cuda") if xq is not None else None
+    row = mode == m.MOE_SCALE_ROW_DYNAMIC and xscale is not None
+    ss = torch.full((m_cap,), 7.0, dtype=torch.float32, device="cuda") if row else None
+    ws = m.workspace(m.MOE_OP_SORT_BY_EXPERT, M, 0, 0, E)
+    print(f"sort T={T} k={k} E={E} g0={g0} El={El} H={H} m_cap={m_cap}", flush=True)
+    m.moe_sort_by_expert(dev_i32(ids) if M else torch.zeros(1, dtype=torch.int32, device="cuda"), T, k, E, g0, El,
+                         dev_u8(xq) if xq is not None else None,
+                         dev_f32(xscale) if xscale is not None else None, mode, H, m_cap, perm, inv, gs, xs, ss, ws)
+    err = m.moe_debug_check(ws)
+    out = {"perm": host(perm), "inv_pos": host(inv), "group_sizes": host(gs), "err": err}
+    if xs is not None:
+        out["xs"] = host(xs)
+    if ss is not None:
+        out["ss"] = host(ss)
+    return out
+
+
+def _check_sort(g, o, with_rows=True):
+    assert g["err"] == 0
+    assert_bits_equal(g["perm"], o["perm"], "perm")
+    assert_bits_equal(g["inv_pos"], o["inv_pos"], "inv_pos")
+    assert_bits_equal(g["group_sizes"], o["group_sizes"], "group_sizes")
+    assert int(o["group_sizes"].sum()) == len(o["perm"])
+    if with_rows and "xs" in g:
+        assert_bits_equal(g["xs"], o["xs"], "xs")
+    if with_rows and "ss" in g and "ss" in o and o["ss"].shape == g["ss"].shape:
+        assert_bits_equal(g["ss"], o["ss"], "ss")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_sort_config_routing(cid):
+    cfg = CONFIGS[cid]
+    d = generate(cfg, with_weights=False)
+    mode = SCALE_TENSOR_STATIC if cfg.static else SCALE_ROW_DYNAMIC
+    st = STATIC_ACT_SCALE if cfg.static else None
+    xq, xsc, _ = quantize_rows(d["x"], mode, static_scale=st)
+    o = sort_by_expert(d["ids"], cfg.E, cfg.group_offset, cfg.E_loc, xq=xq, xscale=xsc, xscale_mode=mode)
+    m_cap = cfg.M if cfg.E_loc == cfg.E else ((o["n"] + 255) // 256) * 256
+    o = sort_by_expert(d["ids"], cfg.E, cfg.group_offset, cfg.E_loc, xq=xq, xscale=xsc, xscale_mode=mode,
+                       m_cap=m_cap)
+    g = gpu_sort(d["ids"], cfg.E, cfg.group_offset, cfg.E_loc, xq, xsc, mode, m_cap)
+    _check_sort(g, o)
+    if cid == 3:
+        assert (o["group_sizes"] == 0).sum() >= 2
+
+
+@pytest.mark.parametrize("T,k,E,g0,El,extra", [(1, 1, 1, 0, 1, 0), (5, 3, 7, 2, 3, 10), (700, 2, 16, 0, 16, 0),
+                                               (1000, 5, 300, 17, 200, 33), (3000, 8, 1024, 512, 512, 0),
+                                               (0, 4, 8, 0, 8, 16), (2049, 1, 3, 1, 1, 5)])
+def test_sort_edge_cases(T, k, E, g0, El, extra):
+    rng = np.random.default_rng(T + E)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    if T > 10:
+        ids[: T // 2] = g0          # one expert takes half the rows
+    H = 32
+    xq = rng.integers(0, 256, (T, H)).astype(np.uint8)
+    xsc = rng.uniform(0.1, 1.0, T).astype(np.float32)
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc)
+    m_cap = o["n"] + extra
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc, m_cap=m_cap)
+    g = gpu_sort(ids, E, g0, El, xq, xsc, m.MOE_SCALE_ROW_DYNAMIC, m_cap)
+    _check_sort(g, o)
+
+
+def test_sort_tensor_scale_and_metadata_only():
+    rng = np.random.default_rng(9)
+    ids = rng.integers(0, 6, (50, 2)).astype(np.int32)
+    o = sort_by_expert(ids, 6, 1, 4)
+    g = gpu_sort(ids, 6, 1, 4)
+    _check_sort(g, o, with_rows=False)
+
+
+def test_sort_flags_bad_ids_without_faulting():
+    ids = np.array([[0, 5], [9, 1], [-2, 3]], np.int32)     # 9 and -2 are out of range for E = 6
+    xq = np.arange(3 * 16, dtype=np.uint8).reshape(3, 16)
+    g = gpu_sort(ids, 6, 0, 6, xq, np.ones(3, np.float32), m_cap=6)
+    assert g["err"] & m.MOE_DEVERR_EXPERT_ID
+    assert int(g["group_sizes"].sum()) == 4
+    assert sorted(g["perm"].tolist()) == list(range(6))        # still a permutation
+    inv = g["inv_pos"]
+    assert inv[2] == -1 and inv[4] == -1
+
+
+def test_sort_flags_rows_beyond_capacity():
+    ids = np.zeros((20, 2), np.int32)
+    xq = np.ones((20, 16), np.uint8)
+    g = gpu_sort(ids, 2, 0, 2, xq, np.ones(20, np.float32), m_cap=10)
+    assert g["err"] & m.MOE_DEVERR_ROWS
+    assert (g["inv_pos"] >= 10).sum() == 0

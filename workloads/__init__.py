@@ -21,10 +21,12 @@ configurations stand in for them:
 5. MoE backward: T=8192, H=4096, E=64, top-4, I=1536, uniform routing,
    dY ~ N(0, 1e-3) in sorted-row space, static activation/weight scales.
 
-Generator: ``numpy.random.default_rng(1000 + c)``; draw order router logits
-(+ Zipf bias) -> x -> weights (wi_0, wi_1, wo, or the single up weight) ->
-dY -> outlier rows; every float32 draw is rounded to bfloat16 by torch's CPU
-cast (round to nearest even).
+Generator: every tensor has its own stream, ``numpy.random.default_rng([1000
++ c, s])`` with s = 0 routing (logits, then the Zipf rank permutation), 1
+activations x, 2 outlier rows, 3 dY, 10 + i the i-th weight (wi_0, wi_1, wo,
+or the single up weight), so that any subset can be drawn on its own; every
+float32 draw is rounded to bfloat16 by torch's CPU cast (round to nearest
+even).
 """
 
 from dataclasses import dataclass, field
@@ -126,16 +128,21 @@ def _route_softmax(logits, k):
     return order.astype(np.int32), w
 
 
+def _rng(cfg, seed, stream):
+    return np.random.default_rng([1000 + cfg.cid if seed is None else seed, stream])
+
+
 def generate(cfg: MoEConfig, seed=None, with_weights=True):
     """Draw one workload.  Returns a dict of numpy arrays:
 
     ids int32 [T, k], topk_w float32 [T, k], x uint16 [T, H] (bf16 bits),
     weights {name: uint16 [E_loc, K, N]}, and for the backward config
-    dy uint16 [T*k, I].  Also the config's group_offset / E_loc.
+    dy uint16 [T*k, I].  ``with_weights`` is True (all weights), False (none)
+    or a collection of weight names.
     """
-    rng = np.random.default_rng(1000 + cfg.cid if seed is None else seed)
     T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
     out = {"cfg": cfg}
+    rng = _rng(cfg, seed, 0)
     if cfg.routing == "uniform":
         ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) if T else \
             np.zeros((0, k), np.int32)
@@ -150,20 +157,26 @@ def generate(cfg: MoEConfig, seed=None, with_weights=True):
         if cfg.routing == "zipf" and T >= 64:
             empty = int((np.bincount(out["ids"].ravel(), minlength=E) == 0).sum())
             assert empty >= 2, "Zipf-skewed routing is expected to leave experts empty"
-    x = rng.standard_normal((T, H), dtype=np.float32)
-    weights = {}
-    if with_weights:
-        for name, shp in cfg.weight_shapes():
-            weights[name] = to_bf16_bits(rng.standard_normal(shp, dtype=np.float32) * np.float32(0.02))
-    out["weights"] = weights
-    if cfg.pipeline == "bwd":
-        out["dy"] = to_bf16_bits(rng.standard_normal((T * k, cfg.I), dtype=np.float32) * np.float32(1e-3))
+    x = _rng(cfg, seed, 1).standard_normal((T, H), dtype=np.float32)
     if cfg.outlier_frac > 0 and T:
         n_out = int(round(cfg.outlier_frac * T))
-        rows = rng.choice(T, n_out, replace=False)
+        rows = _rng(cfg, seed, 2).choice(T, n_out, replace=False)
         x[rows] *= np.float32(cfg.outlier_mult)
         out["outlier_rows"] = np.sort(rows)
     out["x"] = to_bf16_bits(x)
+    del x
+    weights = {}
+    for i, (name, shp) in enumerate(cfg.weight_shapes()):
+        if with_weights is True or (with_weights and name in with_weights):
+            w = _rng(cfg, seed, 10 + i).standard_normal(shp, dtype=np.float32)
+            w *= np.float32(0.02)
+            weights[name] = to_bf16_bits(w)
+            del w
+    out["weights"] = weights
+    if cfg.pipeline == "bwd":
+        dy = _rng(cfg, seed, 3).standard_normal((T * k, cfg.I), dtype=np.float32)
+        dy *= np.float32(1e-3)
+        out["dy"] = to_bf16_bits(dy)
     return out
 
 
