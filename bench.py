@@ -59,7 +59,7 @@ def step_accounting(path, n, U):
     return acc
 
 
-def run_gpu(cfg_id, steps, warmup):
+def run_gpu(cfg_id, steps, warmup, calib_mib=0):
     import moe_fp8_grouped_amd as m
     from moe_fp8_grouped_amd.pipeline import ForwardPath
     from workloads import CONFIGS, generate, m_cap_for
@@ -108,6 +108,14 @@ def run_gpu(cfg_id, steps, warmup):
             timed("gmm_wo", lambda: path.gmm(path.hq, path.hs, m.MOE_SCALE_ROW_DYNAMIC, path.w["wo"], path.y), record)
         timed("gather_reduce", path.combine, record)
 
+    if calib_mib:
+        # a plain copy kernel of known size: its HBM counters calibrate the profiler's byte counts
+        src = torch.ones(calib_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 0.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(warmup):
         one_step(False)
     torch.cuda.synchronize()
@@ -205,12 +213,14 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (profiler byte-counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {a.gpus}); expert parallelism is modelled "
               f"as one GPU's expert slice", file=sys.stderr)
         sys.exit(2)
-    res, cfg = run_gpu(a.config, a.steps, a.warmup)
+    res, cfg = run_gpu(a.config, a.steps, a.warmup, a.calib_copy_mib)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, a.cpu_tokens)
     print(json.dumps(res), flush=True)

@@ -17,11 +17,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 }
 
 // float32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+// Branch-free (a select, not a divergent branch, handles NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((b >> 16) | 0x0040u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return static_cast<uint16_t>(b >> 16);
+  const uint32_t b = __float_as_uint(f);
+  const uint32_t rounded = (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (b >> 16) | 0x0040u;
+  return static_cast<uint16_t>((b & 0x7fffffffu) > 0x7f800000u ? quiet : rounded);
 }
 
 // ---------------------------------------------------------------- e4m3fn

@@ -1,0 +1,139 @@
+// moe_tgmm_fp8: transposed grouped matmul for weight gradients on the gfx950
+// fp8 matrix cores ("Support quantization for tokamax gmm v2": quantized
+// gmm2 / tgmm2, backward split into an input-gradient gmm and a per-group
+//   out[g, k, c] = ls[k] * rs[c] * sum_{r in group g} X[r, k] dY[r, c]
+// weight-gradient tgmm).  The contraction runs over each group's rows, so
+// both operands are row-contiguous: 128 x 128-byte row tiles are staged
+// through LDS (rows padded to 144 bytes) and read with ds_read_b64_tr_b8;
+// rows past the group's end are staged as zeros.  A 256-thread workgroup
+// owns a 128 x 128 output tile (four 64 x 64 wave quarters of 16 x 16 MFMA
+// tiles); persistent workgroups take tiles from an XCD-contiguous range.
+// Bound by the float32 output write (E_loc * K * N * 4 bytes).
+#include "tile_common.hpp"
+
+namespace moe {
+namespace {
+using namespace tile;
+
+// ------------------------------------------------------------------ tgmm
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void tgmm_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
+                                                   int ls_len, const uint8_t* __restrict__ rhs,
+                                                   const float* __restrict__ rs, int rs_len,
+                                                   const int32_t* __restrict__ group_sizes, int g0, int El,
+                                                   int64_t M, int64_t K, int64_t N, void* __restrict__ out,
+                                                   int32_t* __restrict__ err) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TILE_BYTES];
+  __shared__ GroupTable gt;
+  __shared__ int tmp[kMaxLocal];
+  uint8_t* Xs = smem;                 // [row][k]
+  uint8_t* Ds = smem + TILE_BYTES;    // [row][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  build_groups(group_sizes, g0, El, M, 0, BM, err, gt, tmp);
+  const int KTo = static_cast<int>(K / BM), NT = static_cast<int>(N / BN);
+  const int per_group = KTo * NT;
+  const int total = El * per_group;
+  int first, last, step;
+  xcd_share(total, first, last, step);
+
+  for (int t = first; t < last; t += step) {
+    const int g = t / per_group;
+    const int local = t % per_group;
+    const int kt_o = local % KTo, nt = local / KTo;   // k-tiles fastest: they share the dY tile
+    const int64_t k0 = static_cast<int64_t>(kt_o) * BM, n0 = static_cast<int64_t>(nt) * BN;
+    const int64_t r0 = gt.rows_off[g];
+    const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
+    const int RT = (m_g + BK - 1) / BK;
+
+    stage_t rx, rd;
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (RT > 0) {
+      tgmm_load(lhs, rhs, K, N, r0, m_g, k0, n0, 0, tid, rx, rd);
+      __syncthreads();
+      stash_tiles(Xs, Ds, tid, rx, rd);
+      __syncthreads();
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt + 1 < RT) tgmm_load(lhs, rhs, K, N, r0, m_g, k0, n0, rt + 1, tid, rx, rd);
+        v8i a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = frag_tr(Xs, wm * 64 + i * 16, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = frag_tr(Ds, wn * 64 + j * 16, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f8(a[i], b[j], acc[i][j]);
+        __syncthreads();
+        if (rt + 1 < RT) {
+          stash_tiles(Xs, Ds, tid, rx, rd);
+          __syncthreads();
+        }
+      }
+    }
+    // epilogue: out[g, k, n] = ls[k] * rs[n] * acc
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
+      const float rsn = rs_len == 1 ? rs[0] : rs[n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int64_t k = k0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
+          const float lsk = ls_len == 1 ? ls[0] : ls[k];
+          const float o = (lsk * rsn) * acc[i][j][v];
+          const int64_t idx = (static_cast<int64_t>(g) * K + k) * N + n;
+          if (OUT_BF16)
+            static_cast<uint16_t*>(out)[idx] = f32_to_bf16(o);
+          else
+            static_cast<float*>(out)[idx] = o;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t lhs_scale_len,
+                            const uint8_t* rhs, const float* rhs_scale, int32_t rhs_scale_len,
+                            const int32_t* group_sizes, int32_t E, int32_t group_offset,
+                            int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
+                            void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0 || K % 128 || N % 128) return MOE_ERR_SHAPE;
+  if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 ||
+      num_local_experts > moe::tile::kMaxLocal || group_offset + num_local_experts > E)
+    return MOE_ERR_SHAPE;
+  if (M > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (lhs_scale_len != 1 && lhs_scale_len != K) return MOE_ERR_UNSUPPORTED;
+  if (rhs_scale_len != 1 && rhs_scale_len != N) return MOE_ERR_UNSUPPORTED;
+  if (out_dtype == MOE_DTYPE_DEFAULT) out_dtype = MOE_F32;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  const int El = num_local_experts;
+  if (El == 0) return MOE_OK;
+  if (!out || !group_sizes || !lhs_scale || !rhs_scale) return MOE_ERR_NULL;
+  if (M > 0 && (!lhs || !rhs)) return MOE_ERR_NULL;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe::tile::kHdr) return MOE_ERR_WORKSPACE;
+  if (static_cast<int64_t>(El) * (K / 128) * (N / 128) > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* err = static_cast<int32_t*>(ws);
+  const int64_t ub = static_cast<int64_t>(El) * (K / moe::tile::BM) * (N / moe::tile::BN);
+  int64_t grid = 2LL * moe::tile::num_cus();
+  if (ub < grid) grid = ub;
+  if (grid < 8) grid = 8;
+  if (out_dtype == MOE_BF16)
+    moe::tgmm_kernel<true><<<static_cast<unsigned>(grid), 256, 0, st>>>(
+        lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, group_sizes, group_offset, El, M, K, N, out, err);
+  else
+    moe::tgmm_kernel<false><<<static_cast<unsigned>(grid), 256, 0, st>>>(
+        lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, group_sizes, group_offset, El, M, K, N, out, err);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

@@ -1,0 +1,192 @@
+// Shared pieces of the grouped-matmul kernels: the fp8 MFMA, the local group
+// table every workgroup builds from group_sizes, the XCD-aware split of a tile
+// range, and the LDS fragment readers of the 144-byte-padded staging layout.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+namespace tile {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+// four 16-byte chunks held in registers between a global load and an LDS store
+typedef uint32_t stage_t __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 128, BN = 128, BK = 128;
+constexpr int LDS_STRIDE = BK + 16;         // bytes per staged row
+constexpr int TILE_BYTES = 128 * LDS_STRIDE;
+constexpr int kHdr = 256;                   // workspace header (error word)
+constexpr int kMaxLocal = 1024;
+
+__device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Fragment of a K-contiguous staged tile: 32 bytes at row `row`, byte 32*grp.
+__device__ __forceinline__ v8i frag_rows(const uint8_t* lds, int row, int grp) {
+  const uint4* p = reinterpret_cast<const uint4*>(lds + row * LDS_STRIDE + 32 * grp);
+  const uint4 lo = p[0], hi = p[1];
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+// Fragment of a [contraction][column] staged tile for columns col0..col0+15,
+// through four transpose loads.
+__device__ __forceinline__ v8i frag_tr(const uint8_t* lds, int col0, int lane) {
+  const int grp = lane >> 4, L = lane & 15;
+  v8i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 32 * grp + 8 * q + (L >> 1);
+    const uint8_t* p = lds + row * LDS_STRIDE + col0 + 8 * (L & 1);
+    const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p));
+    r[2 * q] = t[0];
+    r[2 * q + 1] = t[1];
+  }
+  return r;
+}
+
+// Local group table, computed by every workgroup from group_sizes.
+struct GroupTable {
+  int rows_off[kMaxLocal + 1];   // first compact row of each local group
+  int tiles_off[kMaxLocal + 1];  // first tile of each local group
+};
+
+// Exclusive scan of v[0..n) into out[0..n] (out[n] = total) by wave 0.
+__device__ void wave0_scan(const int* v, int* out, int n) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int carry = 0;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + lane;
+    const int x = i < n ? v[i] : 0;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (i < n) out[i] = carry + incl - x;
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) out[n] = carry;
+}
+
+// Fill the table: clamps negative sizes and rows past max_rows (flagging
+// the error word) so that every tile stays inside the buffers; a group of m
+// rows owns ceil(m / bm) * tiles_per_mrow tiles.
+__device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, int El, int64_t max_rows,
+                             int tiles_per_mrow, int bm, int32_t* err, GroupTable& gt, int* tmp) {
+  for (int g = threadIdx.x; g < El; g += blockDim.x) {
+    int m = group_sizes[g0 + g];
+    if (m < 0) {
+      if (blockIdx.x == 0) raise_error(err, MOE_DEVERR_GROUP_SIZE);
+      m = 0;
+    }
+    tmp[g] = m;
+  }
+  __syncthreads();
+  wave0_scan(tmp, gt.rows_off, El);
+  __syncthreads();
+  for (int g = threadIdx.x; g < El; g += blockDim.x) {
+    int64_t lo = gt.rows_off[g], hi = gt.rows_off[g + 1];
+    if (hi > max_rows) {
+      if (blockIdx.x == 0) raise_error(err, MOE_DEVERR_ROWS);
+      hi = max_rows;
+      if (lo > hi) lo = hi;
+    }
+    tmp[g] = static_cast<int>(hi - lo);   // clamped rows
+  }
+  __syncthreads();
+  // recompute offsets from clamped sizes; then tiles
+  wave0_scan(tmp, gt.rows_off, El);
+  __syncthreads();
+  for (int g = threadIdx.x; g < El; g += blockDim.x) {
+    const int m = gt.rows_off[g + 1] - gt.rows_off[g];
+    tmp[g] = tiles_per_mrow > 0 ? ((m + bm - 1) / bm) * tiles_per_mrow : 1;
+  }
+  __syncthreads();
+  wave0_scan(tmp, gt.tiles_off, El);
+  __syncthreads();
+}
+
+__device__ __forceinline__ int find_group(const GroupTable& gt, int El, int t) {
+  int lo = 0, hi = El - 1;             // last g with tiles_off[g] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gt.tiles_off[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The XCD-contiguous share of [0, total) for this workgroup: tiles
+// first, first + step, ... < last.
+__device__ __forceinline__ void xcd_share(int total, int& first, int& last, int& step) {
+  const int nxcd = 8;
+  const int x = blockIdx.x % nxcd;
+  const int nb = gridDim.x;
+  const int in_x = (nb - x + nxcd - 1) / nxcd;     // workgroups on this XCD
+  const int lo = static_cast<int>((static_cast<int64_t>(total) * x) / nxcd);
+  const int hi = static_cast<int>((static_cast<int64_t>(total) * (x + 1)) / nxcd);
+  first = lo + static_cast<int>(blockIdx.x / nxcd);
+  last = hi;
+  step = in_x;
+}
+
+__device__ __forceinline__ void put4(stage_t& s, int i, const uint4& v) {
+  s[4 * i] = v.x; s[4 * i + 1] = v.y; s[4 * i + 2] = v.z; s[4 * i + 3] = v.w;
+}
+__device__ __forceinline__ uint4 get4(const stage_t& s, int i) {
+  return make_uint4(s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]);
+}
+
+// tgmm staging: rows of the group (past its end: zeros, they must not add).
+__device__ __forceinline__ void tgmm_load(const uint8_t* __restrict__ lhs, const uint8_t* __restrict__ rhs, int64_t K,
+                                          int64_t N, int64_t r0, int m_g, int64_t k0, int64_t n0, int rt, int tid,
+                                          stage_t& rx, stage_t& rd) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, cb = (c & 7) * 16;
+    const int rr = rt * BK + r;
+    uint4 x = make_uint4(0, 0, 0, 0), d = make_uint4(0, 0, 0, 0);
+    if (rr < m_g) {
+      x = *reinterpret_cast<const uint4*>(lhs + (r0 + rr) * K + k0 + cb);
+      d = *reinterpret_cast<const uint4*>(rhs + (r0 + rr) * N + n0 + cb);
+    }
+    put4(rx, i, x);
+    put4(rd, i, d);
+  }
+}
+
+__device__ __forceinline__ void stash_tiles(uint8_t* As, uint8_t* Bs, int tid, const stage_t& ra,
+                                            const stage_t& rb) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c >> 3, cb = (c & 7) * 16;
+    *reinterpret_cast<uint4*>(As + r * LDS_STRIDE + cb) = get4(ra, i);
+    *reinterpret_cast<uint4*>(Bs + r * LDS_STRIDE + cb) = get4(rb, i);
+  }
+}
+
+inline int num_cus() {
+  static int g_num_cus = 0;
+  if (g_num_cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+}  // namespace tile
+}  // namespace moe
