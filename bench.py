@@ -20,8 +20,10 @@ on the stream the kernels run on (torch's current stream).
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -34,6 +36,33 @@ sys.path.insert(0, ROOT)
 METRIC = "fp8 MoE GMM TFLOP/s (% fp8 MFMA peak) + sort/gather HBM GB/s, 1×MI355X"
 PEAK_FP8_TFLOPS = 5000.0      # dense fp8 MFMA, MI355X
 PEAK_HBM_GBPS = 8000.0        # HBM3E
+# sources of the dominant kernel; a counter summary applies only to the build it was taken on
+GMM_SOURCES = ("moe_fp8_grouped_amd/csrc/gmm.hip", "moe_fp8_grouped_amd/csrc/tile_common.hpp",
+               "moe_fp8_grouped_amd/csrc/common.hpp")
+GMM_COUNTERS = "profiles/gmm_kernel__gated-ffn-fwd__hbm_counters.md"
+
+
+def gmm_source_hash():
+    h = hashlib.sha256()
+    for rel in GMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gmm launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
+    summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, GMM_COUNTERS)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"^- source_hash: (\w+)", text, re.M)
+    m_bytes = re.search(r"^- hbm_bytes_per_launch: (\d+)", text, re.M)
+    if not m_hash or not m_bytes or m_hash.group(1) != gmm_source_hash():
+        return None
+    return int(m_bytes.group(1))
 
 
 def step_accounting(path, n, U):
@@ -147,8 +176,12 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
     gmm_us = sum(kern[nm]["avg_us"] for nm in gmm_names)
     achieved_gbps = gmm_bytes / (gmm_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+            "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(),
             "kernel": "moe_gmm_fp8 (gmm_kernel)",
+            "launches_per_step": len(gmm_names),
+            "avg_launch_us": round(gmm_us / len(gmm_names), 2),
+            "alg_bytes_per_launch": int(gmm_bytes / len(gmm_names)),
+            "source_hash": gmm_source_hash(),
             "alg_intensity_flop_per_byte": round(gmm_flops / gmm_bytes, 1),
             "mfma_TFLOP_s": round(gmm_flops / (gmm_us * 1e-6) / 1e12, 1),
             "mfma_frac_fp8_peak": round(gmm_flops / (gmm_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)}
