@@ -39,6 +39,13 @@
 // results are staged through LDS so each 256-byte output row segment is
 // written with full 16-byte stores.
 //
+// Short groups: a group's last m-tile often holds only a few rows.  When the
+// remainder is at most BM/2 rows it is covered by wide tiles of BM/2 rows x
+// 2*BN columns (two n-tiles at once): the stage holds 128 A rows and 256 B
+// rows -- the same bytes and the same 12 loads per wave as a plain tile --
+// and each wave owns rows 0..127 and its own 64 columns, so such a tail costs
+// half a plain tile per n-tile.
+//
 // Scheduling: persistent workgroups (as many per CU as the LDS allows).
 // Each derives the local group table (row and tile offsets) from
 // group_sizes in LDS -- empty groups
@@ -66,52 +73,58 @@ __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >
 // a lane needs only two offsets per operand; the rest of the address is
 // uniform (scalar registers).
 struct LaneOff {
-  uint32_t v[2];
+  uint32_t v0, v1;
+  // arithmetic select: keeps the pair in registers
+  __device__ __forceinline__ uint32_t pick(int bit) const { return v0 ^ ((v0 ^ v1) & (0u - static_cast<uint32_t>(bit))); }
 };
 
 __device__ __forceinline__ LaneOff stage_lane_off(int lane, int64_t stride) {
   const int sub = lane >> 3, c0 = (lane & 7) ^ (sub >> 1);
   LaneOff o;
-  o.v[0] = static_cast<uint32_t>(sub * stride + 16 * c0);
-  o.v[1] = static_cast<uint32_t>(sub * stride + 16 * (c0 ^ 4));
+  o.v0 = static_cast<uint32_t>(sub * stride + 16 * c0);
+  o.v1 = static_cast<uint32_t>(sub * stride + 16 * (c0 ^ 4));
   return o;
 }
 
 // Swizzle bit of the instruction that fills rows R .. R+7 (R % 8 == 0).
 __device__ __forceinline__ int stage_bit(int R) { return ((R >> 3) & 1) ^ ((R >> 5) & 1); }
 
-// Direct-to-LDS load instruction i of one K step for wave `wave`: A rows
-// (BM/4)*wave + 8i .. +7 (i < BM/32) and B rows (BN/4)*wave + 8i .. +7 (i < BN/32).
-// tail: the tile reaches past the last lhs row, so lhs rows are clamped.
-template <int BM>
-__device__ __forceinline__ void issue_a(uint8_t* stage, const uint8_t* __restrict__ lhs, int64_t K, int64_t row0,
-                                        int64_t M, bool tail, int64_t kb, int wave, int lane, int i,
-                                        const LaneOff& offK) {
-  const int R = wave * (BM / 4) + i * 8;          // first staged row of this instruction
-  const int bit = stage_bit(R);
+// Load slot S (0 .. 11) of one K step for wave `wave`: one direct-to-LDS
+// instruction filling 8 staged rows.  A plain tile stages 256 A rows and 128
+// B rows (slots 0-7 A, 8-11 B); a wide tile 128 A rows and 256 B rows (slots
+// 0-3 A, 4-11 B) -- the same 48 KiB and the same 12 loads per wave, so the
+// pipeline's wait counts do not depend on the tile kind.  Each wave fills a
+// quarter of either operand.  tail: the tile reaches past the last lhs row,
+// so lhs rows are clamped.
+template <bool TRANS, int S>
+__device__ __forceinline__ void issue_slot(bool wide, uint8_t* stage, const uint8_t* __restrict__ lhs,
+                                           const uint8_t* __restrict__ wg, int64_t K, int64_t N, int64_t row0,
+                                           int64_t col0, int64_t M, bool tail, int64_t kb, int wave, int lane,
+                                           const LaneOff offK, const LaneOff offN) {
+  const int nA = wide ? 4 : 8;
+  const bool isA = S < nA;
   const uint8_t* src;
-  if (!tail) {
-    src = lhs + (row0 + R) * K + kb + offK.v[bit];
+  int dst;
+  if (isA) {
+    const int R = wave * (wide ? 32 : 64) + 8 * S;
+    const uint32_t off = offK.pick(stage_bit(R));
+    if (!tail) {
+      src = lhs + (row0 + R) * K + kb + off;
+    } else {
+      const int sub = lane >> 3;
+      const int64_t r = min(row0 + R + sub, M - 1);
+      src = lhs + r * K + kb + (off - static_cast<uint32_t>(sub * K));
+    }
+    dst = R * G_BK;
   } else {
-    const int sub = lane >> 3;
-    const int64_t r = min(row0 + R + sub, M - 1);
-    src = lhs + r * K + kb + (offK.v[bit] - static_cast<uint32_t>(sub * K));
+    const int R = wave * (wide ? 64 : 32) + 8 * (S - nA);
+    if (TRANS)      // staged row r = output column col0 + r
+      src = wg + (col0 + R) * K + kb + offK.pick(stage_bit(R));
+    else            // staged half R / 128 holds columns 128h.., staged row = contraction index
+      src = wg + (kb + (R & 127)) * N + col0 + 128 * (R >> 7) + offN.pick(stage_bit(R));
+    dst = (wide ? 128 : 256) * G_BK + R * G_BK;
   }
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + R * G_BK), 16, 0, 0);
-}
-
-template <bool TRANS, int BM, int BN>
-__device__ __forceinline__ void issue_b(uint8_t* stage, const uint8_t* __restrict__ wg, int64_t K, int64_t N,
-                                        int64_t col0, int64_t kb, int wave, int i, const LaneOff& offK,
-                                        const LaneOff& offN) {
-  const int R = wave * (BN / 4) + i * 8;
-  const int bit = stage_bit(R);
-  const uint8_t* src;
-  if (TRANS)        // staged row r = output column col0 + r
-    src = wg + (col0 + R) * K + kb + offK.v[bit];
-  else              // staged half R / 128 holds columns 128h.., staged row = contraction index
-    src = wg + (kb + (R & 127)) * N + col0 + 128 * (R >> 7) + offN.v[bit];
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + BM * G_BK + R * G_BK), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + dst), 16, 0, 0);
 }
 
 // LDS byte offsets of the two 16-byte chunks of MFMA fragment rows
@@ -204,7 +217,8 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: keeps staging addresses scalar
   const int wm = wave >> 1, wn = wave & 1;
   const int NT = static_cast<int>(N / BN);
-  build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem));
+  static_assert(BM == 2 * BN && MI == 8 && JN == 4, "wide tail tiles are BM/2 x 2BN with the same wave tiles");
+  build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), true);
   const int total = gt.tiles_off[El];
   const int n_rows = gt.rows_off[El];
   const int KT = static_cast<int>(K / G_BK);
@@ -214,28 +228,58 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
   xcd_share(total, first, last, step);
   const LaneOff offK = stage_lane_off(lane, K);
   const LaneOff offN = stage_lane_off(lane, N);
-  const FragOff fa = frag_off(wm * WM, lane);
-  const FragOff fb = frag_off(wn * WN, lane);
 
   for (int t = first; t < last; t += step) {
+    // ---- decode tile t of the group table (tiles of a group: n-tile major,
+    // m-tiles fastest; a short remainder of at most BM/2 rows is covered by
+    // wide tiles of two n-tiles each, placed after the two n-tiles' full
+    // m-tiles so they reuse the same weight columns from L2)
     const int g = find_group(gt, El, t);
     const int local = t - gt.tiles_off[g];
     const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
-    const int mtiles = (m_g + BM - 1) / BM;
-    const int nt = local / mtiles, mt = local % mtiles;
+    const int full = m_g / BM, rem = m_g - full * BM;
+    int nt, mt;
+    bool wide = false;
+    if (rem == 0 || rem > BM / 2) {
+      const int per = full + (rem ? 1 : 0);
+      nt = local / per;
+      mt = local - nt * per;
+    } else {
+      const int pairblk = 2 * full + 1, npair = NT / 2;
+      if (local < npair * pairblk) {
+        const int pr = local / pairblk, w = local - pr * pairblk;
+        if (w < 2 * full) {
+          const int h = w >= full ? 1 : 0;
+          nt = 2 * pr + h;
+          mt = w - h * full;
+        } else {
+          nt = 2 * pr;
+          mt = full;
+          wide = true;
+        }
+      } else {
+        nt = NT - 1;
+        mt = local - npair * pairblk;
+      }
+    }
     const int64_t row0 = gt.rows_off[g] + static_cast<int64_t>(mt) * BM;
     const int rows_here = min(BM, m_g - mt * BM);
     const int64_t col0 = static_cast<int64_t>(nt) * BN;
     const uint8_t* wg = rhs + static_cast<int64_t>(g) * K * N;
-    const bool tail = row0 + BM > M;
+    const int bm_t = wide ? BM / 2 : BM, bn_t = wide ? 2 * BN : BN;     // this tile's shape
+    const bool tail = row0 + bm_t > M;
+    // this wave's output block: rows rbase .. +127, columns cbase .. +63
+    const int rbase = wide ? 0 : wm * WM, cbase = wide ? wave * 64 : wn * WN;
+    const FragOff fa = frag_off(rbase, lane);
+    const FragOff fb = frag_off(cbase, lane);
     // scale-column block of each of this lane's output columns
     uint32_t cblk[JN];
 #pragma unroll
-    for (int j = 0; j < JN; ++j) cblk[j] = static_cast<uint32_t>(col0 + wn * WN + j * 16 + (lane & 15)) / ncol_blk;
+    for (int j = 0; j < JN; ++j) cblk[j] = static_cast<uint32_t>(col0 + cbase + j * 16 + (lane & 15)) / ncol_blk;
     const float* rs_g = rs + static_cast<int64_t>(g) * Kb * Nb;
     // blockwise scales ride the stages: lane l of wave w stages the scale of
     // tile column 64w + l (clamped to the tile; surplus lanes repeat a column)
-    const float* rs_lane = rs_g + static_cast<uint32_t>(col0 + min(wave * 64 + lane, BN - 1)) / ncol_blk;
+    const float* rs_lane = rs_g + static_cast<uint32_t>(col0 + min(wave * 64 + lane, bn_t - 1)) / ncol_blk;
 
     v4f acc[MI][JN];
 #pragma unroll
@@ -251,11 +295,12 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
     for (int s = 0; s < NST - 1; ++s) {
       if (s < KT) {
         const int64_t kb = static_cast<int64_t>(s) * G_BK;
-#pragma unroll
-        for (int i = 0; i < BM / 32; ++i) issue_a<BM>(smem + s * STAGE, lhs, K, row0, M, tail, kb, wave, lane, i, offK);
-#pragma unroll
-        for (int i = 0; i < BN / 32; ++i)
-          issue_b<TRANS, BM, BN>(smem + s * STAGE, wg, K, N, col0, kb, wave, i, offK, offN);
+#define MOE_SLOT(S, stg, kbv) \
+  issue_slot<TRANS, S>(wide, stg, lhs, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
+        MOE_SLOT(0, smem + s * STAGE, kb); MOE_SLOT(1, smem + s * STAGE, kb); MOE_SLOT(2, smem + s * STAGE, kb);
+        MOE_SLOT(3, smem + s * STAGE, kb); MOE_SLOT(4, smem + s * STAGE, kb); MOE_SLOT(5, smem + s * STAGE, kb);
+        MOE_SLOT(6, smem + s * STAGE, kb); MOE_SLOT(7, smem + s * STAGE, kb); MOE_SLOT(8, smem + s * STAGE, kb);
+        MOE_SLOT(9, smem + s * STAGE, kb); MOE_SLOT(10, smem + s * STAGE, kb); MOE_SLOT(11, smem + s * STAGE, kb);
         if (KBLOCKS)
           __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(s / steps_per_block) * Nb,
                                            (lds_void*)(smem + s * STAGE + C::SC_OFF + wave * 256), 4, 0, 0);
@@ -275,17 +320,17 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       const int64_t kb_next = static_cast<int64_t>(ks) * G_BK;
       uint8_t* nxt = smem + (ks % NST) * STAGE;
       const uint8_t* As = smem + (kt % NST) * STAGE;
-      const uint8_t* Bs = As + BM * G_BK;
+      const uint8_t* Bs = As + bm_t * G_BK;
       float s_col[JN];
       if (KBLOCKS) {
-        const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + wn * WN + (lane & 15);
+        const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + (lane & 15);
 #pragma unroll
         for (int j = 0; j < JN; ++j) s_col[j] = sc[j * 16];
       }
       v8i b[JN];
 #pragma unroll
       for (int j = 0; j < JN; ++j) {
-        const int n0 = wn * WN + j * 16;
+        const int n0 = cbase + j * 16;
         if (TRANS)
           b[j] = frag_i(Bs, fb, j);
         else
@@ -294,17 +339,19 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       // MI rounds: an A fragment, this round's share of the loads of step ks,
       // then the round's MFMAs -- so memory back-pressure on the loads never
       // holds up a long run of MFMA issue
-      constexpr int LA = BM / 32, LB = BN / 32;
+      // (round i issues load slots 3i/2 .. (3i+3)/2 - 1: 12 over the 8 rounds)
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const v8i a = frag_i(As, fa, i);
         if (more) {
-#pragma unroll
-          for (int u = i * LA / MI; u < (i + 1) * LA / MI; ++u)
-            issue_a<BM>(nxt, lhs, K, row0, M, tail, kb_next, wave, lane, u, offK);
-#pragma unroll
-          for (int u = i * LB / MI; u < (i + 1) * LB / MI; ++u)
-            issue_b<TRANS, BM, BN>(nxt, wg, K, N, col0, kb_next, wave, u, offK, offN);
+          if (i == 0) { MOE_SLOT(0, nxt, kb_next); }
+          if (i == 1) { MOE_SLOT(1, nxt, kb_next); MOE_SLOT(2, nxt, kb_next); }
+          if (i == 2) { MOE_SLOT(3, nxt, kb_next); }
+          if (i == 3) { MOE_SLOT(4, nxt, kb_next); MOE_SLOT(5, nxt, kb_next); }
+          if (i == 4) { MOE_SLOT(6, nxt, kb_next); }
+          if (i == 5) { MOE_SLOT(7, nxt, kb_next); MOE_SLOT(8, nxt, kb_next); }
+          if (i == 6) { MOE_SLOT(9, nxt, kb_next); }
+          if (i == 7) { MOE_SLOT(10, nxt, kb_next); MOE_SLOT(11, nxt, kb_next); }
           if (KBLOCKS && i == 0)
             __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(ks / steps_per_block) * Nb,
                                              (lds_void*)(nxt + C::SC_OFF + wave * 256), 4, 0, 0);
@@ -327,19 +374,18 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < JN; ++j) s_out[j] = KBLOCKS ? 1.0f : rs_g[cblk[j]];
     if (OUT_BF16) {
-      constexpr int CH = BN / 8;                // 16-byte chunks per output row
-      constexpr int OS = C::OUT_STRIDE;
+      const int ch_log = wide ? 5 : 4;          // log2 of the 16-byte chunks per output row
+      const int OS = bn_t + 8;
       __syncthreads();                          // all waves are done with the operand stages
-      // [BM rows][BN cols] bf16 with rows padded to OS elements: the four 16-lane
-      // groups of a write (rows 4 apart) land 16 banks apart, and every address is
-      // the lane's base plus a constant
+      // [bm_t rows][bn_t cols] bf16 with rows padded to OS elements: the four
+      // 16-lane groups of a write (rows 4 apart) land 16 banks apart
       uint16_t* st = reinterpret_cast<uint16_t*>(smem);
-      uint16_t* st_lane = st + (wm * WM + 4 * (lane >> 4)) * OS + wn * WN + (lane & 15);
+      uint16_t* st_lane = st + (rbase + 4 * (lane >> 4)) * OS + cbase + (lane & 15);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float lsr = ls_tile[wm * WM + i * 16 + 4 * (lane >> 4) + v];
+          const float lsr = ls_tile[rbase + i * 16 + 4 * (lane >> 4) + v];
 #pragma unroll
           for (int j = 0; j < JN; ++j)
             st_lane[(i * 16 + v) * OS + j * 16] = f32_to_bf16(lsr * (acc[i][j][v] * s_out[j]));
@@ -348,9 +394,9 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       __syncthreads();
       uint16_t* o = static_cast<uint16_t*>(out);
 #pragma unroll 4
-      for (int it = 0; it < BM * CH / G_THREADS; ++it) {
+      for (int it = 0; it < BM * (BN / 8) / G_THREADS; ++it) {     // same chunk count for both shapes
         const int id = it * G_THREADS + tid;
-        const int r = id / CH, c = id % CH;
+        const int r = id >> ch_log, c = id & ((1 << ch_log) - 1);
         if (r < rows_here) {
           const uint4 v = *reinterpret_cast<const uint4*>(st + r * OS + c * 8);
           *reinterpret_cast<uint4*>(o + (row0 + r) * N + col0 + c * 8) = v;
@@ -361,12 +407,12 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int r = wm * WM + i * 16 + 4 * (lane >> 4) + v;
+          const int r = rbase + i * 16 + 4 * (lane >> 4) + v;
           if (r >= rows_here) continue;
           const float lsr = ls_tile[r];
 #pragma unroll
           for (int j = 0; j < JN; ++j) {
-            const int64_t col = col0 + wn * WN + j * 16 + (lane & 15);
+            const int64_t col = col0 + cbase + j * 16 + (lane & 15);
             static_cast<float*>(out)[(row0 + r) * N + col] = lsr * (acc[i][j][v] * s_out[j]);
           }
         }
@@ -374,6 +420,7 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
     }
   }
 
+#undef MOE_SLOT
   // rows [n, M) are zero
   const int64_t zero_rows = M - n_rows;
   if (zero_rows > 0) {

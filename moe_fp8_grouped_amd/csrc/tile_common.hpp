@@ -77,11 +77,24 @@ __device__ void wave0_scan(const int* v, int* out, int n) {
   if (lane == 0) out[n] = carry;
 }
 
+// Tiles of a group of m rows.  Plain: ceil(m / bm) m-tiles per n-tile.  With
+// wide tails (gmm): full m-tiles of bm rows, and a remainder of at most bm/2
+// rows is covered by tiles of bm/2 rows x two n-tiles (an odd last n-tile
+// keeps a plain tail tile).
+__device__ __forceinline__ int group_tiles(int m, int bm, int nt, bool wide_tail) {
+  if (nt <= 0) return 1;
+  const int full = m / bm, rem = m - full * bm;
+  if (!wide_tail || rem == 0 || rem > bm / 2) return (full + (rem ? 1 : 0)) * nt;
+  return (nt / 2) * (2 * full + 1) + (nt & 1) * (full + 1);
+}
+
 // Fill the table: clamps negative sizes and rows past max_rows (flagging
 // the error word) so that every tile stays inside the buffers; a group of m
-// rows owns ceil(m / bm) * tiles_per_mrow tiles.
+// rows owns group_tiles(m, bm, tiles_per_mrow, wide_tail) tiles
+// (tiles_per_mrow = 0: one entry per group).
 __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, int El, int64_t max_rows,
-                             int tiles_per_mrow, int bm, int32_t* err, GroupTable& gt, int* tmp) {
+                             int tiles_per_mrow, int bm, int32_t* err, GroupTable& gt, int* tmp,
+                             bool wide_tail = false) {
   for (int g = threadIdx.x; g < El; g += blockDim.x) {
     int m = group_sizes[g0 + g];
     if (m < 0) {
@@ -108,7 +121,7 @@ __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, in
   __syncthreads();
   for (int g = threadIdx.x; g < El; g += blockDim.x) {
     const int m = gt.rows_off[g + 1] - gt.rows_off[g];
-    tmp[g] = tiles_per_mrow > 0 ? ((m + bm - 1) / bm) * tiles_per_mrow : 1;
+    tmp[g] = group_tiles(m, bm, tiles_per_mrow, wide_tail);
   }
   __syncthreads();
   wave0_scan(tmp, gt.tiles_off, El);
