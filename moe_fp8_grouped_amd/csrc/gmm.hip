@@ -11,8 +11,7 @@
 // waves form a 2 x 2 grid; wave w owns rows (BM/2)*(w/2) .. and columns
 // (BN/2)*(w%2) ..: (BM/32) x (BN/32) MFMA tiles of 16 x 16 whose float
 // accumulators live in the accumulation registers.  An MFMA lane l supplies
-// row l%16 and contraction bytes 32*(l/16) .. +31 of each operand; output
-// lane l holds rows 4*(l/16) + v of column l%16.
+// row l%16 and contraction bytes 32*(l/16) .. +31 of each operand.
 //
 // Staging: NST LDS stages (A: BM rows, B: BN rows, 128 bytes each, plus a
 // 1 KiB slot for the step's blockwise weight scales), filled straight from
@@ -32,12 +31,16 @@
 //  * rhs stored [E, K, N] is staged as [128 k][128 n] halves and read with
 //    ds_read_b64_tr_b8 (within a 16-lane group, lane i gets byte i%8 of the
 //    chunks addressed by lanes 2j + i/8, j = 0..7).
+// The product is formed transposed per 16 x 16 block (the MFMA gets the
+// weight fragment as its first operand), so output lane l holds one output
+// row and four consecutive output columns.
 // Scales: per-channel weight scales multiply at the end; blockwise K scales
 // (K/Kb a multiple of 128) are folded every K step, tot += rs * P_step,
 // which is the same sum as rs * (sum of the block's steps) up to rounding.
-// The lhs row scale is applied in float32 before the single rounding; bf16
-// results are staged through LDS so each 256-byte output row segment is
-// written with full 16-byte stores.
+// The lhs row scale is applied in float32 before the single rounding to
+// bfloat16 (round to nearest even, the hardware's packed conversion); each
+// lane writes its four columns as one 8-byte LDS store, and the staged tile
+// goes out with full 16-byte stores per output row segment.
 //
 // Short groups: a group's last m-tile often holds only a few rows.  When the
 // remainder is at most BM/2 rows it is covered by wide tiles of BM/2 rows x
@@ -125,6 +128,38 @@ __device__ __forceinline__ void issue_slot(bool wide, uint8_t* stage, const uint
     dst = (wide ? 128 : 256) * G_BK + R * G_BK;
   }
   __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + dst), 16, 0, 0);
+}
+
+// Two floats to packed bfloat16 (low half from lo), rounding to nearest even
+// with the gfx950 conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), bf2));
+}
+
+// Four 16-byte LDS reads at p + {0, 16, 32, 48} floats, completed before
+// returning.  One asm block: the blockwise-scale slot is filled by direct
+// loads whose completion the caller has already waited for, and the
+// compiler's own tracking of those loads would add a wait for every load
+// still in flight before a plain read of it.
+__device__ __forceinline__ void lds_read_4x16f(const float* p, float4 (&r)[4]) {
+  typedef const __attribute__((address_space(3))) float lds_f32;
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_f32*)p));   // LDS byte offset
+  v4f t0, t1, t2, t3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:64\n\t"
+      "ds_read_b128 %2, %4 offset:128\n\t"
+      "ds_read_b128 %3, %4 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)
+      : "v"(a)
+      : "memory");
+  r[0] = make_float4(t0[0], t0[1], t0[2], t0[3]);
+  r[1] = make_float4(t1[0], t1[1], t1[2], t1[3]);
+  r[2] = make_float4(t2[0], t2[1], t2[2], t2[3]);
+  r[3] = make_float4(t3[0], t3[1], t3[2], t3[3]);
 }
 
 // LDS byte offsets of the two 16-byte chunks of MFMA fragment rows
@@ -272,10 +307,6 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
     const int rbase = wide ? 0 : wm * WM, cbase = wide ? wave * 64 : wn * WN;
     const FragOff fa = frag_off(rbase, lane);
     const FragOff fb = frag_off(cbase, lane);
-    // scale-column block of each of this lane's output columns
-    uint32_t cblk[JN];
-#pragma unroll
-    for (int j = 0; j < JN; ++j) cblk[j] = static_cast<uint32_t>(col0 + cbase + j * 16 + (lane & 15)) / ncol_blk;
     const float* rs_g = rs + static_cast<int64_t>(g) * Kb * Nb;
     // blockwise scales ride the stages: lane l of wave w stages the scale of
     // tile column 64w + l (clamped to the tile; surplus lanes repeat a column)
@@ -321,11 +352,11 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       uint8_t* nxt = smem + (ks % NST) * STAGE;
       const uint8_t* As = smem + (kt % NST) * STAGE;
       const uint8_t* Bs = As + bm_t * G_BK;
-      float s_col[JN];
+      float4 s_col[JN];    // scales of this lane's output columns 16j + 4(l/16) .. +3
       if (KBLOCKS) {
-        const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < JN; ++j) s_col[j] = sc[j * 16];
+        const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + 4 * (lane >> 4);
+        static_assert(JN == 4, "four column groups per scale read");
+        lds_read_4x16f(sc, s_col);
       }
       v8i b[JN];
 #pragma unroll
@@ -359,36 +390,51 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
           if (KBLOCKS) {
-            const v4f p = mfma_f8(a, b[j], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(s_col[j], p[v], acc[i][j][v]);
+            const v4f p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
+            acc[i][j][0] = fmaf(s_col[j].x, p[0], acc[i][j][0]);
+            acc[i][j][1] = fmaf(s_col[j].y, p[1], acc[i][j][1]);
+            acc[i][j][2] = fmaf(s_col[j].z, p[2], acc[i][j][2]);
+            acc[i][j][3] = fmaf(s_col[j].w, p[3], acc[i][j][3]);
           } else {
-            acc[i][j] = mfma_f8(a, b[j], acc[i][j]);
+            acc[i][j] = mfma_f8(b[j], a, acc[i][j]);
           }
         }
       }
     }
 
     // ---- epilogue: out = ls[row] * (rs[col] *) acc
-    float s_out[JN];
+    // The product is formed transposed per 16 x 16 block (D = B^T A^T), so
+    // lane l holds output row rbase + 16i + l%16 and the four consecutive
+    // columns cbase + 16j + 4(l/16) .. +3.
+    float4 s_out[JN];
 #pragma unroll
-    for (int j = 0; j < JN; ++j) s_out[j] = KBLOCKS ? 1.0f : rs_g[cblk[j]];
+    for (int j = 0; j < JN; ++j) {
+      const int64_t c = col0 + cbase + j * 16 + 4 * (lane >> 4);
+      if (KBLOCKS)
+        s_out[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+      else if (ncol_blk == 1)
+        s_out[j] = *reinterpret_cast<const float4*>(rs_g + c);
+      else
+        s_out[j] = make_float4(rs_g[static_cast<uint32_t>(c) / ncol_blk], rs_g[static_cast<uint32_t>(c + 1) / ncol_blk],
+                               rs_g[static_cast<uint32_t>(c + 2) / ncol_blk], rs_g[static_cast<uint32_t>(c + 3) / ncol_blk]);
+    }
     if (OUT_BF16) {
       const int ch_log = wide ? 5 : 4;          // log2 of the 16-byte chunks per output row
       const int OS = bn_t + 8;
       __syncthreads();                          // all waves are done with the operand stages
-      // [bm_t rows][bn_t cols] bf16 with rows padded to OS elements: the four
-      // 16-lane groups of a write (rows 4 apart) land 16 banks apart
+      // [bm_t rows][bn_t cols] bf16 with rows padded to OS elements (OS/2 = 4 mod
+      // 64 dwords): each half-wave's 8-byte writes (16 rows x two 8-byte
+      // column steps) land on distinct bank pairs
       uint16_t* st = reinterpret_cast<uint16_t*>(smem);
-      uint16_t* st_lane = st + (rbase + 4 * (lane >> 4)) * OS + cbase + (lane & 15);
+      uint16_t* st_lane = st + (rbase + (lane & 15)) * OS + cbase + 4 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        const float lsr = ls_tile[rbase + i * 16 + (lane & 15)];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float lsr = ls_tile[rbase + i * 16 + 4 * (lane >> 4) + v];
-#pragma unroll
-          for (int j = 0; j < JN; ++j)
-            st_lane[(i * 16 + v) * OS + j * 16] = f32_to_bf16(lsr * (acc[i][j][v] * s_out[j]));
+        for (int j = 0; j < JN; ++j) {
+          const uint32_t lo = pack_bf16x2(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y));
+          const uint32_t hi = pack_bf16x2(lsr * (acc[i][j][2] * s_out[j].z), lsr * (acc[i][j][3] * s_out[j].w));
+          *reinterpret_cast<uint2*>(st_lane + i * 16 * OS + j * 16) = make_uint2(lo, hi);
         }
       }
       __syncthreads();
@@ -405,17 +451,15 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
     } else {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        const int r = rbase + i * 16 + (lane & 15);
+        if (r >= rows_here) continue;
+        const float lsr = ls_tile[r];
+        float* o = static_cast<float*>(out) + (row0 + r) * N + col0 + cbase + 4 * (lane >> 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = rbase + i * 16 + 4 * (lane >> 4) + v;
-          if (r >= rows_here) continue;
-          const float lsr = ls_tile[r];
-#pragma unroll
-          for (int j = 0; j < JN; ++j) {
-            const int64_t col = col0 + cbase + j * 16 + (lane & 15);
-            static_cast<float*>(out)[(row0 + r) * N + col] = lsr * (acc[i][j][v] * s_out[j]);
-          }
-        }
+        for (int j = 0; j < JN; ++j)
+          *reinterpret_cast<float4*>(o + j * 16) =
+              make_float4(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y),
+                          lsr * (acc[i][j][2] * s_out[j].z), lsr * (acc[i][j][3] * s_out[j].w));
       }
     }
   }
