@@ -318,9 +318,9 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
 #pragma unroll
       for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();      // the previous tile's epilogue is done with the LDS
-    // the tile's lhs row scales, read once into LDS for the epilogue
-    for (int r = tid; r < BM; r += G_THREADS) ls_tile[r] = r < rows_here ? (ls_per_row ? ls[row0 + r] : ls[0]) : 0.0f;
+    // the previous tile's epilogue is done with the LDS (a bare barrier: its
+    // output stores need not have completed)
+    step_barrier();
     // prologue: stages 0 .. NST-2 in flight
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s) {
@@ -335,6 +335,10 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
         if (KBLOCKS)
           __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(s / steps_per_block) * Nb,
                                            (lds_void*)(smem + s * STAGE + C::SC_OFF + wave * 256), 4, 0, 0);
+        if (s == 0) {   // the tile's lhs row scales ride its first stage (rows past the tile repeat its last)
+          const int r = min(wave * 64 + lane, rows_here - 1);
+          __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? row0 + r : 0), (lds_void*)(ls_tile + wave * 64), 4, 0, 0);
+        }
       }
     }
 
