@@ -6,12 +6,14 @@
 // "Keep qwix out of tpu-inference's fused MoE kernel and pre-quantize
 // weights": 32-bit accumulator, [E, blocks, 1, N] weight scales).
 //
-// Workgroup tile BM x BN x (K step 128), 256 threads, one wave per SIMD
-// (the shipped configuration: BM = 256, BN = 128, three LDS stages).  The
-// waves form a 2 x 2 grid; wave w owns rows (BM/2)*(w/2) .. and columns
-// (BN/2)*(w%2) ..: (BM/32) x (BN/32) MFMA tiles of 16 x 16 whose float
-// accumulators live in the accumulation registers.  An MFMA lane l supplies
-// row l%16 and contraction bytes 32*(l/16) .. +31 of each operand.
+// Workgroup tile BM x BN x (K step 128) with NW waves (the shipped
+// configuration: BM = 256, BN = 128, three LDS stages, 8 waves = two per
+// SIMD).  The waves form a 4 x 2 grid of 64 x 64 wave tiles, 4 x 4 MFMA
+// tiles of 16 x 16 each, whose float accumulators stay in registers.  Two
+// waves per SIMD: direct-to-LDS loads are issue-limited per wave, and a
+// second wave keeps the matrix core busy while the other issues its loads.
+// An MFMA lane l supplies row l%16 and contraction bytes 32*(l/16) .. +31 of
+// each operand.
 //
 // Staging: NST LDS stages (A: BM rows, B: BN rows, 128 bytes each, plus a
 // 1 KiB slot for the step's blockwise weight scales), filled straight from
@@ -45,9 +47,9 @@
 // Short groups: a group's last m-tile often holds only a few rows.  When the
 // remainder is at most BM/2 rows it is covered by wide tiles of BM/2 rows x
 // 2*BN columns (two n-tiles at once): the stage holds 128 A rows and 256 B
-// rows -- the same bytes and the same 12 loads per wave as a plain tile --
-// and each wave owns rows 0..127 and its own 64 columns, so such a tail costs
-// half a plain tile per n-tile.
+// rows -- the same bytes and the same loads per wave as a plain tile --
+// and the waves split it into the same 64 x 64 wave tiles, so such a tail costs
+// half a plain tile per n-tile (the wide tile's wave grid is 2 x 4).
 //
 // Scheduling: persistent workgroups (as many per CU as the LDS allows).
 // Each derives the local group table (row and tile offsets) from
@@ -64,7 +66,6 @@ namespace {
 using namespace tile;
 
 constexpr int G_BK = 128;
-constexpr int G_THREADS = 256;
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 5) & 1) << 2); }
@@ -92,24 +93,25 @@ __device__ __forceinline__ LaneOff stage_lane_off(int lane, int64_t stride) {
 // Swizzle bit of the instruction that fills rows R .. R+7 (R % 8 == 0).
 __device__ __forceinline__ int stage_bit(int R) { return ((R >> 3) & 1) ^ ((R >> 5) & 1); }
 
-// Load slot S (0 .. 11) of one K step for wave `wave`: one direct-to-LDS
-// instruction filling 8 staged rows.  A plain tile stages 256 A rows and 128
-// B rows (slots 0-7 A, 8-11 B); a wide tile 128 A rows and 256 B rows (slots
-// 0-3 A, 4-11 B) -- the same 48 KiB and the same 12 loads per wave, so the
-// pipeline's wait counts do not depend on the tile kind.  Each wave fills a
-// quarter of either operand.  tail: the tile reaches past the last lhs row,
+// Load slot S (0 .. 48/NW - 1) of one K step for wave `wave` of NW: one
+// direct-to-LDS instruction filling 8 staged rows.  A plain tile stages 256
+// A rows and 128 B rows; a wide tile 128 A rows and 256 B rows -- the same
+// 48 KiB and the same 48/NW loads per wave, so the pipeline's wait counts do
+// not depend on the tile kind.  Each wave fills 1/NW of either operand; its
+// first slots load A.  tail: the tile reaches past the last lhs row,
 // so lhs rows are clamped.
-template <bool TRANS, int S>
+template <bool TRANS, int NW, int S>
 __device__ __forceinline__ void issue_slot(bool wide, uint8_t* stage, const uint8_t* __restrict__ lhs,
                                            const uint8_t* __restrict__ wg, int64_t K, int64_t N, int64_t row0,
                                            int64_t col0, int64_t M, bool tail, int64_t kb, int wave, int lane,
                                            const LaneOff offK, const LaneOff offN) {
-  const int nA = wide ? 4 : 8;
+  // rows per wave: plain A 256/NW, B 128/NW; wide A 128/NW, B 256/NW
+  const int nA = wide ? 16 / NW : 32 / NW;
   const bool isA = S < nA;
   const uint8_t* src;
   int dst;
   if (isA) {
-    const int R = wave * (wide ? 32 : 64) + 8 * S;
+    const int R = wave * (wide ? 128 / NW : 256 / NW) + 8 * S;
     const uint32_t off = offK.pick(stage_bit(R));
     if (!tail) {
       src = lhs + (row0 + R) * K + kb + off;
@@ -120,7 +122,7 @@ __device__ __forceinline__ void issue_slot(bool wide, uint8_t* stage, const uint
     }
     dst = R * G_BK;
   } else {
-    const int R = wave * (wide ? 64 : 32) + 8 * (S - nA);
+    const int R = wave * (wide ? 256 / NW : 128 / NW) + 8 * (S - nA);
     if (TRANS)      // staged row r = output column col0 + r
       src = wg + (col0 + R) * K + kb + offK.pick(stage_bit(R));
     else            // staged half R / 128 holds columns 128h.., staged row = contraction index
@@ -218,13 +220,16 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // compiler memory barrier so no LDS access moves across it.
 __device__ __forceinline__ void step_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Tile configuration: BM x BN output tile, NST LDS stages, 4 waves (2 x 2).
-// A stage holds the A rows, the B rows and 1 KiB for the step's blockwise
-// weight scales (one float per tile column).
-template <int BM_, int BN_, int NST_>
+// Tile configuration: BM x BN output tile, NST LDS stages, NW waves.  A
+// plain tile is split over a (BM/WM) x (BN/WN) wave grid, a wide tile
+// (BM/2 x 2BN) over (BM/2WM) x (2BN/WN); both use WM x WN wave tiles (NW = 4:
+// 128 x 64, NW = 8: 64 x 64).  A stage holds the A rows, the B rows and 1 KiB
+// for the step's blockwise weight scales (one float per tile column).
+template <int BM_, int BN_, int NST_, int NW_ = 4>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, NST = NST_;
-  static constexpr int WM = BM / 2, WN = BN / 2;           // wave tile
+  static constexpr int BM = BM_, BN = BN_, NST = NST_, NW = NW_, THREADS = 64 * NW;
+  static constexpr int WN = 64, WM = BM * BN / (NW * WN);  // wave tile
+  static constexpr int SLOTS = 48 / NW;                    // direct loads per wave per K step
   static constexpr int MI = WM / 16, JN = WN / 16;         // 16 x 16 MFMA tiles per wave
   static constexpr int SC_OFF = (BM + BN) * G_BK;          // scale slot inside a stage
   static constexpr int STAGE = SC_OFF + 1024;
@@ -234,10 +239,10 @@ struct Cfg {
 };
 
 template <class C, bool KBLOCKS>
-constexpr int loads_per_step() { return (C::BM + C::BN) / 32 + (KBLOCKS ? 1 : 0); }   // per wave
+constexpr int loads_per_step() { return C::SLOTS + (KBLOCKS ? 1 : 0); }   // per wave
 
 template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16>
-__global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
+__global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
                                                        int ls_per_row, const uint8_t* __restrict__ rhs,
                                                        const float* __restrict__ rs, int Kb, int Nb,
                                                        const int32_t* __restrict__ group_sizes, int g0, int El,
@@ -250,9 +255,10 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
   __shared__ float ls_tile[BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: keeps staging addresses scalar
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int NW = C::NW, G_THREADS = C::THREADS;
   const int NT = static_cast<int>(N / BN);
-  static_assert(BM == 2 * BN && MI == 8 && JN == 4, "wide tail tiles are BM/2 x 2BN with the same wave tiles");
+  static_assert(BM == 256 && BN == 128 && JN == 4 && (NW == 4 || NW == 8),
+                "wide tail tiles are BM/2 x 2BN with the same wave tiles");
   build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), true);
   const int total = gt.tiles_off[El];
   const int n_rows = gt.rows_off[El];
@@ -303,14 +309,17 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
     const uint8_t* wg = rhs + static_cast<int64_t>(g) * K * N;
     const int bm_t = wide ? BM / 2 : BM, bn_t = wide ? 2 * BN : BN;     // this tile's shape
     const bool tail = row0 + bm_t > M;
-    // this wave's output block: rows rbase .. +127, columns cbase .. +63
-    const int rbase = wide ? 0 : wm * WM, cbase = wide ? wave * 64 : wn * WN;
+    // this wave's output block: rows rbase .. +WM-1, columns cbase .. +63
+    const int gn = wide ? 2 * BN / WN : BN / WN;          // wave-grid columns
+    const int rbase = (wave / gn) * WM, cbase = (wave % gn) * WN;
     const FragOff fa = frag_off(rbase, lane);
     const FragOff fb = frag_off(cbase, lane);
     const float* rs_g = rs + static_cast<int64_t>(g) * Kb * Nb;
     // blockwise scales ride the stages: lane l of wave w stages the scale of
-    // tile column 64w + l (clamped to the tile; surplus lanes repeat a column)
-    const float* rs_lane = rs_g + static_cast<uint32_t>(col0 + min(wave * 64 + lane, bn_t - 1)) / ncol_blk;
+    // tile column 64(w mod 4) + l (clamped to the tile; surplus lanes and the
+    // upper four of eight waves repeat columns, writing the same values)
+    const int w4 = wave & 3;
+    const float* rs_lane = rs_g + static_cast<uint32_t>(col0 + min(w4 * 64 + lane, bn_t - 1)) / ncol_blk;
 
     v4f acc[MI][JN];
 #pragma unroll
@@ -327,17 +336,19 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       if (s < KT) {
         const int64_t kb = static_cast<int64_t>(s) * G_BK;
 #define MOE_SLOT(S, stg, kbv) \
-  issue_slot<TRANS, S>(wide, stg, lhs, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
+  issue_slot<TRANS, NW, S>(wide, stg, lhs, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
         MOE_SLOT(0, smem + s * STAGE, kb); MOE_SLOT(1, smem + s * STAGE, kb); MOE_SLOT(2, smem + s * STAGE, kb);
         MOE_SLOT(3, smem + s * STAGE, kb); MOE_SLOT(4, smem + s * STAGE, kb); MOE_SLOT(5, smem + s * STAGE, kb);
-        MOE_SLOT(6, smem + s * STAGE, kb); MOE_SLOT(7, smem + s * STAGE, kb); MOE_SLOT(8, smem + s * STAGE, kb);
-        MOE_SLOT(9, smem + s * STAGE, kb); MOE_SLOT(10, smem + s * STAGE, kb); MOE_SLOT(11, smem + s * STAGE, kb);
+        if constexpr (C::SLOTS == 12) {
+          MOE_SLOT(6, smem + s * STAGE, kb); MOE_SLOT(7, smem + s * STAGE, kb); MOE_SLOT(8, smem + s * STAGE, kb);
+          MOE_SLOT(9, smem + s * STAGE, kb); MOE_SLOT(10, smem + s * STAGE, kb); MOE_SLOT(11, smem + s * STAGE, kb);
+        }
         if (KBLOCKS)
           __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(s / steps_per_block) * Nb,
-                                           (lds_void*)(smem + s * STAGE + C::SC_OFF + wave * 256), 4, 0, 0);
+                                           (lds_void*)(smem + s * STAGE + C::SC_OFF + w4 * 256), 4, 0, 0);
         if (s == 0) {   // the tile's lhs row scales ride its first stage (rows past the tile repeat its last)
-          const int r = min(wave * 64 + lane, rows_here - 1);
-          __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? row0 + r : 0), (lds_void*)(ls_tile + wave * 64), 4, 0, 0);
+          const int r = min(w4 * 64 + lane, rows_here - 1);
+          __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? row0 + r : 0), (lds_void*)(ls_tile + w4 * 64), 4, 0, 0);
         }
       }
     }
@@ -374,22 +385,29 @@ __global__ __launch_bounds__(G_THREADS) void gmm_kernel(const uint8_t* __restric
       // MI rounds: an A fragment, this round's share of the loads of step ks,
       // then the round's MFMAs -- so memory back-pressure on the loads never
       // holds up a long run of MFMA issue
-      // (round i issues load slots 3i/2 .. (3i+3)/2 - 1: 12 over the 8 rounds)
+      // (the step's SLOTS loads spread over the MI rounds, 1.5 per round)
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const v8i a = frag_i(As, fa, i);
         if (more) {
-          if (i == 0) { MOE_SLOT(0, nxt, kb_next); }
-          if (i == 1) { MOE_SLOT(1, nxt, kb_next); MOE_SLOT(2, nxt, kb_next); }
-          if (i == 2) { MOE_SLOT(3, nxt, kb_next); }
-          if (i == 3) { MOE_SLOT(4, nxt, kb_next); MOE_SLOT(5, nxt, kb_next); }
-          if (i == 4) { MOE_SLOT(6, nxt, kb_next); }
-          if (i == 5) { MOE_SLOT(7, nxt, kb_next); MOE_SLOT(8, nxt, kb_next); }
-          if (i == 6) { MOE_SLOT(9, nxt, kb_next); }
-          if (i == 7) { MOE_SLOT(10, nxt, kb_next); MOE_SLOT(11, nxt, kb_next); }
+          if constexpr (C::SLOTS == 12) {
+            if (i == 0) { MOE_SLOT(0, nxt, kb_next); }
+            if (i == 1) { MOE_SLOT(1, nxt, kb_next); MOE_SLOT(2, nxt, kb_next); }
+            if (i == 2) { MOE_SLOT(3, nxt, kb_next); }
+            if (i == 3) { MOE_SLOT(4, nxt, kb_next); MOE_SLOT(5, nxt, kb_next); }
+            if (i == 4) { MOE_SLOT(6, nxt, kb_next); }
+            if (i == 5) { MOE_SLOT(7, nxt, kb_next); MOE_SLOT(8, nxt, kb_next); }
+            if (i == 6) { MOE_SLOT(9, nxt, kb_next); }
+            if (i == 7) { MOE_SLOT(10, nxt, kb_next); MOE_SLOT(11, nxt, kb_next); }
+          } else {
+            if (i == 0) { MOE_SLOT(0, nxt, kb_next); MOE_SLOT(1, nxt, kb_next); }
+            if (i == 1) { MOE_SLOT(2, nxt, kb_next); }
+            if (i == 2) { MOE_SLOT(3, nxt, kb_next); MOE_SLOT(4, nxt, kb_next); }
+            if (i == 3) { MOE_SLOT(5, nxt, kb_next); }
+          }
           if (KBLOCKS && i == 0)
             __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(ks / steps_per_block) * Nb,
-                                             (lds_void*)(nxt + C::SC_OFF + wave * 256), 4, 0, 0);
+                                             (lds_void*)(nxt + C::SC_OFF + w4 * 256), 4, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
@@ -493,7 +511,7 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
   int64_t grid = static_cast<int64_t>(per_cu) * tile::num_cus();
   if (ub < grid) grid = ub;
   if (grid < 8) grid = 8;
-  gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16><<<static_cast<unsigned>(grid), G_THREADS, 0, st>>>(
+  gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
       lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err);
   return hipGetLastError();
 }
@@ -543,7 +561,7 @@ extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_s
   const bool bf16 = out_dtype == MOE_BF16;
   hipError_t e;
 #ifndef MOE_GMM_CFG
-#define MOE_GMM_CFG 256, 128, 3
+#define MOE_GMM_CFG 256, 128, 3, 8
 #endif
   using C = moe::Cfg<MOE_GMM_CFG>;
 #define MOE_GMM_ARGS bf16, lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, group_sizes, group_offset, El, M, K, N, out, err, st
