@@ -5,9 +5,11 @@
 // follows only when it is per token).
 //
 // Four launches on the caller's stream:
-//  1. hist   one block per tile of 2048 routed slots: per-tile expert counts.
-//  2. scan   one block: per-expert exclusive scan over tiles, the expert
-//            bases, group_sizes, and this shard's window (start, n).
+//  1. hist   one block per tile of 512 routed slots (2048 for inputs whose
+//            tile table would not fit in LDS): per-tile expert counts.
+//  2. scan   one block: per-expert exclusive scan over tiles (in LDS when the
+//            table fits), the expert bases, group_sizes, and this shard's
+//            window (start, n).
 //  3. rank   one block per tile: the stable rank of every slot inside its
 //            tile (a wave ranks 64 slots at a time: ballots over the bits of
 //            the expert id give each lane the set of lanes holding the same
@@ -23,7 +25,9 @@
 namespace moe {
 namespace {
 
-constexpr int kTile = 2048;          // routed slots per tile (256 threads x 8)
+constexpr int kTile = 2048;          // routed slots per tile (256 threads x 8), large inputs
+constexpr int kTileSmall = 512;      // routed slots per tile when the tile table fits in LDS
+constexpr int kScanLds = 15360;      // int32 entries of the tile table the scan keeps in LDS (60 KiB)
 constexpr int kHdr = 256;            // workspace header bytes
 // header int32 slots
 constexpr int kErr = 0, kStart = 1, kN = 2, kValid = 3;
@@ -36,14 +40,15 @@ __device__ __forceinline__ int key_of(int32_t id, int E, int32_t* err) {
   return id;
 }
 
+template <int TILE>
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
                                                         int32_t* __restrict__ hdr, int32_t* __restrict__ tile_hist) {
   extern __shared__ int hist[];
   for (int e = threadIdx.x; e <= E; e += 256) hist[e] = 0;
   __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kTile;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * TILE;
 #pragma unroll
-  for (int i = 0; i < kTile / 256; ++i) {
+  for (int i = 0; i < TILE / 256; ++i) {
     const int64_t f = base + i * 256 + threadIdx.x;
     if (f < M) atomicAdd(&hist[key_of(ids[f], E, hdr + kErr)], 1);
   }
@@ -71,15 +76,25 @@ __device__ void wave0_exclusive_scan(int* a, int n) {
   }
 }
 
+// in_lds: the whole [ntiles][E + 1] table is read into LDS with coalesced
+// loads, scanned there and written back (small tables); otherwise each
+// thread walks its experts' column in global memory.
 __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ tile_hist, int ntiles, int E,
                                                          int g0, int El, int32_t* __restrict__ group_sizes,
-                                                         int32_t* __restrict__ hdr) {
-  extern __shared__ int tot[];        // [E + 1]
+                                                         int32_t* __restrict__ hdr, int in_lds) {
+  extern __shared__ int tot[];        // [E + 1], then the table when in_lds
+  int* tab = tot + (E + 1);
+  const int64_t cells = static_cast<int64_t>(ntiles) * (E + 1);
+  int32_t* col = in_lds ? tab : tile_hist;
+  if (in_lds) {
+    for (int64_t i = threadIdx.x; i < cells; i += blockDim.x) tab[i] = tile_hist[i];
+    __syncthreads();
+  }
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
     int run = 0;
     for (int t = 0; t < ntiles; ++t) {
-      const int c = tile_hist[static_cast<int64_t>(t) * (E + 1) + e];
-      tile_hist[static_cast<int64_t>(t) * (E + 1) + e] = run;
+      const int c = col[static_cast<int64_t>(t) * (E + 1) + e];
+      col[static_cast<int64_t>(t) * (E + 1) + e] = run;
       run += c;
     }
     tot[e] = run;
@@ -88,9 +103,13 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
   __syncthreads();
   wave0_exclusive_scan(tot, E + 1);
   __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) {
-    const int b = tot[e];
-    for (int t = 0; t < ntiles; ++t) tile_hist[static_cast<int64_t>(t) * (E + 1) + e] += b;
+  if (in_lds) {
+    for (int64_t i = threadIdx.x; i < cells; i += blockDim.x) tile_hist[i] = tab[i] + tot[i % (E + 1)];
+  } else {
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+      const int b = tot[e];
+      for (int t = 0; t < ntiles; ++t) tile_hist[static_cast<int64_t>(t) * (E + 1) + e] += b;
+    }
   }
   if (threadIdx.x == 0) {
     const int start = tot[g0];
@@ -100,6 +119,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
   }
 }
 
+template <int TILE>
 __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E, int nbits,
                                                         int64_t M_cap, int32_t* __restrict__ hdr,
                                                         const int32_t* __restrict__ tile_off,
@@ -113,12 +133,12 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
     off[e] = tile_off[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
   }
   __syncthreads();
-  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * kTile + w * (kTile / 4);
+  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * TILE + w * (TILE / 4);
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  int keys[kTile / 256], rank[kTile / 256];
+  int keys[TILE / 256], rank[TILE / 256];
   int* my = cnt + w * (E + 1);
 #pragma unroll
-  for (int c = 0; c < kTile / 256; ++c) {
+  for (int c = 0; c < TILE / 256; ++c) {
     const int64_t f = wbase + c * 64 + lane;
     const bool valid = f < M;
     const int key = valid ? key_of(ids[f], E, nullptr) : 0;
@@ -150,7 +170,7 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
   __syncthreads();
   const int start = hdr[kStart], n = hdr[kN];
 #pragma unroll
-  for (int c = 0; c < kTile / 256; ++c) {
+  for (int c = 0; c < TILE / 256; ++c) {
     const int key = keys[c];
     if (key < 0) continue;
     const int64_t f = wbase + c * 64 + lane;
@@ -220,7 +240,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const uint8_t* __rest
 }  // namespace
 
 size_t sort_ws_bytes(int64_t M, int E) {
-  const int64_t ntiles = moe_cdiv(M, kTile);
+  const int64_t ntiles = moe_cdiv(M, kTileSmall);      // enough for either tile size
   return kHdr + static_cast<size_t>(moe_cdiv(ntiles * (E + 1) * 4, 256) * 256);
 }
 
@@ -248,20 +268,32 @@ extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* hdr = static_cast<int32_t*>(ws);
   int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + moe::kHdr);
-  const int ntiles = static_cast<int>(moe_cdiv(M, moe::kTile));
+  // small tiles (more workgroups) whenever their table fits the scan's LDS
+  const bool small = moe_cdiv(M, moe::kTileSmall) * (E + 1) <= moe::kScanLds;
+  const int tile = small ? moe::kTileSmall : moe::kTile;
+  const int ntiles = static_cast<int>(moe_cdiv(M, tile));
+  const bool scan_in_lds = static_cast<int64_t>(ntiles) * (E + 1) <= moe::kScanLds;
   int nbits = 0;
   while ((1 << nbits) < E + 1) ++nbits;
   const size_t hist_lds = (E + 1) * sizeof(int);
   if (ntiles > 0) {
-    moe::sort_hist_kernel<<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+    if (small)
+      moe::sort_hist_kernel<moe::kTileSmall><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+    else
+      moe::sort_hist_kernel<moe::kTile><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
     MOE_CHECK_LAUNCH();
   }
-  moe::sort_scan_kernel<<<1, 1024, hist_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
-                                                    group_sizes, hdr);
+  const size_t scan_lds = hist_lds + (scan_in_lds ? static_cast<size_t>(ntiles) * (E + 1) * sizeof(int) : 0);
+  moe::sort_scan_kernel<<<1, 1024, scan_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
+                                                   group_sizes, hdr, scan_in_lds ? 1 : 0);
   MOE_CHECK_LAUNCH();
   if (ntiles > 0) {
-    moe::sort_rank_kernel<<<ntiles, 256, 5 * hist_lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr, tile_hist,
-                                                             perm, inv_pos);
+    if (small)
+      moe::sort_rank_kernel<moe::kTileSmall><<<ntiles, 256, 5 * hist_lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr,
+                                                                                 tile_hist, perm, inv_pos);
+    else
+      moe::sort_rank_kernel<moe::kTile><<<ntiles, 256, 5 * hist_lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr,
+                                                                            tile_hist, perm, inv_pos);
     MOE_CHECK_LAUNCH();
   }
   if (xs || ss) {
