@@ -4,12 +4,13 @@
 // gathered by the sorted token indices into this shard's window, the scale
 // follows only when it is per token).
 //
-// Four launches on the caller's stream:
+// Three or four launches on the caller's stream:
 //  1. hist   one block per tile of 512 routed slots (2048 for inputs whose
 //            tile table would not fit in LDS): per-tile expert counts.
-//  2. scan   one block: per-expert exclusive scan over tiles (in LDS when the
-//            table fits), the expert bases, group_sizes, and this shard's
-//            window (start, n).
+//  2. scan   per-expert exclusive scan over tiles, the expert bases,
+//            group_sizes, and this shard's window (start, n).  When the tile
+//            table fits in LDS every rank block does this itself (no launch);
+//            otherwise one block does it in global memory.
 //  3. rank   one block per tile: the stable rank of every slot inside its
 //            tile (a wave ranks 64 slots at a time: ballots over the bits of
 //            the expert id give each lane the set of lanes holding the same
@@ -119,18 +120,63 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
   }
 }
 
-template <int TILE>
+// FUSED_SCAN: tile_off holds the per-tile counts (no scan kernel ran); every
+// block reads the whole [ntiles][E + 1] table into LDS and derives its own
+// tile's offsets -- the counts of the earlier tiles plus the expert bases --
+// and block 0 writes group_sizes and the window header.  Otherwise tile_off
+// holds the offsets the scan kernel wrote.
+template <int TILE, bool FUSED_SCAN>
 __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E, int nbits,
                                                         int64_t M_cap, int32_t* __restrict__ hdr,
-                                                        const int32_t* __restrict__ tile_off,
+                                                        const int32_t* __restrict__ tile_off, int ntiles, int g0,
+                                                        int El, int32_t* __restrict__ group_sizes,
                                                         int32_t* __restrict__ perm, int32_t* __restrict__ inv_pos) {
   extern __shared__ int lds[];
   int* cnt = lds;                      // [4][E + 1] running counts per wave
   int* off = lds + 4 * (E + 1);        // [E + 1] global base of this tile
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e <= E; e += 256) {
-    cnt[e] = cnt[(E + 1) + e] = cnt[2 * (E + 1) + e] = cnt[3 * (E + 1) + e] = 0;
-    off[e] = tile_off[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
+  __shared__ int win[2];               // start, n of the local window
+  if constexpr (FUSED_SCAN) {
+    int* tab = lds + 5 * (E + 1);      // [ntiles][E + 1] counts
+    int* tot = tab + ntiles * (E + 1); // [E + 1] totals, then their exclusive scan
+    const int cells = ntiles * (E + 1);
+    for (int i = threadIdx.x; i < cells; i += 256) tab[i] = tile_off[i];
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += 256) {
+      int before = 0, all = 0;
+      for (int t = 0; t < ntiles; ++t) {
+        const int c = tab[t * (E + 1) + e];
+        before += t < static_cast<int>(blockIdx.x) ? c : 0;
+        all += c;
+      }
+      off[e] = before;
+      tot[e] = all;
+      if (blockIdx.x == 0 && e < E) group_sizes[e] = all;
+    }
+    __syncthreads();
+    wave0_exclusive_scan(tot, E + 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e <= E; e += 256) off[e] += tot[e];
+    if (threadIdx.x == 0) {
+      win[0] = tot[g0];
+      win[1] = tot[g0 + El] - tot[g0];
+      if (blockIdx.x == 0) {
+        hdr[kStart] = win[0];
+        hdr[kN] = win[1];
+        hdr[kValid] = tot[E];
+      }
+    }
+    for (int e = threadIdx.x; e <= E; e += 256)
+      cnt[e] = cnt[(E + 1) + e] = cnt[2 * (E + 1) + e] = cnt[3 * (E + 1) + e] = 0;
+  } else {
+    for (int e = threadIdx.x; e <= E; e += 256) {
+      cnt[e] = cnt[(E + 1) + e] = cnt[2 * (E + 1) + e] = cnt[3 * (E + 1) + e] = 0;
+      off[e] = tile_off[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
+    }
+    if (threadIdx.x == 0) {
+      win[0] = hdr[kStart];
+      win[1] = hdr[kN];
+    }
   }
   __syncthreads();
   const int64_t wbase = static_cast<int64_t>(blockIdx.x) * TILE + w * (TILE / 4);
@@ -168,7 +214,7 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
     }
   }
   __syncthreads();
-  const int start = hdr[kStart], n = hdr[kN];
+  const int start = win[0], n = win[1];
 #pragma unroll
   for (int c = 0; c < TILE / 256; ++c) {
     const int key = keys[c];
@@ -283,18 +329,35 @@ extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t 
       moe::sort_hist_kernel<moe::kTile><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
     MOE_CHECK_LAUNCH();
   }
-  const size_t scan_lds = hist_lds + (scan_in_lds ? static_cast<size_t>(ntiles) * (E + 1) * sizeof(int) : 0);
-  moe::sort_scan_kernel<<<1, 1024, scan_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
-                                                   group_sizes, hdr, scan_in_lds ? 1 : 0);
-  MOE_CHECK_LAUNCH();
-  if (ntiles > 0) {
+  // hist -> rank with the scan fused into every rank block when the tile
+  // table fits in LDS; hist -> scan -> rank otherwise
+  const size_t rank_lds = 6 * hist_lds + static_cast<size_t>(ntiles) * (E + 1) * sizeof(int);
+  if (ntiles > 0 && scan_in_lds && rank_lds <= 64 * 1024) {
     if (small)
-      moe::sort_rank_kernel<moe::kTileSmall><<<ntiles, 256, 5 * hist_lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr,
-                                                                                 tile_hist, perm, inv_pos);
+      moe::sort_rank_kernel<moe::kTileSmall, true><<<ntiles, 256, rank_lds, st>>>(
+          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+          perm, inv_pos);
     else
-      moe::sort_rank_kernel<moe::kTile><<<ntiles, 256, 5 * hist_lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr,
-                                                                            tile_hist, perm, inv_pos);
+      moe::sort_rank_kernel<moe::kTile, true><<<ntiles, 256, rank_lds, st>>>(
+          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+          perm, inv_pos);
     MOE_CHECK_LAUNCH();
+  } else {
+    const size_t scan_lds = hist_lds + (scan_in_lds ? static_cast<size_t>(ntiles) * (E + 1) * sizeof(int) : 0);
+    moe::sort_scan_kernel<<<1, 1024, scan_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
+                                                     group_sizes, hdr, scan_in_lds ? 1 : 0);
+    MOE_CHECK_LAUNCH();
+    if (ntiles > 0) {
+      if (small)
+        moe::sort_rank_kernel<moe::kTileSmall, false><<<ntiles, 256, 5 * hist_lds, st>>>(
+            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+            perm, inv_pos);
+      else
+        moe::sort_rank_kernel<moe::kTile, false><<<ntiles, 256, 5 * hist_lds, st>>>(
+            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+            perm, inv_pos);
+      MOE_CHECK_LAUNCH();
+    }
   }
   if (xs || ss) {
     int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
