@@ -41,13 +41,41 @@ __device__ __forceinline__ void load_vals(const uint16_t* __restrict__ x, const 
   }
 }
 
-__device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t off, const float v[8], float s) {
-  uint32_t lo = 0, hi = 0;
+// x / s for one row's scale s, correctly rounded.  For s in [2^-64, 2^64]
+// the quotient comes from the row's reciprocal y = RN(1/s) and one
+// correction, q = RN(q0 + RN(x - s*q0) * y) with q0 = RN(x*y): Markstein's
+// theorem (a correctly rounded reciprocal and a quotient within one ulp give
+// the correctly rounded quotient after one FMA correction), which needs the
+// residual x - s*q0 to be exact -- true in this range for every quotient of
+// magnitude at least 2^-10, and smaller ones encode to a signed zero either
+// way.  Zeros keep their sign and infinities or NaN pass through; other
+// scales use the division.
+struct RowDiv {
+  float s, y;
+  bool fast;
+  __device__ __forceinline__ explicit RowDiv(float s_) : s(s_), y(1.0f / s_),
+      fast(s_ >= 0x1p-64f && s_ <= 0x1p64f) {}
+  __device__ __forceinline__ float operator()(float x) const {
+    if (!fast) return x / s;
+    const float q0 = x * y;
+    const float r = fmaf(-s, q0, x);
+    const float q = fmaf(r, y, q0);
+    return (q0 == 0.0f || !(fabsf(q0) <= 3.0e38f)) ? q0 : q;
+  }
+};
+
+// Eight values to e4m3fn codes: clip to [-448, 448], then the gfx950 fp8
+// conversion (round to nearest even; on this clipped range it is the
+// encoder in common.hpp, bit for bit).
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t off, const float v[8], const RowDiv& d) {
+  float c[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= quantize_one(v[i], s) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= quantize_one(v[4 + i], s) << (8 * i);
-  *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(d(v[i]), -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+  *reinterpret_cast<uint2*>(q + off) = make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
 }
 
 __device__ __forceinline__ float scale_from_amax(float amax) {
@@ -83,10 +111,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     }
     amax = wave_max(amax);
     const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
+    const RowDiv div(s);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t ch = lane + 64 * c;
-      if (ch < nchunks) store_codes(q, base + ch * 8, v[c], s);
+      if (ch < nchunks) store_codes(q, base + ch * 8, v[c], div);
     }
     if (lane == 0) {
       if (MODE == MODE_ROW) scale[row] = s;
@@ -101,10 +130,11 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     }
     amax = wave_max(amax);
     const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
+    const RowDiv div(s);
     for (int64_t ch = lane; ch < nchunks; ch += 64) {
       float v[8];
       load_vals<ACT>(x, xu, base + ch * 8, v);
-      store_codes(q, base + ch * 8, v, s);
+      store_codes(q, base + ch * 8, v, div);
     }
     if (lane == 0) {
       if (MODE == MODE_ROW) scale[row] = s;
