@@ -87,14 +87,23 @@ __device__ __forceinline__ float scale_from_amax(float amax) {
 constexpr int MODE_ROW = 0;
 constexpr int MODE_GIVEN = 1;
 
-template <int CPL, int ACT, int MODE>
+// LPR lanes per row (64: one row per wave; 32: two rows per wave, for rows
+// whose chunk count is an odd multiple of 32, e.g. 768 elements = 96 chunks).
+template <int LPR>
+__device__ __forceinline__ float row_max(float v) {
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+  return v;
+}
+
+template <int CPL, int ACT, int MODE, int LPR = 64>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu, int64_t R, int64_t C,
     const float* __restrict__ given_scale, uint8_t* __restrict__ q, float* __restrict__ scale,
     float* __restrict__ row_amax) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
+  const int lane = threadIdx.x % LPR;
+  const int64_t row = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * (64 / LPR) + (threadIdx.x & 63) / LPR;
+  if (row >= R) return;     // (a half-wave's partner rows never read this half's lanes)
   const int64_t nchunks = C >> 3;
   const int64_t base = row * C;
   float amax = 0.0f;
@@ -102,19 +111,19 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     float v[CPL][8];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int64_t ch = lane + 64 * c;
+      const int64_t ch = lane + LPR * c;
       if (ch < nchunks) {
         load_vals<ACT>(x, xu, base + ch * 8, v[c]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
       }
     }
-    amax = wave_max(amax);
+    amax = row_max<LPR>(amax);
     const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
     const RowDiv div(s);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int64_t ch = lane + 64 * c;
+      const int64_t ch = lane + LPR * c;
       if (ch < nchunks) store_codes(q, base + ch * 8, v[c], div);
     }
     if (lane == 0) {
@@ -191,6 +200,18 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t
                        uint8_t* q, float* scale, float* row_amax, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(moe_cdiv(R, 4))), block(256);
   const int64_t chunks_per_lane = moe_cdiv(C / 8, 64);
+  // rows of 96 + 64j chunks: two rows per wave, 32 lanes each, no idle lanes
+  const int64_t nch = C / 8;
+  if (nch % 64 == 32 && nch <= 32 * 5) {
+    const dim3 grid2(static_cast<unsigned>(moe_cdiv(R, 8)));
+    if (nch == 32)
+      quantize_rows_kernel<1, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    else if (nch == 96)
+      quantize_rows_kernel<3, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    else
+      quantize_rows_kernel<5, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    return hipGetLastError();
+  }
   // Keep the row in registers when it fits (the SiLU variant holds float32).
   const int max_cpl = (ACT == MOE_ACT_SILU_MUL) ? 8 : 16;
   if (chunks_per_lane <= 1)

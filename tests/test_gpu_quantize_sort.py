@@ -34,7 +34,8 @@ def _bits(rng, shape, scale=1.0):
     return to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
-@pytest.mark.parametrize("R,C", [(1, 16), (7, 48), (256, 512), (300, 2048), (33, 7168), (5, 8192), (3, 8208)])
+@pytest.mark.parametrize("R,C", [(1, 16), (7, 48), (256, 512), (300, 2048), (33, 7168), (5, 8192), (3, 8208),
+                                 (5, 256), (9, 768), (3, 1280)])
 def test_row_quantize_bit_exact(R, C):
     rng = np.random.default_rng(R * 7 + C)
     x = _bits(rng, (R, C), 3.0)
@@ -81,7 +82,7 @@ def test_tensor_and_static_modes():
     assert_bits_equal(s, so, "static scale")
 
 
-@pytest.mark.parametrize("R,C", [(64, 768), (37, 2048), (2, 16)])
+@pytest.mark.parametrize("R,C", [(64, 768), (33, 768), (7, 256), (37, 2048), (2, 16)])
 def test_silu_mul_requantize_bit_exact(R, C):
     rng = np.random.default_rng(R + C)
     a = _bits(rng, (R, C), 4.0)
