@@ -12,6 +12,102 @@
 namespace moe {
 namespace {
 
+// Weighted sum of 8 values (one 16-byte chunk of a y row) into acc.
+template <int YBF16>
+__device__ __forceinline__ void fma_chunk(float acc[8], float wj, const uint4 lo, const uint4 hi) {
+  if (YBF16) {
+    const uint32_t wv[4] = {lo.x, lo.y, lo.z, lo.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(wj, __uint_as_float(wv[i] << 16), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(wj, __uint_as_float(wv[i] & 0xffff0000u), acc[2 * i + 1]);
+    }
+  } else {
+    const float v[8] = {__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(lo.z), __uint_as_float(lo.w),
+                        __uint_as_float(hi.x), __uint_as_float(hi.y), __uint_as_float(hi.z), __uint_as_float(hi.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+  }
+}
+
+template <int OBF16>
+__device__ __forceinline__ void store_chunk(void* __restrict__ out, int64_t t, int64_t N, int64_t ch, const float acc[8]) {
+  if (OBF16) {
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+    o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+    o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+    o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+    reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * N)[ch] = o;
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + t * N) + 2 * ch;
+    p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+// k <= 8: every slot's row chunk for two chunks per lane is loaded before any
+// is summed (16 loads in flight per lane), then summed in slot order.
+template <int YBF16, int OBF16>
+__global__ __launch_bounds__(256) void gather_reduce_k8_kernel(const void* __restrict__ y,
+                                                               const int32_t* __restrict__ inv,
+                                                               const float* __restrict__ wts, int64_t T, int k,
+                                                               int64_t N, void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int my_r = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_r = inv[t * k + lane];
+    my_w = wts[t * k + lane];
+  }
+  const uint64_t m = __ballot(my_r >= 0);
+  int r[8];
+  float w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    r[j] = __builtin_amdgcn_readlane(my_r, j);
+    w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), j));
+  }
+  const int64_t chunks = N >> 3;            // 8 elements per chunk
+  const int64_t rowb = YBF16 ? N * 2 : N * 4;
+  const uint8_t* yb = static_cast<const uint8_t*>(y);
+  for (int64_t c0 = lane; c0 < chunks; c0 += 128) {
+    const int64_t c1 = c0 + 64;
+    const bool two = c1 < chunks;
+    uint4 lo[2][8], hi[2][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((m >> j) & 1ull) {                // uniform across the wave
+        const uint8_t* row = yb + static_cast<int64_t>(r[j]) * rowb;
+        if (YBF16) {
+          lo[0][j] = reinterpret_cast<const uint4*>(row)[c0];
+          if (two) lo[1][j] = reinterpret_cast<const uint4*>(row)[c1];
+        } else {
+          lo[0][j] = reinterpret_cast<const uint4*>(row)[2 * c0];
+          hi[0][j] = reinterpret_cast<const uint4*>(row)[2 * c0 + 1];
+          if (two) {
+            lo[1][j] = reinterpret_cast<const uint4*>(row)[2 * c1];
+            hi[1][j] = reinterpret_cast<const uint4*>(row)[2 * c1 + 1];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)            // slot order
+        if ((m >> j) & 1ull) fma_chunk<YBF16>(acc, w[j], lo[u][j], hi[u][j]);
+      store_chunk<OBF16>(out, t, N, u ? c1 : c0, acc);
+    }
+  }
+}
+
 template <int YBF16, int OBF16>
 __global__ __launch_bounds__(256) void gather_reduce_kernel(const void* __restrict__ y, const int32_t* __restrict__ inv,
                                                             const float* __restrict__ wts, int64_t T, int k,
@@ -80,13 +176,17 @@ extern "C" int moe_gather_reduce(const void* y, int y_dtype, const int32_t* inv_
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(moe_cdiv(T, 4))), block(256);
   if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
-    moe::gather_reduce_kernel<1, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+    k <= 8 ? moe::gather_reduce_k8_kernel<1, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out)
+           : moe::gather_reduce_kernel<1, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
   else if (y_dtype == MOE_BF16)
-    moe::gather_reduce_kernel<1, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+    k <= 8 ? moe::gather_reduce_k8_kernel<1, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out)
+           : moe::gather_reduce_kernel<1, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
   else if (out_dtype == MOE_BF16)
-    moe::gather_reduce_kernel<0, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+    k <= 8 ? moe::gather_reduce_k8_kernel<0, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out)
+           : moe::gather_reduce_kernel<0, 1><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
   else
-    moe::gather_reduce_kernel<0, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+    k <= 8 ? moe::gather_reduce_k8_kernel<0, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out)
+           : moe::gather_reduce_kernel<0, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
