@@ -136,6 +136,25 @@ class ForwardPath:
         self.experts()
         self.combine()
 
+    # -- HIP graph of one step ------------------------------------------------
+    def capture_graph(self, warmup=2):
+        """Record one step (every launch of the path, on one stream) into a HIP
+        graph; replay() then runs the step with a single submission.  Every
+        buffer a step writes is fully rewritten by it, so replays are
+        identical to eager steps."""
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+
     # -- accounting ----------------------------------------------------------
     def gmm_flops(self, n_local):
         """Algorithmic GMM flops of one step for n_local routed local rows."""

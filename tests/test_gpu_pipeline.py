@@ -216,3 +216,34 @@ def test_backward_pipeline_config5_stagewise():
     o = tgmm(srt["xs"], xsc, dq_t, ds_t, gs, 0, cfg.E, sample=(gi, ki, ci))
     B = lambda idx: tgmm_allowance(srt["xs"], xsc, dq_t, ds_t, gs, 0, cfg.E, gi[idx], ki[idx], ci[idx])
     check_f32(host(path.dw)[gi, ki, ci], o["out"], o["abs_sum"], B, "dW")
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_forward_step_hip_graph_replays_match_eager(cid):
+    """The bench's timed step is a HIP graph of the forward step: every
+    replay, with eager steps and host synchronizations between replays,
+    leaves exactly the eager step's bits in every buffer the step writes."""
+    cfg = CONFIGS[cid]
+    data = generate(cfg)
+    n = int(((data["ids"] >= cfg.group_offset) & (data["ids"] < cfg.group_offset + cfg.E_loc)).sum())
+    from workloads import m_cap_for
+    share = 8 if cfg.E_loc < cfg.E else 1
+    path = ForwardPath(cfg, data, m_cap=m_cap_for(cfg, n), share=share)
+    names = ["xq", "xscale", "perm", "inv_pos", "group_sizes", "xs", "ss", "y", "out"] + \
+        (["a", "b", "hq", "hs"] if cfg.pipeline == "ffn" else [])
+    path.step()
+    torch.cuda.synchronize()
+    ref = {k: getattr(path, k).clone() for k in names}
+    path.capture_graph(warmup=1)
+    for rep in range(3):
+        for k in names:                      # scribble over the outputs between replays
+            if share > 1 and k in ("xq", "xscale"):
+                continue                     # the other GPUs' slots are written once, at set-up
+            getattr(path, k).view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        path.replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(getattr(path, k).view(torch.uint8), ref[k].view(torch.uint8)), (cid, rep, k)
+        path.step()                          # an eager step in between
+        torch.cuda.synchronize()
