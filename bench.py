@@ -224,6 +224,118 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
     return res, cfg
 
 
+def _time_calls(calls, steps, warmup):
+    """Eager timing of a list of (name, fn) launches: HIP events around each."""
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    ev = {nm: [] for nm, _ in calls}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for nm, fn in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[nm].append((a, b))
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    out = {}
+    for nm, lst in ev.items():
+        d = [a.elapsed_time(b) for a, b in lst]
+        out[nm] = (float(np.mean(d)) * 1e3, float(np.min(d)) * 1e3)
+    return out, ms
+
+
+def _kern_entry(us, us_min, nbytes, flops=0):
+    e = {"avg_us": round(us, 2), "min_us": round(us_min, 2), "alg_bytes": int(nbytes),
+         "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+    if flops:
+        tf = flops / (us * 1e-6) / 1e12
+        e.update({"alg_flops": int(flops), "TFLOP_s": round(tf, 1), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)})
+    return e
+
+
+def secondary_ep_slice(steps, warmup):
+    """Config 4: one GPU's expert slice of an 8-GPU expert-parallel forward
+    (T=8192 H=7168, 256 experts, top-8, this GPU's experts 64..95, 128x128
+    blockwise weight scales) -- the large-GMM case."""
+    import moe_fp8_grouped_amd as m
+    from moe_fp8_grouped_amd.pipeline import ForwardPath
+    from workloads import CONFIGS, generate, m_cap_for
+
+    cfg = CONFIGS[4]
+    data = generate(cfg)
+    ids = data["ids"]
+    local = (ids >= cfg.group_offset) & (ids < cfg.group_offset + cfg.E_loc)
+    n, U = int(local.sum()), int(local.any(axis=1).sum())
+    path = ForwardPath(cfg, data, m_cap=m_cap_for(cfg, n), share=8)
+    gs = np.bincount(ids.ravel(), minlength=cfg.E)[cfg.group_offset:cfg.group_offset + cfg.E_loc]
+    path.nonempty_local = int((gs > 0).sum())
+    del data
+    acc = step_accounting(path, n, U)
+    ls = path.ss
+    calls = [("quantize", path.quantize), ("sort", path.sort),
+             ("gmm_wi_0", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_0"], path.a)),
+             ("gmm_wi_1", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_1"], path.b)),
+             ("silu_quant", lambda: m.moe_quantize_rows(path.a, path.b, m.MOE_ACT_SILU_MUL, path.m_cap, cfg.I,
+                                                        m.MOE_SCALE_ROW_DYNAMIC, 0.0, path.hq, path.hs, None, None)),
+             ("gmm_wo", lambda: path.gmm(path.hq, path.hs, m.MOE_SCALE_ROW_DYNAMIC, path.w["wo"], path.y)),
+             ("gather_reduce", path.combine)]
+    t, ms_eager = _time_calls(calls, steps, warmup)
+    kern = {}
+    for nm, (us, us_min) in t.items():
+        if nm.startswith("gmm_"):
+            g = next(g for g in acc["gmm"] if "gmm_" + g["name"] == nm)
+            kern[nm] = _kern_entry(us, us_min, g["bytes"], g["flops"])
+        else:
+            kern[nm] = _kern_entry(us, us_min, acc[nm]["bytes"])
+    path.capture_graph(warmup=1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        path.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gmm_flops = sum(g["flops"] for g in acc["gmm"])
+    res = {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.k} I={cfg.I}, local experts "
+                       f"{cfg.group_offset}..{cfg.group_offset + cfg.E_loc - 1}, 128x128 weight blocks",
+           "routed_local_rows": n, "ms_per_step": round(ms, 4), "ms_per_step_eager": round(ms_eager, 4),
+           "gmm_TFLOP_s_whole_step": round(gmm_flops / (ms * 1e-3) / 1e12, 1), "kernels": kern}
+    del path
+    torch.cuda.empty_cache()
+    return res
+
+
+def secondary_backward(steps, warmup):
+    """Config 5: the backward of an up projection (T=8192 H=4096 E=64 top-4
+    I=1536, static scales): dX = gmm(dY, W^T) and dW = tgmm(X_sorted, dY)."""
+    from moe_fp8_grouped_amd.pipeline import BackwardPath
+    from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate
+
+    cfg = CONFIGS[5]
+    data = generate(cfg)
+    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE)
+    del data
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    M = T * k
+    calls = [("quantize_x_and_sort", path.quantize_and_sort), ("quantize_dy_row_and_tensor", path.quantize_dy),
+             ("gmm_dx", path.grad_input), ("tgmm_dw", path.grad_weight)]
+    t, ms_eager = _time_calls(calls, steps, warmup)
+    by = {"quantize_x_and_sort": T * H * 3 + 4 + (M * 4 + 2 * M * 4 + E * 4 + T * H + M * H),
+          "quantize_dy_row_and_tensor": (M * I * 3 + M * 4) + (M * I * 2 + M * I * 3 + 4),
+          "gmm_dx": M * I + E * I * H + M * H * 2 + M * 4 + E * 4,
+          "tgmm_dw": M * H + M * I + E * H * I * 4}
+    fl = {"gmm_dx": 2 * M * I * H, "tgmm_dw": 2 * M * H * I}
+    kern = {nm: _kern_entry(us, us_min, by[nm], fl.get(nm, 0)) for nm, (us, us_min) in t.items()}
+    res = {"workload": f"{cfg.name}: T={T} H={H} E={E} top-{k} I={I}, static activation and weight scales",
+           "ms_per_step_eager": round(ms_eager, 4), "kernels": kern}
+    del path
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, tokens=2048):
     """The oracle's forward pipeline on the first ``tokens`` tokens."""
     from threadpoolctl import threadpool_info
@@ -261,6 +373,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the expert-slice forward and the backward measured beside the headline step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (profiler byte-counter calibration)")
     a = ap.parse_args()
@@ -269,6 +383,10 @@ def main():
               f"as one GPU's expert slice", file=sys.stderr)
         sys.exit(2)
     res, cfg = run_gpu(a.config, a.steps, a.warmup, a.calib_copy_mib)
+    if not a.no_secondary:
+        torch.cuda.empty_cache()
+        res["secondary"] = {"ep_slice_forward": secondary_ep_slice(min(a.steps, 10), 2),
+                            "backward": secondary_backward(min(a.steps, 10), 2)}
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, a.cpu_tokens)
     print(json.dumps(res), flush=True)
