@@ -6,6 +6,7 @@ namespace moe {
 size_t quantize_rows_ws_bytes(int64_t R, int64_t C, int mode);
 size_t sort_ws_bytes(int64_t M, int E);
 size_t gmm_ws_bytes();
+size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int E);
 }  // namespace moe
 
 extern "C" int moe_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2, int32_t E, size_t* bytes) {
@@ -20,9 +21,12 @@ extern "C" int moe_workspace_bytes(int op, int64_t d0, int64_t d1, int64_t d2, i
       *bytes = moe::sort_ws_bytes(d0, E);
       return MOE_OK;
     case MOE_OP_GMM:
-    case MOE_OP_TGMM:
       if (d0 < 0 || d1 < 0 || d2 < 0) return MOE_ERR_SHAPE;
       *bytes = moe::gmm_ws_bytes();
+      return MOE_OK;
+    case MOE_OP_TGMM:
+      if (d0 < 0 || d1 < 0 || d2 < 0 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
+      *bytes = moe::tgmm_ws_bytes(d0, d1, d2, E);
       return MOE_OK;
     case MOE_OP_GATHER_REDUCE:
     case MOE_OP_QUANTIZE_WEIGHTS:

@@ -61,6 +61,10 @@
 // Rows [n, M) are zeroed after the tiles.
 #include "tile_common.hpp"
 
+#ifndef MOE_GMM_CFG
+#define MOE_GMM_CFG 256, 128, 3, 8     // BM, BN, stages, waves
+#endif
+
 namespace moe {
 namespace {
 using namespace tile;
@@ -241,13 +245,18 @@ struct Cfg {
 template <class C, bool KBLOCKS>
 constexpr int loads_per_step() { return C::SLOTS + (KBLOCKS ? 1 : 0); }   // per wave
 
-template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16>
+// BATCH (the weight-gradient product): one independent matmul per local
+// group g, out[g] (M x N) = A_g B_g^T with A and B stored contraction-
+// contiguous, row stride K, group g's contraction at columns
+// 128 * tiles_off[g] .. of both (its rows, zero-padded to a multiple of 128);
+// rows = the group table's row bound (max_rows).  Empty groups get zeros.
+template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH = false>
 __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
                                                        int ls_per_row, const uint8_t* __restrict__ rhs,
                                                        const float* __restrict__ rs, int Kb, int Nb,
                                                        const int32_t* __restrict__ group_sizes, int g0, int El,
                                                        int64_t M, int64_t K, int64_t N, void* __restrict__ out,
-                                                       int32_t* __restrict__ err) {
+                                                       int32_t* __restrict__ err, int64_t max_rows = 0) {
   constexpr int BM = C::BM, BN = C::BN, NST = C::NST, WM = C::WM, WN = C::WN, MI = C::MI, JN = C::JN;
   constexpr int STAGE = C::STAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
@@ -259,8 +268,12 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
   const int NT = static_cast<int>(N / BN);
   static_assert(BM == 256 && BN == 128 && JN == 4 && (NW == 4 || NW == 8),
                 "wide tail tiles are BM/2 x 2BN with the same wave tiles");
-  build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), true);
-  const int total = gt.tiles_off[El];
+  const int MTb = static_cast<int>(M / BM);          // BATCH: m-tiles per group
+  if constexpr (BATCH)   // tiles_off = the groups' padded row offsets in 128-row blocks
+    build_groups(group_sizes, g0, El, max_rows, 1, G_BK, err, gt, reinterpret_cast<int*>(smem), false);
+  else
+    build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), true);
+  const int total = BATCH ? El * MTb * NT : gt.tiles_off[El];
   const int n_rows = gt.rows_off[El];
   const int KT = static_cast<int>(K / G_BK);
   const int steps_per_block = static_cast<int>(K / Kb / G_BK);
@@ -275,13 +288,16 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     // m-tiles fastest; a short remainder of at most BM/2 rows is covered by
     // wide tiles of two n-tiles each, placed after the two n-tiles' full
     // m-tiles so they reuse the same weight columns from L2)
-    const int g = find_group(gt, El, t);
-    const int local = t - gt.tiles_off[g];
+    const int g = BATCH ? t / (MTb * NT) : find_group(gt, El, t);
+    const int local = BATCH ? t - g * (MTb * NT) : t - gt.tiles_off[g];
     const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
     const int full = m_g / BM, rem = m_g - full * BM;
     int nt, mt;
     bool wide = false;
-    if (rem == 0 || rem > BM / 2) {
+    if (BATCH) {
+      nt = local / MTb;
+      mt = local - nt * MTb;
+    } else if (rem == 0 || rem > BM / 2) {
       const int per = full + (rem ? 1 : 0);
       nt = local / per;
       mt = local - nt * per;
@@ -303,10 +319,17 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
         mt = local - npair * pairblk;
       }
     }
-    const int64_t row0 = gt.rows_off[g] + static_cast<int64_t>(mt) * BM;
-    const int rows_here = min(BM, m_g - mt * BM);
+    const int64_t row0 = BATCH ? static_cast<int64_t>(mt) * BM : gt.rows_off[g] + static_cast<int64_t>(mt) * BM;
+    const int rows_here = BATCH ? BM : min(BM, m_g - mt * BM);
     const int64_t col0 = static_cast<int64_t>(nt) * BN;
-    const uint8_t* wg = rhs + static_cast<int64_t>(g) * K * N;
+    // BATCH: the group's contraction columns, its K steps and its output matrix
+    const int64_t cofs = BATCH ? static_cast<int64_t>(gt.tiles_off[g]) * G_BK : 0;
+    const int KTt = BATCH ? (m_g + G_BK - 1) / G_BK : KT;
+    const uint8_t* lhs_t = lhs + cofs;
+    const uint8_t* wg = BATCH ? rhs + cofs : rhs + static_cast<int64_t>(g) * K * N;
+    void* out_t = BATCH ? static_cast<void*>(static_cast<uint8_t*>(out) +
+                                             static_cast<int64_t>(g) * M * N * (OUT_BF16 ? 2 : 4))
+                        : out;
     const int bm_t = wide ? BM / 2 : BM, bn_t = wide ? 2 * BN : BN;     // this tile's shape
     const bool tail = row0 + bm_t > M;
     // this wave's output block: rows rbase .. +WM-1, columns cbase .. +63
@@ -314,7 +337,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     const int rbase = (wave / gn) * WM, cbase = (wave % gn) * WN;
     const FragOff fa = frag_off(rbase, lane);
     const FragOff fb = frag_off(cbase, lane);
-    const float* rs_g = rs + static_cast<int64_t>(g) * Kb * Nb;
+    const float* rs_g = BATCH ? rs : rs + static_cast<int64_t>(g) * Kb * Nb;
     // blockwise scales ride the stages: lane l of wave w stages the scale of
     // tile column 64(w mod 4) + l (clamped to the tile; surplus lanes and the
     // upper four of eight waves repeat columns, writing the same values)
@@ -333,10 +356,10 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     // prologue: stages 0 .. NST-2 in flight
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s) {
-      if (s < KT) {
+      if (s < KTt) {
         const int64_t kb = static_cast<int64_t>(s) * G_BK;
 #define MOE_SLOT(S, stg, kbv) \
-  issue_slot<TRANS, NW, S>(wide, stg, lhs, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
+  issue_slot<TRANS, NW, S>(wide, stg, lhs_t, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
         MOE_SLOT(0, smem + s * STAGE, kb); MOE_SLOT(1, smem + s * STAGE, kb); MOE_SLOT(2, smem + s * STAGE, kb);
         MOE_SLOT(3, smem + s * STAGE, kb); MOE_SLOT(4, smem + s * STAGE, kb); MOE_SLOT(5, smem + s * STAGE, kb);
         if constexpr (C::SLOTS == 12) {
@@ -353,16 +376,16 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       }
     }
 
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KTt; ++kt) {
       // this wave's loads of step kt have landed once at most the loads of the
       // NST-2 later stages are outstanding (loads complete in order)
-      if (kt + NST - 1 <= KT)
+      if (kt + NST - 1 <= KTt)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * loads_per_step<C, KBLOCKS>()));
       else
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       step_barrier();                         // everyone's have, and step kt-1's readers are done
       const int ks = kt + NST - 1;            // the step whose loads are issued now
-      const bool more = ks < KT;
+      const bool more = ks < KTt;
       const int64_t kb_next = static_cast<int64_t>(ks) * G_BK;
       uint8_t* nxt = smem + (ks % NST) * STAGE;
       const uint8_t* As = smem + (kt % NST) * STAGE;
@@ -440,6 +463,12 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
         s_out[j] = make_float4(rs_g[static_cast<uint32_t>(c) / ncol_blk], rs_g[static_cast<uint32_t>(c + 1) / ncol_blk],
                                rs_g[static_cast<uint32_t>(c + 2) / ncol_blk], rs_g[static_cast<uint32_t>(c + 3) / ncol_blk]);
     }
+    // BATCH: a group without rows writes exact zeros (its row scales were never loaded)
+    const bool empty = BATCH && KTt == 0;
+    if (empty) {
+#pragma unroll
+      for (int j = 0; j < JN; ++j) s_out[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     if (OUT_BF16) {
       const int ch_log = wide ? 5 : 4;          // log2 of the 16-byte chunks per output row
       const int OS = bn_t + 8;
@@ -451,7 +480,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       uint16_t* st_lane = st + (rbase + (lane & 15)) * OS + cbase + 4 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const float lsr = ls_tile[rbase + i * 16 + (lane & 15)];
+        const float lsr = empty ? 0.f : ls_tile[rbase + i * 16 + (lane & 15)];
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
           const uint32_t lo = pack_bf16x2(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y));
@@ -460,7 +489,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
         }
       }
       __syncthreads();
-      uint16_t* o = static_cast<uint16_t*>(out);
+      uint16_t* o = static_cast<uint16_t*>(out_t);
 #pragma unroll 4
       for (int it = 0; it < BM * (BN / 8) / G_THREADS; ++it) {     // same chunk count for both shapes
         const int id = it * G_THREADS + tid;
@@ -475,8 +504,8 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       for (int i = 0; i < MI; ++i) {
         const int r = rbase + i * 16 + (lane & 15);
         if (r >= rows_here) continue;
-        const float lsr = ls_tile[r];
-        float* o = static_cast<float*>(out) + (row0 + r) * N + col0 + cbase + 4 * (lane >> 4);
+        const float lsr = empty ? 0.f : ls_tile[r];
+        float* o = static_cast<float*>(out_t) + (row0 + r) * N + col0 + cbase + 4 * (lane >> 4);
 #pragma unroll
         for (int j = 0; j < JN; ++j)
           *reinterpret_cast<float4*>(o + j * 16) =
@@ -485,10 +514,9 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       }
     }
   }
-
 #undef MOE_SLOT
   // rows [n, M) are zero
-  const int64_t zero_rows = M - n_rows;
+  const int64_t zero_rows = BATCH ? 0 : M - n_rows;
   if (zero_rows > 0) {
     const int64_t per16 = OUT_BF16 ? 8 : 4;
     const int64_t total_chunks = zero_rows * N / per16;
@@ -528,6 +556,31 @@ hipError_t launch_dtype(bool bf16, const uint8_t* lhs, const float* ls, int per_
 
 size_t gmm_ws_bytes() { return tile::kHdr; }
 
+// The weight-gradient product on the gmm pipeline: for each local group g,
+// out[g] (M x N, f32 or bf16) = ls[m] * rs[n] * sum_r A[m, c_g + r] B[n, c_g + r]
+// with A [M, K] and B [N, K] contraction-contiguous (row stride K), c_g =
+// 128 * (the group's padded row offset in 128-row blocks), the group's rows
+// zero-padded to a multiple of 128; ls_len in {1, M}, rs_len in {1, N}.
+// Requires M % 256 == 0 and N % 128 == 0.
+hipError_t gmm_batched_launch(const uint8_t* A, const float* ls, int ls_len, const uint8_t* B, const float* rs,
+                              int rs_len, const int32_t* group_sizes, int g0, int El, int64_t max_rows, int64_t M,
+                              int64_t K, int64_t N, bool bf16, void* out, int32_t* err, hipStream_t st) {
+  using C = Cfg<MOE_GMM_CFG>;
+  const int64_t tiles = static_cast<int64_t>(El) * (M / C::BM) * (N / C::BN);
+  int64_t grid = tile::num_cus();
+  if (tiles < grid) grid = tiles;
+  if (grid < 8) grid = 8;          // the XCD split gives each of the 8 parts its own workgroups
+  const int per_row = ls_len == M ? 1 : 0;
+  const int Nb = rs_len == 1 ? 1 : static_cast<int>(N);
+  if (bf16)
+    gmm_kernel<C, true, false, true, true><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
+        A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
+  else
+    gmm_kernel<C, true, false, false, true><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
+        A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
+  return hipGetLastError();
+}
+
 }  // namespace moe
 
 extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const uint8_t* rhs,
@@ -560,9 +613,6 @@ extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_s
   const int per_row = lhs_scale_mode == MOE_SCALE_ROW_DYNAMIC ? 1 : 0;
   const bool bf16 = out_dtype == MOE_BF16;
   hipError_t e;
-#ifndef MOE_GMM_CFG
-#define MOE_GMM_CFG 256, 128, 3, 8
-#endif
   using C = moe::Cfg<MOE_GMM_CFG>;
 #define MOE_GMM_ARGS bf16, lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, group_sizes, group_offset, El, M, K, N, out, err, st
   if (transpose_rhs)

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void tgmm_kernel(const uint8_t* __restrict__ l
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f8(a[i], b[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f8(b[j], a[i], acc[i][j]);
         __syncthreads();
         if (rt + 1 < RT) {
           stash_tiles(Xs, Ds, tid, rx, rd);
@@ -75,30 +75,101 @@ __global__ __launch_bounds__(256) void tgmm_kernel(const uint8_t* __restrict__ l
         }
       }
     }
-    // epilogue: out[g, k, n] = ls[k] * rs[n] * acc
+    // epilogue: out[g, k, n] = ls[k] * rs[n] * acc.  The block product is
+    // formed transposed (dY fragment first), so lane l holds row
+    // k0 + 64 wm + 16 i + l%16 and the four consecutive columns
+    // n0 + 64 wn + 16 j + 4 (l/16) .. +3: one 16-byte (f32) or 8-byte (bf16)
+    // store per block.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + (lane & 15);
-      const float rsn = rs_len == 1 ? rs[0] : rs[n];
+      const int64_t n = n0 + wn * 64 + j * 16 + 4 * (lane >> 4);
+      const float4 rsn = rs_len == 1 ? make_float4(rs[0], rs[0], rs[0], rs[0])
+                                     : make_float4(rs[n], rs[n + 1], rs[n + 2], rs[n + 3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t k = k0 + wm * 64 + i * 16 + 4 * (lane >> 4) + v;
-          const float lsk = ls_len == 1 ? ls[0] : ls[k];
-          const float o = (lsk * rsn) * acc[i][j][v];
-          const int64_t idx = (static_cast<int64_t>(g) * K + k) * N + n;
-          if (OUT_BF16)
-            static_cast<uint16_t*>(out)[idx] = f32_to_bf16(o);
-          else
-            static_cast<float*>(out)[idx] = o;
+        const int64_t k = k0 + wm * 64 + i * 16 + (lane & 15);
+        const float lsk = ls_len == 1 ? ls[0] : ls[k];
+        const float o0 = (lsk * rsn.x) * acc[i][j][0], o1 = (lsk * rsn.y) * acc[i][j][1];
+        const float o2 = (lsk * rsn.z) * acc[i][j][2], o3 = (lsk * rsn.w) * acc[i][j][3];
+        const int64_t idx = (static_cast<int64_t>(g) * K + k) * N + n;
+        if (OUT_BF16) {
+          const uint32_t lo = f32_to_bf16(o0) | (static_cast<uint32_t>(f32_to_bf16(o1)) << 16);
+          const uint32_t hi = f32_to_bf16(o2) | (static_cast<uint32_t>(f32_to_bf16(o3)) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(o0, o1, o2, o3);
         }
       }
     }
   }
 }
 
+// ------------------------------------------------------------------ transpose
+// AT[c, 128 * tiles_off[g] + i] = A[rows_off[g] + i, c] for i < m_g and 0 for
+// m_g <= i < the group's padded length (a multiple of 128): the rows of each
+// group become a contraction axis of its own, contiguous per column.  64 x 64
+// byte tiles through LDS (row stride 68 bytes: the column reads of 64 rows hit
+// 64 distinct banks); grid-strided over (padded 64-row block, 64-column block).
+__global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __restrict__ A, int64_t C,
+                                                               const int32_t* __restrict__ group_sizes, int g0,
+                                                               int El, int64_t max_rows, int64_t Mpad,
+                                                               uint8_t* __restrict__ AT, int32_t* __restrict__ err) {
+  __shared__ GroupTable gt;
+  __shared__ int tmp[kMaxLocal];
+  __shared__ __attribute__((aligned(16))) uint8_t tl[64 * 68];
+  build_groups(group_sizes, g0, El, max_rows, 1, 128, err, gt, tmp, false);
+  const int64_t P = static_cast<int64_t>(gt.tiles_off[El]) * 128;    // padded rows
+  const int64_t cblocks = C / 64;
+  const int64_t items = (P / 64) * cblocks;
+  const int tid = threadIdx.x;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t pb = it / cblocks, cb = it - pb * cblocks;
+    const int64_t p0 = pb * 64;
+    // the group holding padded rows p0 .. p0 + 63 (padded lengths are multiples of 128)
+    int lo = 0, hi = El - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (static_cast<int64_t>(gt.tiles_off[mid]) * 128 <= p0) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int64_t i0 = p0 - static_cast<int64_t>(gt.tiles_off[g]) * 128;   // first local row of the block
+    const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
+    __syncthreads();                          // the previous item's reads of tl are done
+    {
+      const int r = tid >> 2, c16 = (tid & 3) * 16;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (i0 + r < m_g)
+        v = *reinterpret_cast<const uint4*>(A + (gt.rows_off[g] + i0 + r) * C + cb * 64 + c16);
+      uint32_t* d = reinterpret_cast<uint32_t*>(tl + r * 68 + c16);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    {
+      const int c = tid >> 2, r16 = (tid & 3) * 16;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        w[q] = static_cast<uint32_t>(tl[(r16 + 4 * q) * 68 + c]) |
+               (static_cast<uint32_t>(tl[(r16 + 4 * q + 1) * 68 + c]) << 8) |
+               (static_cast<uint32_t>(tl[(r16 + 4 * q + 2) * 68 + c]) << 16) |
+               (static_cast<uint32_t>(tl[(r16 + 4 * q + 3) * 68 + c]) << 24);
+      }
+      *reinterpret_cast<uint4*>(AT + (cb * 64 + c) * Mpad + p0 + r16) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 }  // namespace
+
+// Transposed-operand staging of the weight-gradient product: padded row
+// capacity (a multiple of 256) and workspace bytes.
+int64_t tgmm_mpad(int64_t M, int E) { return moe_cdiv(M + 128 * static_cast<int64_t>(E), 256) * 256; }
+size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int E) {
+  return tile::kHdr + static_cast<size_t>((K + N) * tgmm_mpad(M, E));
+}
+hipError_t gmm_batched_launch(const uint8_t* A, const float* ls, int ls_len, const uint8_t* B, const float* rs,
+                              int rs_len, const int32_t* group_sizes, int g0, int El, int64_t max_rows, int64_t M,
+                              int64_t K, int64_t N, bool bf16, void* out, int32_t* err, hipStream_t st);
 }  // namespace moe
 
 extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t lhs_scale_len,
@@ -124,6 +195,25 @@ extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t 
   if (static_cast<int64_t>(El) * (K / 128) * (N / 128) > INT32_MAX) return MOE_ERR_SHAPE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* err = static_cast<int32_t*>(ws);
+  // Main path: both operands transposed into the workspace (each group's rows
+  // become a contraction axis of their own), then the gmm pipeline per group.
+  // The one-kernel path (transposing in LDS while multiplying) serves smaller
+  // workspaces and K not a multiple of 256.
+  if (K % 256 == 0 && ws_bytes >= moe::tgmm_ws_bytes(M, K, N, E)) {
+    const int64_t Mpad = moe::tgmm_mpad(M, E);
+    uint8_t* XT = static_cast<uint8_t*>(ws) + moe::tile::kHdr;
+    uint8_t* DT = XT + K * Mpad;
+    const unsigned tgrid = static_cast<unsigned>(4 * moe::tile::num_cus());
+    if (M > 0) {
+      moe::transpose_groups_kernel<<<tgrid, 256, 0, st>>>(lhs, K, group_sizes, group_offset, El, M, Mpad, XT, err);
+      MOE_CHECK_LAUNCH();
+      moe::transpose_groups_kernel<<<tgrid, 256, 0, st>>>(rhs, N, group_sizes, group_offset, El, M, Mpad, DT, err);
+      MOE_CHECK_LAUNCH();
+    }
+    return moe::gmm_batched_launch(XT, lhs_scale, lhs_scale_len, DT, rhs_scale, rhs_scale_len, group_sizes,
+                                   group_offset, El, M, K, Mpad, N, out_dtype == MOE_BF16, out, err, st) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
+  }
   const int64_t ub = static_cast<int64_t>(El) * (K / moe::tile::BM) * (N / moe::tile::BN);
   int64_t grid = 2LL * moe::tile::num_cus();
   if (ub < grid) grid = ub;

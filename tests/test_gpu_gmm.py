@@ -246,3 +246,29 @@ def test_tgmm_config5_sampled():
     print("config 5 dW", st)
     # property at full size: every group's gradient was written (no fill value left)
     assert not (g == 5.0).any()
+
+
+@pytest.mark.parametrize("K,small_ws", [(384, False), (256, True)])
+def test_tgmm_one_kernel_path(K, small_ws):
+    """The one-kernel tgmm (operands transposed in LDS while multiplying) serves
+    K not a multiple of 256 and workspaces too small for the transposed copies."""
+    rng = np.random.default_rng(K + small_ws)
+    gs = np.array([5, 0, 140, 67], np.int32)
+    E = len(gs)
+    M = int(gs.sum()) + 3
+    N = 256
+    X = rng.integers(0, 0x7E, (M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)).astype(np.uint8) << 7)
+    D = rng.integers(0, 0x7E, (M, N)).astype(np.uint8) | (rng.integers(0, 2, (M, N)).astype(np.uint8) << 7)
+    xs = np.array([0.02], np.float32)
+    ds = rng.uniform(0.01, 1, N).astype(np.float32)
+    o = tgmm(X, xs, D, ds, gs, 0, E)
+    out = torch.full((E, K, N), 5.0, dtype=torch.float32, device="cuda")
+    ws = m.workspace(m.MOE_OP_GMM if small_ws else m.MOE_OP_TGMM, M, K, N, E)
+    print(f"tgmm one-kernel K={K} ws={ws.numel()}", flush=True)
+    m.moe_tgmm_fp8(dev_u8(X), dev_f32(xs), 1, dev_u8(D), dev_f32(ds), N, dev_i32(gs), E, 0, E, M, K, N, m.MOE_F32,
+                   out, ws)
+    assert m.moe_debug_check(ws) == 0
+    g = host(out)
+    B = lambda idx: tgmm_allowance(X, xs, D, ds, gs, 0, E, idx // (K * N), (idx // N) % K, idx % N)
+    check_f32(g, o["out"], o["abs_sum"], B, f"tgmm one-kernel K={K}")
+    assert not g[1].any()
