@@ -24,10 +24,12 @@
 // complete in order), then one barrier per K step.  The loads of a step are
 // spread over the MFMA rounds of the previous ones so a stalled load issue
 // never holds a long run of MFMAs.  Inside a staged row the 16-byte chunk c
-// sits at slot c ^ f(row), f(r) = ((r >> 1) & 7) ^ (((r >> 5) & 1) << 2):
-// the 16-byte fragment reads of 16 consecutive rows and the 8-byte
-// transpose reads (8 rows from each of two 32-row bands) then touch
-// distinct banks.
+// sits at slot c ^ f(row), f(r) = (r & 7) ^ (((r >> 3) ^ (r >> 5)) & 1):
+// the 16-byte fragment reads of 8 (or 16) consecutive rows per lane group
+// and the 8-byte transpose reads (8 rows from each of two 32-row bands) then
+// touch distinct banks.  (An earlier f, ((r >> 1) & 7) ^ 4((r >> 5) & 1),
+// measured 0.94 bank-conflict cycles per LDS access on this target: it
+// serves a 16-byte read 8 lanes at a time.)
 //  * K-contiguous operands (lhs rows; rhs stored [E, N, K]) are read as two
 //    16-byte chunks per fragment;
 //  * rhs stored [E, K, N] is staged as [128 k][128 n] halves and read with
@@ -64,6 +66,20 @@
 #ifndef MOE_GMM_CFG
 #define MOE_GMM_CFG 256, 128, 3, 8     // BM, BN, stages, waves
 #endif
+#ifndef MOE_SWZ
+#define MOE_SWZ 1                      // 0: the earlier pair-row chunk swizzle
+#endif
+// Which pipeline each entry uses (0: per-tile, 1: streaming, 2: streaming
+// with the stores deferred into the next tile's first step).  Measured: the
+// per-tile kernel is faster on the grouped forward product with ragged
+// groups; the streaming kernel on the weight-gradient product, whose tiles
+// have only a few K steps each.
+#ifndef MOE_GMM_STREAM
+#define MOE_GMM_STREAM 0
+#endif
+#ifndef MOE_GMM_STREAM_BATCH
+#define MOE_GMM_STREAM_BATCH 1
+#endif
 
 namespace moe {
 namespace {
@@ -72,14 +88,25 @@ using namespace tile;
 constexpr int G_BK = 128;
 typedef __attribute__((address_space(3))) void lds_void;
 
+#if MOE_SWZ
+// Chunk slot swizzle of staged row r: any 8 consecutive rows from a multiple
+// of 8 use 8 distinct 16-byte slots, and rows r and r + 8 (and r and r + 32)
+// differ in slot parity, so a 16-byte read of 8 (or 16) consecutive rows per
+// lane group and the 8-byte transpose reads of 8 rows from each of two 32-row
+// bands meet distinct banks.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ (((row >> 3) ^ (row >> 5)) & 1); }
+constexpr int SWZ_FLIP = 1;      // the slot bit the per-instruction bit flips
+#else
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 5) & 1) << 2); }
+constexpr int SWZ_FLIP = 4;
+#endif
 
 // Per-lane pieces of the staging addresses.  A load instruction fills staged
 // rows R .. R+7 (R a multiple of 8); lane l fetches row R + l/8 into slot l%8,
 // i.e. logical chunk (l%8) ^ swz(R + l/8).  For the R a wave issues, that
-// chunk is c0 ^ 4*p with c0 = (l%8) ^ (l/16) and p a per-instruction bit, so
-// a lane needs only two offsets per operand; the rest of the address is
-// uniform (scalar registers).
+// chunk is c0 ^ SWZ_FLIP*p with c0 = (l%8) ^ (the lane's part of the swizzle)
+// and p a per-instruction bit, so a lane needs only two offsets per operand;
+// the rest of the address is uniform (scalar registers).
 struct LaneOff {
   uint32_t v0, v1;
   // arithmetic select: keeps the pair in registers
@@ -87,15 +114,60 @@ struct LaneOff {
 };
 
 __device__ __forceinline__ LaneOff stage_lane_off(int lane, int64_t stride) {
-  const int sub = lane >> 3, c0 = (lane & 7) ^ (sub >> 1);
+  const int sub = lane >> 3, c0 = (lane & 7) ^ (MOE_SWZ ? sub : sub >> 1);
   LaneOff o;
   o.v0 = static_cast<uint32_t>(sub * stride + 16 * c0);
-  o.v1 = static_cast<uint32_t>(sub * stride + 16 * (c0 ^ 4));
+  o.v1 = static_cast<uint32_t>(sub * stride + 16 * (c0 ^ SWZ_FLIP));
   return o;
 }
 
 // Swizzle bit of the instruction that fills rows R .. R+7 (R % 8 == 0).
 __device__ __forceinline__ int stage_bit(int R) { return ((R >> 3) & 1) ^ ((R >> 5) & 1); }
+
+// Slot S of a wave's 48/NW loads per K step loads A (lhs) rows: a wave's
+// first slots load A.
+template <int NW, int S>
+__device__ __forceinline__ bool slot_is_a(bool wide) { return S < (wide ? 16 / NW : 32 / NW); }
+
+// Staged row of slot S's first row inside its operand, and the slot's LDS
+// byte offset inside a stage.
+template <int NW, int S>
+__device__ __forceinline__ int slot_row(bool wide, int wave) {
+  return slot_is_a<NW, S>(wide) ? wave * (wide ? 128 / NW : 256 / NW) + 8 * S
+                                : wave * (wide ? 256 / NW : 128 / NW) + 8 * (S - (wide ? 16 / NW : 32 / NW));
+}
+template <int NW, int S>
+__device__ __forceinline__ int slot_dst(bool wide, int wave) {
+  return slot_is_a<NW, S>(wide) ? slot_row<NW, S>(wide, wave) * G_BK
+                                : (wide ? 128 : 256) * G_BK + slot_row<NW, S>(wide, wave) * G_BK;
+}
+
+// This lane's source of slot S at contraction offset 0; step kb reads
+// src0 + kb (lhs rows, rhs [E, N, K]) or src0 + kb * N (rhs [E, K, N]).
+template <bool TRANS, int NW, int S>
+__device__ __forceinline__ const uint8_t* slot_src0(bool wide, const uint8_t* __restrict__ lhs,
+                                                    const uint8_t* __restrict__ wg, int64_t K, int64_t N, int64_t row0,
+                                                    int64_t col0, int64_t M, bool tail, int wave, int lane,
+                                                    const LaneOff offK, const LaneOff offN) {
+  const int R = slot_row<NW, S>(wide, wave);
+  if (slot_is_a<NW, S>(wide)) {
+    const uint32_t off = offK.pick(stage_bit(R));
+    if (!tail) return lhs + (row0 + R) * K + off;
+    const int sub = lane >> 3;
+    const int64_t r = min(row0 + R + sub, M - 1);
+    return lhs + r * K + (off - static_cast<uint32_t>(sub * K));
+  }
+  if (TRANS)      // staged row r = output column col0 + r
+    return wg + (col0 + R) * K + offK.pick(stage_bit(R));
+  // staged half R / 128 holds columns 128h.., staged row = contraction index
+  return wg + static_cast<int64_t>(R & 127) * N + col0 + 128 * (R >> 7) + offN.pick(stage_bit(R));
+}
+
+// Slot S's direct-to-LDS load from a computed source.
+template <int NW, int S>
+__device__ __forceinline__ void issue_from(const uint8_t* src, bool wide, uint8_t* stage, int wave) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + slot_dst<NW, S>(wide, wave)), 16, 0, 0);
+}
 
 // Load slot S (0 .. 48/NW - 1) of one K step for wave `wave` of NW: one
 // direct-to-LDS instruction filling 8 staged rows.  A plain tile stages 256
@@ -109,31 +181,9 @@ __device__ __forceinline__ void issue_slot(bool wide, uint8_t* stage, const uint
                                            const uint8_t* __restrict__ wg, int64_t K, int64_t N, int64_t row0,
                                            int64_t col0, int64_t M, bool tail, int64_t kb, int wave, int lane,
                                            const LaneOff offK, const LaneOff offN) {
-  // rows per wave: plain A 256/NW, B 128/NW; wide A 128/NW, B 256/NW
-  const int nA = wide ? 16 / NW : 32 / NW;
-  const bool isA = S < nA;
-  const uint8_t* src;
-  int dst;
-  if (isA) {
-    const int R = wave * (wide ? 128 / NW : 256 / NW) + 8 * S;
-    const uint32_t off = offK.pick(stage_bit(R));
-    if (!tail) {
-      src = lhs + (row0 + R) * K + kb + off;
-    } else {
-      const int sub = lane >> 3;
-      const int64_t r = min(row0 + R + sub, M - 1);
-      src = lhs + r * K + kb + (off - static_cast<uint32_t>(sub * K));
-    }
-    dst = R * G_BK;
-  } else {
-    const int R = wave * (wide ? 256 / NW : 128 / NW) + 8 * (S - nA);
-    if (TRANS)      // staged row r = output column col0 + r
-      src = wg + (col0 + R) * K + kb + offK.pick(stage_bit(R));
-    else            // staged half R / 128 holds columns 128h.., staged row = contraction index
-      src = wg + (kb + (R & 127)) * N + col0 + 128 * (R >> 7) + offN.pick(stage_bit(R));
-    dst = (wide ? 128 : 256) * G_BK + R * G_BK;
-  }
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + dst), 16, 0, 0);
+  const uint8_t* src = slot_src0<TRANS, NW, S>(wide, lhs, wg, K, N, row0, col0, M, tail, wave, lane, offK, offN);
+  src += (TRANS || slot_is_a<NW, S>(wide)) ? kb : kb * N;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + slot_dst<NW, S>(wide, wave)), 16, 0, 0);
 }
 
 // Two floats to packed bfloat16 (low half from lo), rounding to nearest even
@@ -169,20 +219,21 @@ __device__ __forceinline__ void lds_read_4x16f(const float* p, float4 (&r)[4]) {
 }
 
 // LDS byte offsets of the two 16-byte chunks of MFMA fragment rows
-// base + 16*i + l%16 (base % 128 == 0): swz of those rows is
-// ((l%16) >> 1) ^ 4*((i >> 1) & 1), so two variants cover every i.
+// base + 16*i + l%16 (base % 64 == 0): swz of those rows is
+// f(l%16) ^ SWZ_FLIP*((i >> 1) & 1), so two variants cover every i.
 struct FragOff {
   int lo[2], hi[2];
 };
 
 __device__ __forceinline__ FragOff frag_off(int base, int lane) {
-  const int l15 = lane & 15, grp = lane >> 4, f = l15 >> 1;
+  const int l15 = lane & 15, grp = lane >> 4;
+  const int f = MOE_SWZ ? (l15 & 7) ^ (l15 >> 3) : l15 >> 1;
   FragOff o;
   const int row = (base + l15) * G_BK;
   o.lo[0] = row + 16 * ((2 * grp) ^ f);
   o.hi[0] = row + 16 * ((2 * grp + 1) ^ f);
-  o.lo[1] = row + 16 * ((2 * grp) ^ f ^ 4);
-  o.hi[1] = row + 16 * ((2 * grp + 1) ^ f ^ 4);
+  o.lo[1] = row + 16 * ((2 * grp) ^ f ^ SWZ_FLIP);
+  o.hi[1] = row + 16 * ((2 * grp + 1) ^ f ^ SWZ_FLIP);
   return o;
 }
 
@@ -528,6 +579,497 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
   }
 }
 
+// ---------------------------------------------------------------- streaming
+// gmm_stream_kernel: the same tiles, wave grid, staging and MFMA rounds as
+// gmm_kernel, with one load pipeline through all of a workgroup's tiles.
+// The loads that go out while the waves multiply step q belong to step
+// q + NST - 1 of the workgroup's whole sequence of K steps, which near the
+// end of a tile is a step of the next tile (or of the one after it, when
+// tiles have a single step) -- so a tile starts with its first stages
+// already landed, and short tiles (few K steps) no longer pay the load
+// latency at every tile start.
+//  * A tile's first step also stages its parameters into one of three LDS
+//    parameter slots: the lhs scales of its rows and the weight scales of its
+//    columns (one 4-byte direct load per wave).  The slot of tile j is read
+//    by tile j's epilogue at the end of its last step and refilled by tile
+//    j + 3's first step, which is issued at least one barrier later.
+//  * The wait before step q counts exactly the loads issued after step q's:
+//    the next step's SLOTS (+1 blockwise scale) loads, plus one when that
+//    step starts a tile.
+//  * The epilogue writes the output from registers, since the stages in
+//    flight occupy the LDS: float32 as one 16-byte store per 16 x 16 block
+//    and lane; bfloat16 after two lane swaps per dword pair
+//    (v_permlane32_swap, then v_permlane16_swap), which turn a lane's two
+//    blocks' four-column pieces into eight consecutive columns of its row --
+//    again one 16-byte store.  With PEND the converted tile waits in
+//    registers and its stores go out during the next tile's first step,
+//    interleaved with its MFMA rounds.
+constexpr int kStreamMaxLocal = 512;   // group table capacity (LDS budget)
+constexpr int PRM = 512;               // floats per parameter slot: 256 row scales, 256 column scales
+constexpr int PRM_SLOTS = 3;
+
+struct TileDesc {
+  int g, KT, rows_here, wide;
+  int64_t row0, col0, cofs;
+};
+
+// Decode tile t exactly as gmm_kernel does (n-tile major, m-tiles fastest,
+// wide tails after their two n-tiles' full m-tiles; BATCH: per-group m x n
+// grid over the group's padded contraction columns).
+template <class C, bool BATCH, class GT>
+__device__ __forceinline__ TileDesc decode_tile(const GT& gt, int El, int MTb, int NT, int KT, int t) {
+  constexpr int BM = C::BM, BN = C::BN;
+  const int g = BATCH ? t / (MTb * NT) : find_group(gt, El, t);
+  const int local = BATCH ? t - g * (MTb * NT) : t - gt.tiles_off[g];
+  const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
+  const int full = m_g / BM, rem = m_g - full * BM;
+  int nt, mt, wide = 0;
+  if (BATCH) {
+    nt = local / MTb;
+    mt = local - nt * MTb;
+  } else if (rem == 0 || rem > BM / 2) {
+    const int per = full + (rem ? 1 : 0);
+    nt = local / per;
+    mt = local - nt * per;
+  } else {
+    const int pairblk = 2 * full + 1, npair = NT / 2;
+    if (local < npair * pairblk) {
+      const int pr = local / pairblk, w = local - pr * pairblk;
+      if (w < 2 * full) {
+        const int h = w >= full ? 1 : 0;
+        nt = 2 * pr + h;
+        mt = w - h * full;
+      } else {
+        nt = 2 * pr;
+        mt = full;
+        wide = 1;
+      }
+    } else {
+      nt = NT - 1;
+      mt = local - npair * pairblk;
+    }
+  }
+  TileDesc d;
+  d.g = g;
+  d.wide = wide;
+  d.row0 = BATCH ? static_cast<int64_t>(mt) * BM : gt.rows_off[g] + static_cast<int64_t>(mt) * BM;
+  d.rows_here = BATCH ? BM : min(BM, m_g - mt * BM);
+  d.col0 = static_cast<int64_t>(nt) * BN;
+  d.cofs = BATCH ? static_cast<int64_t>(gt.tiles_off[g]) * G_BK : 0;
+  d.KT = BATCH ? (m_g + G_BK - 1) / G_BK : KT;
+  return d;
+}
+
+// Four LDS floats at p + {0, 16, 32, 48}, completed before returning (one asm
+// block, for the same reason as lds_read_4x16f).
+__device__ __forceinline__ float4 lds_read_4x1f(const float* p) {
+  typedef const __attribute__((address_space(3))) float lds_f32;
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_f32*)p));
+  float x, y, z, w;
+  asm volatile(
+      "ds_read_b32 %0, %4\n\t"
+      "ds_read_b32 %1, %4 offset:64\n\t"
+      "ds_read_b32 %2, %4 offset:128\n\t"
+      "ds_read_b32 %3, %4 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x), "=&v"(y), "=&v"(z), "=&v"(w)
+      : "v"(a)
+      : "memory");
+  return make_float4(x, y, z, w);
+}
+
+// Lane l = 16 g + r holds, for the blocks of columns 32p .. 32p+15 (P) and
+// 32p+16 .. 32p+31 (Q) of its row r, the packed bfloat16 pairs of columns
+// 4g .. 4g+3 of each.  Returns columns 32p + 8g .. 32p + 8g + 7 of the same
+// row: the 32-lane swap exchanges P of lane groups 2, 3 with Q of groups 0, 1,
+// the 16-lane swap then exchanges odd groups of the first operand with even
+// groups of the second.
+__device__ __forceinline__ uint4 row8_from_blocks(uint32_t p0, uint32_t p1, uint32_t q0, uint32_t q1) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(p0, q0, false, false);
+  const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(p1, q1, false, false);
+  const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+  return make_uint4(t0[0], t1[0], t0[1], t1[1]);
+}
+
+// One tile's output as it leaves the registers: 16-byte pieces of the lane's
+// row (base + 16 i) at column offsets (elements) col_of(i, u).
+template <class C, bool OUT_BF16>
+struct OutPieces {
+  static constexpr int U = OUT_BF16 ? C::JN / 2 : C::JN;   // pieces per row block
+  uint4 v[C::MI][U];
+};
+
+// Scale and convert the accumulators: out = ls[row] * (acc * cs[col]).
+template <class C, bool OUT_BF16>
+__device__ __forceinline__ void convert_tile(const v4f (&acc)[C::MI][C::JN], const float4 lsr, const float4 (&cs)[C::JN],
+                                             OutPieces<C, OUT_BF16>& o) {
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) {
+    const float l = i == 0 ? lsr.x : i == 1 ? lsr.y : i == 2 ? lsr.z : lsr.w;
+    if constexpr (OUT_BF16) {
+#pragma unroll
+      for (int p = 0; p < C::JN / 2; ++p) {
+        const v4f& a = acc[i][2 * p];
+        const v4f& b = acc[i][2 * p + 1];
+        const float4 sa = cs[2 * p], sb = cs[2 * p + 1];
+        const uint32_t p0 = pack_bf16x2(l * (a[0] * sa.x), l * (a[1] * sa.y));
+        const uint32_t p1 = pack_bf16x2(l * (a[2] * sa.z), l * (a[3] * sa.w));
+        const uint32_t q0 = pack_bf16x2(l * (b[0] * sb.x), l * (b[1] * sb.y));
+        const uint32_t q1 = pack_bf16x2(l * (b[2] * sb.z), l * (b[3] * sb.w));
+        o.v[i][p] = row8_from_blocks(p0, p1, q0, q1);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::JN; ++j) {
+        const v4f& a = acc[i][j];
+        o.v[i][j] = make_uint4(__float_as_uint(l * (a[0] * cs[j].x)), __float_as_uint(l * (a[1] * cs[j].y)),
+                               __float_as_uint(l * (a[2] * cs[j].z)), __float_as_uint(l * (a[3] * cs[j].w)));
+      }
+    }
+  }
+}
+
+// The buffer descriptor of a tile's output rows: base = its first row,
+// range = its valid rows, so a piece of a row past the tile is dropped by
+// the range check -- every wave issues the same number of stores, which
+// keeps the pipeline's wait counts exact.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(uint8_t* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
+}
+
+// Row block i of a converted tile: voff = the byte offset of the lane's row
+// of block 0 and its first column from the tile's first row.
+template <class C, bool OUT_BF16>
+__device__ __forceinline__ void store_rows(const OutPieces<C, OUT_BF16>& o, int i, __amdgpu_buffer_rsrc_t r,
+                                           uint32_t voff, uint32_t row_bytes) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int u = 0; u < OutPieces<C, OUT_BF16>::U; ++u) {   // bf16: 32 columns apart; f32: 16
+    const uint4 v = o.v[i][u];
+    __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, voff + 16 * i * row_bytes + u * 64, 0, 0);
+  }
+}
+
+template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH, bool PEND>
+__global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
+    const uint8_t* __restrict__ lhs, const float* __restrict__ ls, int ls_per_row, const uint8_t* __restrict__ rhs,
+    const float* __restrict__ rs, int Kb, int Nb, const int32_t* __restrict__ group_sizes, int g0, int El, int64_t M,
+    int64_t K, int64_t N, void* __restrict__ out, int32_t* __restrict__ err, int64_t max_rows) {
+  constexpr int BM = C::BM, BN = C::BN, NST = C::NST, WM = C::WM, WN = C::WN, MI = C::MI, JN = C::JN;
+  constexpr int STAGE = C::STAGE, NW = C::NW;
+  static_assert(BM == 256 && BN == 128 && NST == 3 && NW == 8 && JN == 4, "streaming layout");
+  constexpr int LPS = loads_per_step<C, KBLOCKS>();
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) float prm[PRM_SLOTS * PRM];
+  __shared__ GroupTableN<kStreamMaxLocal> gt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w4 = wave & 3;
+  const int NT = static_cast<int>(N / BN);
+  const int MTb = static_cast<int>(M / BM);
+  if constexpr (BATCH)
+    build_groups(group_sizes, g0, El, max_rows, 1, G_BK, err, gt, reinterpret_cast<int*>(smem), false);
+  else
+    build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), true);
+  const int total = BATCH ? El * MTb * NT : gt.tiles_off[El];
+  const int n_rows = gt.rows_off[El];
+  const int KT = static_cast<int>(K / G_BK);
+  const int steps_per_block = static_cast<int>(K / Kb / G_BK);
+  const uint32_t ncol_blk = static_cast<uint32_t>(N / Nb);
+  int first, last, tstep;
+  xcd_share(total, first, last, tstep);
+  const LaneOff offK = stage_lane_off(lane, K);
+  const LaneOff offN = stage_lane_off(lane, N);
+  const int64_t row_bytes = N * ESZ;
+
+  // ---- load cursor: tile lt (descriptor L), its step lk, its parameter slot
+  int lt = first, lk = 0, lslot = 0;
+  TileDesc L = {};
+  while (lt < last) {
+    L = decode_tile<C, BATCH>(gt, El, MTb, NT, KT, lt);
+    if (L.KT > 0) break;
+    lt += tstep;
+  }
+
+  // per load tile: this lane's six slot sources at contraction offset 0 and
+  // its blockwise-scale source (first block)
+  const uint8_t* lsrc[6];
+  const float* lsc = rs;
+#define MOE_SPLAN()                                                                                              \
+  do {                                                                                                           \
+    const bool tl = L.row0 + (L.wide ? BM / 2 : BM) > M;                                                         \
+    const uint8_t* lh = lhs + L.cofs;                                                                            \
+    const uint8_t* wgl = BATCH ? rhs + L.cofs : rhs + L.g * K * N;                                               \
+    const bool wd = L.wide != 0;                                                                                 \
+    lsrc[0] = slot_src0<TRANS, NW, 0>(wd, lh, wgl, K, N, L.row0, L.col0, M, tl, wave, lane, offK, offN);         \
+    lsrc[1] = slot_src0<TRANS, NW, 1>(wd, lh, wgl, K, N, L.row0, L.col0, M, tl, wave, lane, offK, offN);         \
+    lsrc[2] = slot_src0<TRANS, NW, 2>(wd, lh, wgl, K, N, L.row0, L.col0, M, tl, wave, lane, offK, offN);         \
+    lsrc[3] = slot_src0<TRANS, NW, 3>(wd, lh, wgl, K, N, L.row0, L.col0, M, tl, wave, lane, offK, offN);         \
+    lsrc[4] = slot_src0<TRANS, NW, 4>(wd, lh, wgl, K, N, L.row0, L.col0, M, tl, wave, lane, offK, offN);         \
+    lsrc[5] = slot_src0<TRANS, NW, 5>(wd, lh, wgl, K, N, L.row0, L.col0, M, tl, wave, lane, offK, offN);         \
+    if (KBLOCKS)                                                                                                 \
+      lsc = (BATCH ? rs : rs + static_cast<int64_t>(L.g) * Kb * Nb) +                                            \
+            static_cast<uint32_t>(L.col0 + min(w4 * 64 + lane, (L.wide ? 2 * BN : BN) - 1)) / ncol_blk;         \
+  } while (0)
+  if (lt < last) MOE_SPLAN();
+#define MOE_SSLOT(S, stg, kbv)                                                                                   \
+  issue_from<NW, S>(lsrc[S] + ((TRANS || slot_is_a<NW, S>(L.wide != 0)) ? (kbv) : (kbv) * N), L.wide != 0, stg, wave)
+  // the step's extra loads: its blockwise weight scales, and on a tile's first
+  // step the tile's parameters (waves 0-3 the row scales, 4-7 the column scales)
+#define MOE_SEXTRA(stg)                                                                                          \
+  do {                                                                                                           \
+    const int bn_l = L.wide ? 2 * BN : BN;                                                                       \
+    const float* rs_l = BATCH ? rs : rs + static_cast<int64_t>(L.g) * Kb * Nb;                                   \
+    if (KBLOCKS)                                                                                                 \
+      __builtin_amdgcn_global_load_lds(lsc + static_cast<int64_t>(lk / steps_per_block) * Nb,                     \
+                                       (lds_void*)(stg + C::SC_OFF + w4 * 256), 4, 0, 0);                         \
+    if (lk == 0) {                                                                                               \
+      float* pslot = prm + lslot * PRM;                                                                          \
+      if (wave < 4) {                                                                                            \
+        const int r = min(w4 * 64 + lane, L.rows_here - 1);                                                      \
+        __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? L.row0 + r : 0), (lds_void*)(pslot + w4 * 64), 4, 0, \
+                                         0);                                                                     \
+      } else {                                                                                                   \
+        const int c = min(w4 * 64 + lane, bn_l - 1);                                                             \
+        __builtin_amdgcn_global_load_lds(rs_l + static_cast<uint32_t>(L.col0 + c) / ncol_blk,                    \
+                                         (lds_void*)(pslot + 256 + w4 * 64), 4, 0, 0);                           \
+      }                                                                                                          \
+    }                                                                                                            \
+  } while (0)
+  // after a step's loads: next step, or the next tile with steps
+#define MOE_SADVANCE()                                 \
+  do {                                                 \
+    if (++lk == L.KT) {                                \
+      lk = 0;                                          \
+      lslot = lslot == PRM_SLOTS - 1 ? 0 : lslot + 1;  \
+      lt += tstep;                                     \
+      while (lt < last) {                              \
+        L = decode_tile<C, BATCH>(gt, El, MTb, NT, KT, lt); \
+        if (L.KT > 0) break;                           \
+        lt += tstep;                                   \
+      }                                                \
+      if (lt < last) MOE_SPLAN();                      \
+    }                                                  \
+  } while (0)
+
+  // ---- prologue: steps 0 .. NST-2 of the sequence
+  int issued = 0;
+  bool next_starts = false;      // the step after the one computed next starts a tile
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) {
+    if (lt < last) {
+      uint8_t* stg = smem + s * STAGE;
+      const int64_t kb = static_cast<int64_t>(lk) * G_BK;
+      MOE_SSLOT(0, stg, kb); MOE_SSLOT(1, stg, kb); MOE_SSLOT(2, stg, kb);
+      MOE_SSLOT(3, stg, kb); MOE_SSLOT(4, stg, kb); MOE_SSLOT(5, stg, kb);
+      if (s == 1) next_starts = lk == 0;
+      MOE_SEXTRA(stg);
+      ++issued;
+      MOE_SADVANCE();
+    }
+  }
+
+  // ---- compute cursor: tile ct (descriptor Cd), its step ck, its slot
+  int ct = first, ck = 0, cslot = 0;
+  TileDesc Cd = {};
+  const int gn_plain = BN / WN;
+  // the empty tiles of a BATCH sequence get zeros; then the first tile with steps
+  OutPieces<C, OUT_BF16> po;
+  __amdgpu_buffer_rsrc_t p_rsrc = tile_rsrc(static_cast<uint8_t*>(out), 0);   // the converted tile's rows
+  uint32_t p_voff = 0;
+  bool have_pend = false;
+  // stores issued after the loads of the steps in flight: st_prev = all
+  // stores of the previous iteration, st_tail2 = the stores that followed
+  // the last load of the iteration before it; drain = zero tiles were
+  // written (a variable count): wait for everything once
+  constexpr int ST = MI * OutPieces<C, OUT_BF16>::U;   // stores per converted tile and wave
+  constexpr int ST_TAIL = PEND ? OutPieces<C, OUT_BF16>::U : ST;
+  bool st_prev = false, st_tail2 = false, drain = false;
+#define MOE_ZERO_TILE(D)                                                                                         \
+  do {                                                                                                           \
+    const int rb = (wave / gn_plain) * WM, cb = (wave % gn_plain) * WN;                                          \
+    const __amdgpu_buffer_rsrc_t zr = tile_rsrc(static_cast<uint8_t*>(out) + static_cast<int64_t>(D.g) * M * row_bytes + \
+                                                D.row0 * row_bytes, static_cast<uint32_t>(D.rows_here * row_bytes)); \
+    const uint32_t zo = static_cast<uint32_t>((rb + (lane & 15)) * row_bytes + (D.col0 + cb) * ESZ + 16 * (lane >> 4)); \
+    OutPieces<C, OUT_BF16> z;                                                                                    \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) _Pragma("unroll") for (int u = 0; u < OutPieces<C, OUT_BF16>::U; ++u) \
+        z.v[i][u] = make_uint4(0, 0, 0, 0);                                                                      \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(z, i, zr, zo, static_cast<uint32_t>(row_bytes)); \
+    drain = true;                                                                                                \
+  } while (0)
+  while (ct < last) {
+    Cd = decode_tile<C, BATCH>(gt, El, MTb, NT, KT, ct);
+    if (Cd.KT > 0) break;
+    MOE_ZERO_TILE(Cd);
+    ct += tstep;
+  }
+  int gn = Cd.wide ? 2 * BN / WN : BN / WN;
+  int rbase = (wave / gn) * WM, cbase = (wave % gn) * WN;
+  FragOff fa = frag_off(rbase, lane);
+  FragOff fb = frag_off(cbase, lane);
+
+  v4f acc[MI][JN];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  int q = 0, cur = 0;            // sequence step being computed, its stage
+  while (ct < last) {
+    // this wave's loads of step q have landed once at most the operations
+    // issued after them are outstanding: the next step's loads and the stores
+    // that went out since (vector-memory operations, loads and stores alike,
+    // complete in issue order)
+    if (issued > q + 1 && !drain) {
+      const int code = (next_starts ? 1 : 0) | (st_prev ? 2 : 0) | (st_tail2 ? 4 : 0);
+      switch (code) {
+        case 0: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST_TAIL)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST_TAIL)); break;
+        case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST + ST_TAIL)); break;
+        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST + ST_TAIL)); break;
+      }
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    drain = false;
+    step_barrier();                         // everyone's have, and step q-1's readers are done
+    const bool more = lt < last;
+    const int nxt_i = cur == 0 ? 2 : cur - 1;     // (cur + NST - 1) % NST
+    uint8_t* nxt = smem + nxt_i * STAGE;
+    const int64_t kb_next = static_cast<int64_t>(lk) * G_BK;
+    const bool starts = lk == 0;
+    const uint8_t* As = smem + cur * STAGE;
+    const uint8_t* Bs = As + (Cd.wide ? BM / 2 : BM) * G_BK;
+    float4 s_col[JN];
+    if (KBLOCKS) {
+      const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + 4 * (lane >> 4);
+      lds_read_4x16f(sc, s_col);
+    }
+    v8i b[JN];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+      const int n0 = cbase + j * 16;
+      if (TRANS)
+        b[j] = frag_i(Bs, fb, j);
+      else
+        b[j] = frag_tr_swz(Bs + (n0 >> 7) * (128 * G_BK), n0 & 127, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const v8i a = frag_i(As, fa, i);
+      if (more) {
+        if (i == 0) { MOE_SSLOT(0, nxt, kb_next); MOE_SSLOT(1, nxt, kb_next); MOE_SEXTRA(nxt); }
+        if (i == 1) { MOE_SSLOT(2, nxt, kb_next); }
+        if (i == 2) { MOE_SSLOT(3, nxt, kb_next); MOE_SSLOT(4, nxt, kb_next); }
+        if (i == 3) { MOE_SSLOT(5, nxt, kb_next); }
+      }
+      if (PEND && have_pend) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        if (KBLOCKS) {
+          const v4f p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
+          acc[i][j][0] = fmaf(s_col[j].x, p[0], acc[i][j][0]);
+          acc[i][j][1] = fmaf(s_col[j].y, p[1], acc[i][j][1]);
+          acc[i][j][2] = fmaf(s_col[j].z, p[2], acc[i][j][2]);
+          acc[i][j][3] = fmaf(s_col[j].w, p[3], acc[i][j][3]);
+        } else {
+          acc[i][j] = mfma_f8(b[j], a, acc[i][j]);
+        }
+      }
+    }
+    // this iteration's stores (PEND: the pending tile's, interleaved with the
+    // rounds' loads; otherwise the epilogue's below, after all its loads)
+    bool st_now = PEND && have_pend;
+    have_pend = false;
+    if (more) {
+      next_starts = starts;
+      ++issued;
+      MOE_SADVANCE();
+    } else {
+      next_starts = false;
+    }
+    ++q;
+    cur = cur == NST - 1 ? 0 : cur + 1;
+
+    if (++ck == Cd.KT) {
+      // ---- epilogue of tile ct: scales from its parameter slot
+      const float* pslot = prm + cslot * PRM;
+      const float4 lsr = lds_read_4x1f(pslot + rbase + (lane & 15));
+      float4 cs[JN];
+      if (KBLOCKS) {
+#pragma unroll
+        for (int j = 0; j < JN; ++j) cs[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+      } else {
+        lds_read_4x16f(pslot + 256 + cbase + 4 * (lane >> 4), cs);
+      }
+      convert_tile<C, OUT_BF16>(acc, lsr, cs, po);
+      p_rsrc = tile_rsrc(static_cast<uint8_t*>(out) + (BATCH ? static_cast<int64_t>(Cd.g) * M * row_bytes : 0) +
+                             Cd.row0 * row_bytes,
+                         static_cast<uint32_t>(Cd.rows_here * row_bytes));
+      p_voff = static_cast<uint32_t>((rbase + (lane & 15)) * row_bytes + (Cd.col0 + cbase) * ESZ + 16 * (lane >> 4));
+      if (!PEND) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+        st_now = true;
+      }
+      have_pend = PEND;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      ck = 0;
+      cslot = cslot == PRM_SLOTS - 1 ? 0 : cslot + 1;
+      ct += tstep;
+      while (ct < last) {
+        Cd = decode_tile<C, BATCH>(gt, El, MTb, NT, KT, ct);
+        if (Cd.KT > 0) break;
+        if (PEND && have_pend) {
+#pragma unroll
+          for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+          have_pend = false;
+        }
+        MOE_ZERO_TILE(Cd);
+        ct += tstep;
+      }
+      gn = Cd.wide ? 2 * BN / WN : BN / WN;
+      rbase = (wave / gn) * WM;
+      cbase = (wave % gn) * WN;
+      fa = frag_off(rbase, lane);
+      fb = frag_off(cbase, lane);
+    }
+    st_tail2 = st_prev;
+    st_prev = st_now;
+  }
+  if (PEND && have_pend) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+  }
+#undef MOE_SSLOT
+#undef MOE_SPLAN
+#undef MOE_SEXTRA
+#undef MOE_SADVANCE
+#undef MOE_ZERO_TILE
+  // rows [n, M) are zero
+  const int64_t zero_rows = BATCH ? 0 : M - n_rows;
+  if (zero_rows > 0) {
+    const int64_t total_chunks = zero_rows * row_bytes / 16;
+    uint4* base = reinterpret_cast<uint4*>(static_cast<uint8_t*>(out) + n_rows * row_bytes);
+    for (int64_t c = static_cast<int64_t>(blockIdx.x) * C::THREADS + tid; c < total_chunks;
+         c += static_cast<int64_t>(gridDim.x) * C::THREADS)
+      base[c] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 // Launch one configuration: persistent grid of (workgroups per CU) x CUs.
 template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16>
 hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs, int Kb,
@@ -539,6 +1081,14 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
   int64_t grid = static_cast<int64_t>(per_cu) * tile::num_cus();
   if (ub < grid) grid = ub;
   if (grid < 8) grid = 8;
+  if constexpr (MOE_GMM_STREAM != 0) {
+    if (El <= kStreamMaxLocal) {
+      gmm_stream_kernel<C, TRANS, KBLOCKS, OUT_BF16, false, MOE_GMM_STREAM == 2>
+          <<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N,
+                                                              out, err, 0);
+      return hipGetLastError();
+    }
+  }
   gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
       lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err);
   return hipGetLastError();
@@ -572,12 +1122,22 @@ hipError_t gmm_batched_launch(const uint8_t* A, const float* ls, int ls_len, con
   if (grid < 8) grid = 8;          // the XCD split gives each of the 8 parts its own workgroups
   const int per_row = ls_len == M ? 1 : 0;
   const int Nb = rs_len == 1 ? 1 : static_cast<int>(N);
-  if (bf16)
-    gmm_kernel<C, true, false, true, true><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
-        A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
-  else
-    gmm_kernel<C, true, false, false, true><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
-        A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
+  const unsigned gx = static_cast<unsigned>(grid);
+  constexpr bool PEND = MOE_GMM_STREAM_BATCH == 2;
+  if (MOE_GMM_STREAM_BATCH != 0 && El <= kStreamMaxLocal) {
+    if (bf16)
+      gmm_stream_kernel<C, true, false, true, true, PEND><<<gx, C::THREADS, 0, st>>>(
+          A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
+    else
+      gmm_stream_kernel<C, true, false, false, true, PEND><<<gx, C::THREADS, 0, st>>>(
+          A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
+  } else if (bf16) {
+    gmm_kernel<C, true, false, true, true><<<gx, C::THREADS, 0, st>>>(A, ls, per_row, B, rs, 1, Nb, group_sizes, g0,
+                                                                       El, M, K, N, out, err, max_rows);
+  } else {
+    gmm_kernel<C, true, false, false, true><<<gx, C::THREADS, 0, st>>>(A, ls, per_row, B, rs, 1, Nb, group_sizes, g0,
+                                                                        El, M, K, N, out, err, max_rows);
+  }
   return hipGetLastError();
 }
 

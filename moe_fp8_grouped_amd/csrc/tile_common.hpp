@@ -51,11 +51,14 @@ __device__ __forceinline__ v8i frag_tr(const uint8_t* lds, int col0, int lane) {
   return r;
 }
 
-// Local group table, computed by every workgroup from group_sizes.
-struct GroupTable {
-  int rows_off[kMaxLocal + 1];   // first compact row of each local group
-  int tiles_off[kMaxLocal + 1];  // first tile of each local group
+// Local group table of up to NMAX groups, computed by every workgroup from
+// group_sizes.
+template <int NMAX>
+struct GroupTableN {
+  int rows_off[NMAX + 1];   // first compact row of each local group
+  int tiles_off[NMAX + 1];  // first tile of each local group
 };
+typedef GroupTableN<kMaxLocal> GroupTable;
 
 // Exclusive scan of v[0..n) into out[0..n] (out[n] = total) by wave 0.
 __device__ void wave0_scan(const int* v, int* out, int n) {
@@ -92,8 +95,9 @@ __device__ __forceinline__ int group_tiles(int m, int bm, int nt, bool wide_tail
 // the error word) so that every tile stays inside the buffers; a group of m
 // rows owns group_tiles(m, bm, tiles_per_mrow, wide_tail) tiles
 // (tiles_per_mrow = 0: one entry per group).
+template <class GT>
 __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, int El, int64_t max_rows,
-                             int tiles_per_mrow, int bm, int32_t* err, GroupTable& gt, int* tmp,
+                             int tiles_per_mrow, int bm, int32_t* err, GT& gt, int* tmp,
                              bool wide_tail = false) {
   for (int g = threadIdx.x; g < El; g += blockDim.x) {
     int m = group_sizes[g0 + g];
@@ -128,7 +132,8 @@ __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, in
   __syncthreads();
 }
 
-__device__ __forceinline__ int find_group(const GroupTable& gt, int El, int t) {
+template <class GT>
+__device__ __forceinline__ int find_group(const GT& gt, int El, int t) {
   int lo = 0, hi = El - 1;             // last g with tiles_off[g] <= t
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
