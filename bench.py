@@ -75,8 +75,9 @@ def step_accounting(path, n, U):
     acc["sort"] = {"bytes": T * k * 4 + 2 * T * k * 4 + E * 4 + U * H + n * H + 8 * n, "flops": 0}
     gm = []
     nonempty = int(path.nonempty_local)
-    for name in (["wi_0", "wi_1", "wo"] if cfg.pipeline == "ffn" else ["w_up"]):
-        w = path.w[name]
+    # the gated FFN's two input projections run as one launch over [W0 | W1]
+    launches = [("wi_01", path.w01), ("wo", path.w["wo"])] if cfg.pipeline == "ffn" else [("w_up", path.w["w_up"])]
+    for name, w in launches:
         K, N = w.K, w.N
         by = n * K + nonempty * K * N + n * N * 2 + (M_cap - n) * N * 2 + n * 4 + nonempty * w.kb * w.nb * 4
         gm.append({"name": name, "bytes": by, "flops": 2 * n * K * N})
@@ -129,11 +130,8 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
         if cfg.pipeline == "up":
             timed("gmm_w_up", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["w_up"], path.y), record)
         else:
-            timed("gmm_wi_0", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_0"], path.a), record)
-            timed("gmm_wi_1", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_1"], path.b), record)
-            timed("silu_quant", lambda: m.moe_quantize_rows(path.a, path.b, m.MOE_ACT_SILU_MUL, path.m_cap, cfg.I,
-                                                            m.MOE_SCALE_ROW_DYNAMIC, 0.0, path.hq, path.hs, None, None),
-                  record)
+            timed("gmm_wi_01", lambda: path.gmm_gate_up(ls), record)
+            timed("silu_quant", path.silu_quant, record)
             timed("gmm_wo", lambda: path.gmm(path.hq, path.hs, m.MOE_SCALE_ROW_DYNAMIC, path.w["wo"], path.y), record)
         timed("gather_reduce", path.combine, record)
 
@@ -277,10 +275,8 @@ def secondary_ep_slice(steps, warmup):
     acc = step_accounting(path, n, U)
     ls = path.ss
     calls = [("quantize", path.quantize), ("sort", path.sort),
-             ("gmm_wi_0", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_0"], path.a)),
-             ("gmm_wi_1", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["wi_1"], path.b)),
-             ("silu_quant", lambda: m.moe_quantize_rows(path.a, path.b, m.MOE_ACT_SILU_MUL, path.m_cap, cfg.I,
-                                                        m.MOE_SCALE_ROW_DYNAMIC, 0.0, path.hq, path.hs, None, None)),
+             ("gmm_wi_01", lambda: path.gmm_gate_up(ls)),
+             ("silu_quant", path.silu_quant),
              ("gmm_wo", lambda: path.gmm(path.hq, path.hs, m.MOE_SCALE_ROW_DYNAMIC, path.w["wo"], path.y)),
              ("gather_reduce", path.combine)]
     t, ms_eager = _time_calls(calls, steps, warmup)

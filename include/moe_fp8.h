@@ -113,6 +113,21 @@ int moe_quantize_rows(const void* x, const void* x_up, int act, int64_t R, int64
                       float* row_amax, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_quantize_rows_strided -- moe_quantize_rows over inputs whose rows are
+ * ldx elements apart (the same step, "Support quantization for tokamax gmm
+ * v2" absmax scheme; for the gated FFN, the requantization of silu(a) * b
+ * where a and b are the two column halves of one grouped-matmul output).
+ *   ldx      row stride of x and x_up in elements; ldx >= C, a multiple of 8,
+ *            and x, x_up 16-byte aligned (MOE_ERR_SHAPE otherwise).  q stays
+ *            [R, C] contiguous.  Every other argument, the result and the
+ *            errors are those of moe_quantize_rows, which is this call with
+ *            ldx = C.
+ */
+int moe_quantize_rows_strided(const void* x, const void* x_up, int64_t ldx, int act, int64_t R, int64_t C,
+                              int scale_mode, float static_scale, uint8_t* q, float* scale,
+                              float* row_amax, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_quantize_weights -- offline blockwise absmax quantization of expert
  * weights, the pre-quantization of "Keep qwix out of tpu-inference's fused
  * MoE kernel and pre-quantize weights" ("Changes in this PR": float8_e4m3fn

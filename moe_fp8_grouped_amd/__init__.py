@@ -31,6 +31,7 @@ MOE_DEVERR_EXPERT_ID, MOE_DEVERR_GROUP_SIZE, MOE_DEVERR_ROWS = 1, 2, 4
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "moe_quantize_rows": (_I, [_P, _P, _I, _I64, _I64, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "moe_quantize_rows_strided": (_I, [_P, _P, _I64, _I, _I64, _I64, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_weights": (_I, [_P, _I64, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _I, _F, _I, _P, _P, _P]),
     "moe_sort_by_expert": (_I, [_P, _I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                 _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -126,6 +127,23 @@ def _nbytes(t):
 def moe_quantize_rows(x, x_up, act, R, C, scale_mode, static_scale, q, scale, row_amax=None, ws=None, stream=None):
     return _call("moe_quantize_rows", _ptr(x), _ptr(x_up), act, R, C, scale_mode, float(static_scale), _ptr(q),
                  _ptr(scale), _ptr(row_amax), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def _ptr_rows(t, ld):
+    """Device pointer of a 2-D view whose rows are ``ld`` elements apart (unit inner stride)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("tensor arguments must be torch tensors in GPU memory")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1) or (t.shape[0] > 1 and t.stride(0) != ld):
+        raise ValueError("expected a 2-D view with rows %d elements apart" % ld)
+    return t.data_ptr()
+
+
+def moe_quantize_rows_strided(x, x_up, ldx, act, R, C, scale_mode, static_scale, q, scale, row_amax=None, ws=None,
+                              stream=None):
+    return _call("moe_quantize_rows_strided", _ptr_rows(x, ldx), _ptr_rows(x_up, ldx), ldx, act, R, C, scale_mode,
+                 float(static_scale), _ptr(q), _ptr(scale), _ptr(row_amax), _ptr(ws), _nbytes(ws), _stream(stream))
 
 
 def moe_quantize_weights(w, E, K, N, kb, nb, scale_mode, static_scale, transpose_out, q, scale, stream=None):

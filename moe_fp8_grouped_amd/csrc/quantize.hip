@@ -98,14 +98,14 @@ __device__ __forceinline__ float row_max(float v) {
 
 template <int CPL, int ACT, int MODE, int LPR = 64>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu, int64_t R, int64_t C,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu, int64_t R, int64_t C, int64_t ldx,
     const float* __restrict__ given_scale, uint8_t* __restrict__ q, float* __restrict__ scale,
     float* __restrict__ row_amax) {
   const int lane = threadIdx.x % LPR;
   const int64_t row = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * (64 / LPR) + (threadIdx.x & 63) / LPR;
   if (row >= R) return;     // (a half-wave's partner rows never read this half's lanes)
   const int64_t nchunks = C >> 3;
-  const int64_t base = row * C;
+  const int64_t base = row * C, xbase = row * ldx;
   float amax = 0.0f;
   if constexpr (CPL > 0) {
     float v[CPL][8];
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     for (int c = 0; c < CPL; ++c) {
       const int64_t ch = lane + LPR * c;
       if (ch < nchunks) {
-        load_vals<ACT>(x, xu, base + ch * 8, v[c]);
+        load_vals<ACT>(x, xu, xbase + ch * 8, v[c]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
       }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   } else {
     for (int64_t ch = lane; ch < nchunks; ch += 64) {
       float v[8];
-      load_vals<ACT>(x, xu, base + ch * 8, v);
+      load_vals<ACT>(x, xu, xbase + ch * 8, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     }
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
     const RowDiv div(s);
     for (int64_t ch = lane; ch < nchunks; ch += 64) {
       float v[8];
-      load_vals<ACT>(x, xu, base + ch * 8, v);
+      load_vals<ACT>(x, xu, xbase + ch * 8, v);
       store_codes(q, base + ch * 8, v, div);
     }
     if (lane == 0) {
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
 template <int ACT>
 __global__ __launch_bounds__(256) void tensor_amax_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ xu, int64_t R,
-                                                          int64_t C, float* __restrict__ partial,
+                                                          int64_t C, int64_t ldx, float* __restrict__ partial,
                                                           float* __restrict__ row_amax) {
   __shared__ float red[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const uint16_t* __rest
     float amax = 0.0f;
     for (int64_t ch = lane; ch < nchunks; ch += 64) {
       float v[8];
-      load_vals<ACT>(x, xu, row * C + ch * 8, v);
+      load_vals<ACT>(x, xu, row * ldx + ch * 8, v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
     }
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restri
 __global__ void fill_scale_kernel(float* scale, float v) { *scale = v; }
 
 template <int ACT, int MODE>
-hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, const float* given,
+hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, int64_t ldx, const float* given,
                        uint8_t* q, float* scale, float* row_amax, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(moe_cdiv(R, 4))), block(256);
   const int64_t chunks_per_lane = moe_cdiv(C / 8, 64);
@@ -205,47 +205,47 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t
   if (nch % 64 == 32 && nch <= 32 * 5) {
     const dim3 grid2(static_cast<unsigned>(moe_cdiv(R, 8)));
     if (nch == 32)
-      quantize_rows_kernel<1, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+      quantize_rows_kernel<1, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
     else if (nch == 96)
-      quantize_rows_kernel<3, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+      quantize_rows_kernel<3, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
     else
-      quantize_rows_kernel<5, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+      quantize_rows_kernel<5, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
     return hipGetLastError();
   }
   // Keep the row in registers when it fits (the SiLU variant holds float32).
   const int max_cpl = (ACT == MOE_ACT_SILU_MUL) ? 8 : 16;
   if (chunks_per_lane <= 1)
-    quantize_rows_kernel<1, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    quantize_rows_kernel<1, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
   else if (chunks_per_lane <= 2)
-    quantize_rows_kernel<2, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    quantize_rows_kernel<2, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
   else if (chunks_per_lane <= 4)
-    quantize_rows_kernel<4, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    quantize_rows_kernel<4, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
   else if (chunks_per_lane <= 8)
-    quantize_rows_kernel<8, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    quantize_rows_kernel<8, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
   else if (chunks_per_lane <= max_cpl)
     quantize_rows_kernel<(ACT == MOE_ACT_SILU_MUL ? 8 : 16), ACT, MODE>
-        <<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+        <<<grid, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
   else
-    quantize_rows_kernel<0, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, given, q, scale, row_amax);
+    quantize_rows_kernel<0, ACT, MODE><<<grid, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
   return hipGetLastError();
 }
 
 constexpr int kTensorBlocks = 1024;
 
 template <int ACT>
-int quantize_rows_impl(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, int mode,
+int quantize_rows_impl(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, int64_t ldx, int mode,
                        float static_scale, uint8_t* q, float* scale, float* row_amax, void* ws,
                        hipStream_t st) {
   if (mode == MOE_SCALE_ROW_DYNAMIC) {
     if (R == 0) return MOE_OK;
-    return launch_rows<ACT, MODE_ROW>(x, xu, R, C, nullptr, q, scale, row_amax, st) == hipSuccess
+    return launch_rows<ACT, MODE_ROW>(x, xu, R, C, ldx, nullptr, q, scale, row_amax, st) == hipSuccess
                ? MOE_OK : MOE_ERR_HIP;
   }
   if (mode == MOE_SCALE_TENSOR_STATIC) {
     fill_scale_kernel<<<1, 1, 0, st>>>(scale, static_scale);
     MOE_CHECK_LAUNCH();
     if (R == 0) return MOE_OK;
-    return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, scale, q, scale, row_amax, st) == hipSuccess
+    return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, ldx, scale, q, scale, row_amax, st) == hipSuccess
                ? MOE_OK : MOE_ERR_HIP;
   }
   // tensor dynamic: partial maxima in the workspace after the error word
@@ -256,11 +256,11 @@ int quantize_rows_impl(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t
     MOE_CHECK_LAUNCH();
     return MOE_OK;
   }
-  tensor_amax_kernel<ACT><<<nblk, 256, 0, st>>>(x, xu, R, C, partial, row_amax);
+  tensor_amax_kernel<ACT><<<nblk, 256, 0, st>>>(x, xu, R, C, ldx, partial, row_amax);
   MOE_CHECK_LAUNCH();
   tensor_scale_kernel<<<1, 256, 0, st>>>(partial, nblk, scale);
   MOE_CHECK_LAUNCH();
-  return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, scale, q, scale, nullptr, st) == hipSuccess
+  return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, ldx, scale, q, scale, nullptr, st) == hipSuccess
              ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -273,10 +273,11 @@ size_t quantize_rows_ws_bytes(int64_t R, int64_t C, int mode) {
 
 }  // namespace moe
 
-extern "C" int moe_quantize_rows(const void* x, const void* x_up, int act, int64_t R, int64_t C,
-                                 int scale_mode, float static_scale, uint8_t* q, float* scale,
-                                 float* row_amax, void* ws, size_t ws_bytes, void* stream) {
+extern "C" int moe_quantize_rows_strided(const void* x, const void* x_up, int64_t ldx, int act, int64_t R,
+                                         int64_t C, int scale_mode, float static_scale, uint8_t* q, float* scale,
+                                         float* row_amax, void* ws, size_t ws_bytes, void* stream) {
   if (R < 0 || C <= 0 || C % 16 != 0) return MOE_ERR_SHAPE;
+  if (ldx < C || ldx % 8 != 0) return MOE_ERR_SHAPE;
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_UNSUPPORTED;
   if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
       scale_mode != MOE_SCALE_TENSOR_STATIC)
@@ -290,12 +291,21 @@ extern "C" int moe_quantize_rows(const void* x, const void* x_up, int act, int64
     if (!ws) return MOE_ERR_WORKSPACE;
     if (ws_bytes < moe::quantize_rows_ws_bytes(R, C, scale_mode)) return MOE_ERR_WORKSPACE;
   }
+  // 16-byte loads: every row start must stay 16-byte aligned
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(x_up)) % 16 != 0) return MOE_ERR_SHAPE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* ub = static_cast<const uint16_t*>(x_up);
   if (act == MOE_ACT_SILU_MUL)
-    return moe::quantize_rows_impl<MOE_ACT_SILU_MUL>(xb, ub, R, C, scale_mode, static_scale, q, scale,
+    return moe::quantize_rows_impl<MOE_ACT_SILU_MUL>(xb, ub, R, C, ldx, scale_mode, static_scale, q, scale,
                                                      row_amax, ws, st);
-  return moe::quantize_rows_impl<MOE_ACT_NONE>(xb, nullptr, R, C, scale_mode, static_scale, q, scale,
+  return moe::quantize_rows_impl<MOE_ACT_NONE>(xb, nullptr, R, C, ldx, scale_mode, static_scale, q, scale,
                                                row_amax, ws, st);
+}
+
+extern "C" int moe_quantize_rows(const void* x, const void* x_up, int act, int64_t R, int64_t C,
+                                 int scale_mode, float static_scale, uint8_t* q, float* scale,
+                                 float* row_amax, void* ws, size_t ws_bytes, void* stream) {
+  return moe_quantize_rows_strided(x, x_up, C, act, R, C, scale_mode, static_scale, q, scale, row_amax, ws,
+                                   ws_bytes, stream);
 }

@@ -22,7 +22,7 @@ import torch
 
 from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_F32, MOE_OP_GMM, MOE_OP_QUANTIZE_ROWS,
                MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
-               MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gmm_fp8, moe_quantize_rows,
+               MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gmm_fp8, moe_quantize_rows, moe_quantize_rows_strided,
                moe_quantize_weights, moe_sort_by_expert, moe_tgmm_fp8, workspace)
 
 
@@ -44,6 +44,18 @@ class QuantizedWeight:
         mode = MOE_SCALE_TENSOR_STATIC if static_scale is not None else MOE_SCALE_ROW_DYNAMIC
         moe_quantize_weights(w_bf16, E, K, N, kb, nb, mode, static_scale or 0.0, 1 if nk else 0, self.q,
                              self.scale, stream=stream)
+
+
+def concat_columns(w0: QuantizedWeight, w1: QuantizedWeight) -> QuantizedWeight:
+    """The two input projections of the gated FFN as one weight of 2N output
+    columns ([w0 | w1] along N, scales likewise): one grouped matmul then
+    produces a and b side by side, reading each lhs tile once."""
+    assert (w0.E, w0.K, w0.N, w0.kb, w0.nb, w0.nk) == (w1.E, w1.K, w1.N, w1.kb, w1.nb, w1.nk)
+    w = QuantizedWeight.__new__(QuantizedWeight)
+    w.E, w.K, w.N, w.kb, w.nb, w.nk = w0.E, w0.K, 2 * w0.N, w0.kb, 2 * w0.nb, w0.nk
+    w.q = torch.cat([w0.q, w1.q], dim=1 if w0.nk else 2).contiguous()
+    w.scale = torch.cat([w0.scale, w1.scale], dim=3).contiguous()
+    return w
 
 
 class ForwardPath:
@@ -82,8 +94,10 @@ class ForwardPath:
         self.xs = torch.empty((self.m_cap, H), dtype=u8, device=device)
         self.ss = torch.empty((self.m_cap,), dtype=f32, device=device)
         if cfg.pipeline == "ffn":
-            self.a = torch.empty((self.m_cap, cfg.I), dtype=bf, device=device)
-            self.b = torch.empty((self.m_cap, cfg.I), dtype=bf, device=device)
+            # a and b are the column halves of one [m_cap, 2I] output
+            self.w01 = concat_columns(self.w["wi_0"], self.w["wi_1"])
+            self.ab = torch.empty((self.m_cap, 2 * cfg.I), dtype=bf, device=device)
+            self.a, self.b = self.ab[:, :cfg.I], self.ab[:, cfg.I:]
             self.hq = torch.empty((self.m_cap, cfg.I), dtype=u8, device=device)
             self.hs = torch.empty((self.m_cap,), dtype=f32, device=device)
         self.y = torch.empty((self.m_cap, N_out), dtype=bf, device=device)
@@ -120,11 +134,18 @@ class ForwardPath:
         if self.cfg.pipeline == "up":
             self.gmm(self.xs, ls, self.act_mode, self.w["w_up"], self.y)
             return
-        self.gmm(self.xs, ls, self.act_mode, self.w["wi_0"], self.a)
-        self.gmm(self.xs, ls, self.act_mode, self.w["wi_1"], self.b)
-        moe_quantize_rows(self.a, self.b, MOE_ACT_SILU_MUL, self.m_cap, self.cfg.I, MOE_SCALE_ROW_DYNAMIC, 0.0,
-                          self.hq, self.hs, None, None)
+        self.gmm_gate_up(ls)
+        self.silu_quant()
         self.gmm(self.hq, self.hs, MOE_SCALE_ROW_DYNAMIC, self.w["wo"], self.y)
+
+    def gmm_gate_up(self, ls):
+        """a = x W0 and b = x W1 for every routed row, as one grouped matmul."""
+        self.gmm(self.xs, ls, self.act_mode, self.w01, self.ab)
+
+    def silu_quant(self):
+        I = self.cfg.I
+        moe_quantize_rows_strided(self.a, self.b, 2 * I, MOE_ACT_SILU_MUL, self.m_cap, I, MOE_SCALE_ROW_DYNAMIC,
+                                  0.0, self.hq, self.hs, None, None)
 
     def combine(self):
         moe_gather_reduce(self.y, MOE_BF16, self.inv_pos, self.topk_w, self.T, self.k, self.N_out, MOE_BF16,

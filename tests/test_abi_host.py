@@ -34,7 +34,7 @@ def lib():
 
 def test_header_declares_the_path_calls():
     names = _declared_functions()
-    for fn in ["moe_quantize_rows", "moe_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
+    for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
                "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
                "moe_version"]:
         assert fn in names
@@ -86,6 +86,17 @@ def test_quantize_rows_validation(lib):
     assert f(one, one, 0, 4, 32, 0, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_UNSUPPORTED # up w/o silu
     assert f(one, None, 0, 4, 32, 1, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_WORKSPACE
     assert f(one, None, 0, 4, 32, 1, 0.0, one, one, None, one, 16, None) == m.MOE_ERR_WORKSPACE
+
+
+def test_quantize_rows_strided_validation(lib):
+    f = lambda *a: _c(lib, "moe_quantize_rows_strided", *a)
+    al = 4096   # 16-byte aligned dummy pointer: never dereferenced on these paths
+    assert f(al, None, 16, 0, 4, 32, 0, 0.0, al, al, None, None, 0, None) == m.MOE_ERR_SHAPE    # ldx < C
+    assert f(al, None, 36, 0, 4, 32, 0, 0.0, al, al, None, None, 0, None) == m.MOE_ERR_SHAPE    # ldx % 8
+    assert f(al + 8, None, 64, 0, 4, 32, 0, 0.0, al, al, None, None, 0, None) == m.MOE_ERR_SHAPE  # x misaligned
+    assert f(al, al + 2, 64, 1, 4, 32, 0, 0.0, al, al, None, None, 0, None) == m.MOE_ERR_SHAPE  # x_up misaligned
+    assert f(al, None, 64, 1, 4, 32, 0, 0.0, al, al, None, None, 0, None) == m.MOE_ERR_NULL     # silu w/o up
+    assert f(al, None, 64, 0, 4, 24, 0, 0.0, al, al, None, None, 0, None) == m.MOE_ERR_SHAPE    # C % 16
 
 
 def test_sort_validation(lib):

@@ -94,6 +94,33 @@ def test_silu_mul_requantize_bit_exact(R, C):
     assert_bits_equal(s, so, "silu scale")
 
 
+@pytest.mark.parametrize("R,C,act,mode", [(37, 768, 1, 0), (4, 256, 1, 0), (9, 2048, 1, 0), (5, 256, 0, 0),
+                                          (300, 512, 0, 1), (70, 96 * 8, 0, 2)])
+def test_quantize_rows_strided_bit_exact(R, C, act, mode):
+    """Rows read 2C elements apart out of one [R, 2C] buffer (a | b, the
+    gated FFN's fused input-projection output): the same bits as the
+    oracle on the two halves."""
+    rng = np.random.default_rng(R + 3 * C + act)
+    ab = _bits(rng, (R, 2 * C), 4.0)
+    ab[0, :4] = to_bf16_bits(np.array([100.0, -100.0, 0.0, -0.0], np.float32))
+    a_bits, b_bits = np.ascontiguousarray(ab[:, :C]), np.ascontiguousarray(ab[:, C:])
+    d = dev_bf16(ab)
+    x, up = d[:, :C], (d[:, C:] if act else None)
+    static = STATIC_ACT_SCALE if mode == m.MOE_SCALE_TENSOR_STATIC else 0.0
+    q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((R if mode == m.MOE_SCALE_ROW_DYNAMIC else 1,), dtype=torch.float32, device="cuda")
+    amax = torch.empty((R,), dtype=torch.float32, device="cuda")
+    ws = m.workspace(m.MOE_OP_QUANTIZE_ROWS, R, C, mode)
+    print(f"quantize strided R={R} C={C} ld={2 * C} act={act} mode={mode}", flush=True)
+    m.moe_quantize_rows_strided(x, up, 2 * C, act, R, C, mode, static, q, sc, amax, ws)
+    torch.cuda.synchronize()
+    qo, so, ao = quantize_rows(a_bits, mode, static_scale=static if static else None,
+                               x_up_bits=b_bits if act else None)
+    assert_bits_equal(host(q), qo, "strided q")
+    assert_bits_equal(host(sc), so, "strided scale")
+    assert_bits_equal(host(amax), ao, "strided row_amax")
+
+
 def test_empty_rows_tensor_dynamic():
     ws = m.workspace(m.MOE_OP_QUANTIZE_ROWS, 0, 32, m.MOE_SCALE_TENSOR_DYNAMIC)
     s = torch.zeros(1, dtype=torch.float32, device="cuda")
