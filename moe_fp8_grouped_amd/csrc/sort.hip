@@ -58,6 +58,25 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e <= E; e += 256) out[e] = hist[e];
 }
 
+// Copy n ints from global memory to LDS with `nthreads` threads: each thread
+// issues eight independent loads before their LDS stores, so a table of many
+// cells per thread costs a few memory latencies instead of one per cell.
+__device__ __forceinline__ void copy_to_lds(const int32_t* __restrict__ src, int* dst, int n, int nthreads) {
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * nthreads) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nthreads;
+      v[u] = i < n ? src[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * nthreads;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
 // Exclusive prefix sum of a[0..n) in LDS by the first wave (n <= 1025).
 __device__ void wave0_exclusive_scan(int* a, int n) {
   if (threadIdx.x >= 64) return;
@@ -88,7 +107,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
   const int64_t cells = static_cast<int64_t>(ntiles) * (E + 1);
   int32_t* col = in_lds ? tab : tile_hist;
   if (in_lds) {
-    for (int64_t i = threadIdx.x; i < cells; i += blockDim.x) tab[i] = tile_hist[i];
+    copy_to_lds(tile_hist, tab, static_cast<int>(cells), blockDim.x);
     __syncthreads();
   }
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
@@ -140,7 +159,7 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
     int* tab = lds + 5 * (E + 1);      // [ntiles][E + 1] counts
     int* tot = tab + ntiles * (E + 1); // [E + 1] totals, then their exclusive scan
     const int cells = ntiles * (E + 1);
-    for (int i = threadIdx.x; i < cells; i += 256) tab[i] = tile_off[i];
+    copy_to_lds(tile_off, tab, cells, 256);
     __syncthreads();
     for (int e = threadIdx.x; e <= E; e += 256) {
       int before = 0, all = 0;
