@@ -39,7 +39,7 @@ PEAK_HBM_GBPS = 8000.0        # HBM3E
 # sources of the dominant kernel; a counter summary applies only to the build it was taken on
 GMM_SOURCES = ("moe_fp8_grouped_amd/csrc/gmm.hip", "moe_fp8_grouped_amd/csrc/tile_common.hpp",
                "moe_fp8_grouped_amd/csrc/common.hpp")
-GMM_COUNTERS = "profiles/gmm_kernel__gated-ffn-fwd__hbm_counters.md"
+GMM_COUNTERS = "profiles/moe_gmm_fp8__gated-ffn-fwd__hbm_counters.md"
 
 
 def gmm_source_hash():
@@ -188,7 +188,7 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
     achieved_gbps = gmm_bytes / (gmm_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved_gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(),
-            "kernel": "moe_gmm_fp8 (gmm_kernel)",
+            "kernel": "moe_gmm_fp8 (gmm256_kernel: the gated FFN's launches have N >= 1536)",
             "launches_per_step": len(gmm_names),
             "avg_launch_us": round(gmm_us / len(gmm_names), 2),
             "alg_bytes_per_launch": int(gmm_bytes / len(gmm_names)),
