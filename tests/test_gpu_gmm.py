@@ -167,6 +167,47 @@ def test_gmm_ragged_groups_and_zero_tail(sizes):
     _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, 0, E, 0, f"ragged kn {sizes}")
 
 
+@pytest.mark.parametrize("sizes,N,nb,static", [
+    ([0, 5, 0, 130, 1, 0, 257, 300, 128, 129, 256, 384, 513], 1536, "channel", False),
+    ([2, 0, 700, 64, 255], 2048, "coarse", False),
+    ([1, 1, 1, 1], 1536, "tensor", True),
+])
+def test_gmm_256_tiles_ragged(sizes, N, nb, static):
+    """The 256 x 256-tile kernel (weights [E, N, K], N >= 1536, bf16 out):
+    empty groups, one-row groups, remainders of at most 128 rows (half
+    tiles) and of more (a full tile with rows not stored), tiles reaching
+    past the buffer, and the zero rows after the last group -- against the
+    oracle over the whole output (its float32 twin runs the 256 x 128 kernel)."""
+    rng = np.random.default_rng(sum(sizes) + N)
+    E = len(sizes)
+    gs = np.array(sizes, np.int32)
+    n = int(gs.sum())
+    M = n + 37
+    K = 384
+    lhs = rng.integers(0, 0x70, (M, K)).astype(np.uint8)
+    w = rng.integers(0, 0x70, (E, K, N)).astype(np.uint8)
+    nbv = {"channel": N, "coarse": N // 128, "tensor": 1}[nb]
+    rs = rng.uniform(0.001, 0.1, (E, 1, 1, nbv)).astype(np.float32)
+    if static:
+        ls, mode = np.array([0.25], np.float32), m.MOE_SCALE_TENSOR_STATIC
+    else:
+        ls, mode = rng.uniform(0.01, 1, M).astype(np.float32), m.MOE_SCALE_ROW_DYNAMIC
+    _check_gmm_full(lhs, ls, mode, w, rs, gs, E, 0, E, 1, f"256 tiles {sizes} N={N} {nb}")
+
+
+def test_gmm_256_tiles_local_slice():
+    rng = np.random.default_rng(21)
+    E, g0, El = 10, 3, 4
+    gs = rng.integers(0, 300, E).astype(np.int32)
+    n = int(gs[g0:g0 + El].sum())
+    K, N = 256, 1536
+    lhs = rng.integers(0, 0x70, (n + 10, K)).astype(np.uint8)
+    w = rng.integers(0, 0x70, (El, K, N)).astype(np.uint8)
+    rs = rng.uniform(0.01, 0.1, (El, 1, 1, N)).astype(np.float32)
+    ls = rng.uniform(0.01, 1, n + 10).astype(np.float32)
+    _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, g0, El, 1, "256 tiles local slice")
+
+
 def test_gmm_local_slice_and_no_local_experts():
     rng = np.random.default_rng(11)
     E, g0, El = 10, 3, 4
