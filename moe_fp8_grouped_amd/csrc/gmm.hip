@@ -66,11 +66,7 @@
 #ifndef MOE_GMM_CFG
 #define MOE_GMM_CFG 256, 128, 3, 8     // BM, BN, stages, waves
 #endif
-#ifndef MOE_SWZ
-#define MOE_SWZ 1                      // 0: the earlier pair-row chunk swizzle
-#endif
-// Which pipeline each entry uses (0: per-tile, 1: streaming, 2: streaming
-// with the stores deferred into the next tile's first step).  Measured: the
+// Which pipeline each entry uses (0: per-tile, 1: streaming).  Measured: the
 // per-tile kernel is faster on the grouped forward product with ragged
 // groups; the streaming kernel on the weight-gradient product, whose tiles
 // have only a few K steps each.
@@ -93,7 +89,6 @@ using namespace tile;
 constexpr int G_BK = 128;
 typedef __attribute__((address_space(3))) void lds_void;
 
-#if MOE_SWZ
 // Chunk slot swizzle of staged row r: any 8 consecutive rows from a multiple
 // of 8 use 8 distinct 16-byte slots, and rows r and r + 8 (and r and r + 32)
 // differ in slot parity, so a 16-byte read of 8 (or 16) consecutive rows per
@@ -101,10 +96,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 // bands meet distinct banks.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ (((row >> 3) ^ (row >> 5)) & 1); }
 constexpr int SWZ_FLIP = 1;      // the slot bit the per-instruction bit flips
-#else
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ (((row >> 5) & 1) << 2); }
-constexpr int SWZ_FLIP = 4;
-#endif
 
 // Per-lane pieces of the staging addresses.  A load instruction fills staged
 // rows R .. R+7 (R a multiple of 8); lane l fetches row R + l/8 into slot l%8,
@@ -119,7 +110,7 @@ struct LaneOff {
 };
 
 __device__ __forceinline__ LaneOff stage_lane_off(int lane, int64_t stride) {
-  const int sub = lane >> 3, c0 = (lane & 7) ^ (MOE_SWZ ? sub : sub >> 1);
+  const int sub = lane >> 3, c0 = (lane & 7) ^ sub;
   LaneOff o;
   o.v0 = static_cast<uint32_t>(sub * stride + 16 * c0);
   o.v1 = static_cast<uint32_t>(sub * stride + 16 * (c0 ^ SWZ_FLIP));
@@ -237,7 +228,7 @@ struct FragOff {
 
 __device__ __forceinline__ FragOff frag_off(int base, int lane) {
   const int l15 = lane & 15, grp = lane >> 4;
-  const int f = MOE_SWZ ? (l15 & 7) ^ (l15 >> 3) : l15 >> 1;
+  const int f = (l15 & 7) ^ (l15 >> 3);
   FragOff o;
   const int row = (base + l15) * G_BK;
   o.lo[0] = row + 16 * ((2 * grp) ^ f);
@@ -611,9 +602,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
 //    and lane; bfloat16 after two lane swaps per dword pair
 //    (v_permlane32_swap, then v_permlane16_swap), which turn a lane's two
 //    blocks' four-column pieces into eight consecutive columns of its row --
-//    again one 16-byte store.  With PEND the converted tile waits in
-//    registers and its stores go out during the next tile's first step,
-//    interleaved with its MFMA rounds.
+//    again one 16-byte store.
 constexpr int kStreamMaxLocal = 512;   // group table capacity (LDS budget)
 constexpr int PRM = 512;               // floats per parameter slot: 256 row scales, 256 column scales
 constexpr int PRM_SLOTS = 3;
@@ -765,7 +754,7 @@ __device__ __forceinline__ void store_rows(const OutPieces<C, OUT_BF16>& o, int 
   }
 }
 
-template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH, bool PEND>
+template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH>
 __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
     const uint8_t* __restrict__ lhs, const float* __restrict__ ls, int ls_per_row, const uint8_t* __restrict__ rhs,
     const float* __restrict__ rs, int Kb, int Nb, const int32_t* __restrict__ group_sizes, int g0, int El, int64_t M,
@@ -893,13 +882,11 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
   OutPieces<C, OUT_BF16> po;
   __amdgpu_buffer_rsrc_t p_rsrc = tile_rsrc(static_cast<uint8_t*>(out), 0);   // the converted tile's rows
   uint32_t p_voff = 0;
-  bool have_pend = false;
-  // stores issued after the loads of the steps in flight: st_prev = all
-  // stores of the previous iteration, st_tail2 = the stores that followed
-  // the last load of the iteration before it; drain = zero tiles were
-  // written (a variable count): wait for everything once
+  // stores issued after the loads of the steps in flight: st_prev = the
+  // previous iteration's epilogue stores, st_tail2 = the one before it
+  // (an epilogue's stores follow all of its iteration's loads); drain = zero
+  // tiles were written (a variable count): wait for everything once
   constexpr int ST = MI * OutPieces<C, OUT_BF16>::U;   // stores per converted tile and wave
-  constexpr int ST_TAIL = PEND ? OutPieces<C, OUT_BF16>::U : ST;
   bool st_prev = false, st_tail2 = false, drain = false;
 #define MOE_ZERO_TILE(D)                                                                                         \
   do {                                                                                                           \
@@ -943,10 +930,10 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
         case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1)); break;
         case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST)); break;
         case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST)); break;
-        case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST_TAIL)); break;
-        case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST_TAIL)); break;
-        case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST + ST_TAIL)); break;
-        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST + ST_TAIL)); break;
+        case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + ST)); break;
+        case 5: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + ST)); break;
+        case 6: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 2 * ST)); break;
+        default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS + 1 + 2 * ST)); break;
       }
     } else {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -983,7 +970,6 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
         if (i == 2) { MOE_SSLOT(3, nxt, kb_next); MOE_SSLOT(4, nxt, kb_next); }
         if (i == 3) { MOE_SSLOT(5, nxt, kb_next); }
       }
-      if (PEND && have_pend) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
 #pragma unroll
       for (int j = 0; j < JN; ++j) {
         if (KBLOCKS) {
@@ -997,10 +983,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
         }
       }
     }
-    // this iteration's stores (PEND: the pending tile's, interleaved with the
-    // rounds' loads; otherwise the epilogue's below, after all its loads)
-    bool st_now = PEND && have_pend;
-    have_pend = false;
+    bool st_now = false;    // this iteration ends a tile: its epilogue stores follow its loads
     if (more) {
       next_starts = starts;
       ++issued;
@@ -1027,12 +1010,9 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
                              Cd.row0 * row_bytes,
                          static_cast<uint32_t>(Cd.rows_here * row_bytes));
       p_voff = static_cast<uint32_t>((rbase + (lane & 15)) * row_bytes + (Cd.col0 + cbase) * ESZ + 16 * (lane >> 4));
-      if (!PEND) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
-        st_now = true;
-      }
-      have_pend = PEND;
+      for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+      st_now = true;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1043,11 +1023,6 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
       while (ct < last) {
         Cd = decode_tile<C, BATCH>(gt, El, MTb, NT, KT, ct);
         if (Cd.KT > 0) break;
-        if (PEND && have_pend) {
-#pragma unroll
-          for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
-          have_pend = false;
-        }
         MOE_ZERO_TILE(Cd);
         ct += tstep;
       }
@@ -1059,10 +1034,6 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
     }
     st_tail2 = st_prev;
     st_prev = st_now;
-  }
-  if (PEND && have_pend) {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
   }
 #undef MOE_SSLOT
 #undef MOE_SPLAN
@@ -1364,7 +1335,7 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
   }
   if constexpr (MOE_GMM_STREAM != 0) {
     if (El <= kStreamMaxLocal) {
-      gmm_stream_kernel<C, TRANS, KBLOCKS, OUT_BF16, false, MOE_GMM_STREAM == 2>
+      gmm_stream_kernel<C, TRANS, KBLOCKS, OUT_BF16, false>
           <<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N,
                                                               out, err, 0);
       return hipGetLastError();
@@ -1404,13 +1375,12 @@ hipError_t gmm_batched_launch(const uint8_t* A, const float* ls, int ls_len, con
   const int per_row = ls_len == M ? 1 : 0;
   const int Nb = rs_len == 1 ? 1 : static_cast<int>(N);
   const unsigned gx = static_cast<unsigned>(grid);
-  constexpr bool PEND = MOE_GMM_STREAM_BATCH == 2;
   if (MOE_GMM_STREAM_BATCH != 0 && El <= kStreamMaxLocal) {
     if (bf16)
-      gmm_stream_kernel<C, true, false, true, true, PEND><<<gx, C::THREADS, 0, st>>>(
+      gmm_stream_kernel<C, true, false, true, true><<<gx, C::THREADS, 0, st>>>(
           A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
     else
-      gmm_stream_kernel<C, true, false, false, true, PEND><<<gx, C::THREADS, 0, st>>>(
+      gmm_stream_kernel<C, true, false, false, true><<<gx, C::THREADS, 0, st>>>(
           A, ls, per_row, B, rs, 1, Nb, group_sizes, g0, El, M, K, N, out, err, max_rows);
   } else if (bf16) {
     gmm_kernel<C, true, false, true, true><<<gx, C::THREADS, 0, st>>>(A, ls, per_row, B, rs, 1, Nb, group_sizes, g0,
