@@ -85,12 +85,39 @@ __device__ __forceinline__ float pinned_exp(float x) {
   return ldexpf(p, static_cast<int>(n));
 }
 
-// h = f32(silu(a) * b), silu(a) = f32(a / f32(1 + e(-a))).
-__device__ __forceinline__ float silu_mul(float a, float b) {
+// The correctly rounded quotient a / d for d = 1 + e(-a) with d <= 2^126
+// (so 1/d is a normal float; a a finite bfloat16 value): a reciprocal
+// estimate, one Newton step y = y0 + y0 (1 - d y0), then Markstein's
+// correction q = q0 + y (a - d q0) with q0 = a y.  Equal to the IEEE
+// float32 quotient for every such a (checked on the device over all finite
+// bfloat16 values); a zero quotient keeps the sign of a.
+__device__ __forceinline__ float silu_quotient(float a, float d) {
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  const float y = fmaf(fmaf(-d, y0, 1.0f), y0, y0);
+  const float q0 = a * y;
+  const float q = fmaf(fmaf(-d, q0, a), y, q0);
+  return q0 == 0.0f ? q0 : q;
+}
+
+// h[i] = f32(silu(a[i]) * b[i]), silu(a) = f32(a / f32(1 + e(-a))), for eight
+// values.  One branch for the group: the reciprocal path unless some
+// denominator exceeds 2^126 (gates below about -87.3), then the IEEE divide.
+__device__ __forceinline__ void silu_mul8(const float a[8], const float b[8], float h[8]) {
 #pragma clang fp contract(off)
-  const float den = 1.0f + pinned_exp(-a);
-  const float s = a / den;
-  return s * b;
+  float den[8];
+  float dmax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    den[i] = 1.0f + pinned_exp(-a[i]);
+    dmax = fmaxf(dmax, den[i]);
+  }
+  if (dmax <= 0x1p126f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = silu_quotient(a[i], den[i]) * b[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (a[i] / den[i]) * b[i];
+  }
 }
 
 // ---------------------------------------------------------------- reductions

@@ -33,8 +33,13 @@ __device__ __forceinline__ void load_vals(const uint16_t* __restrict__ x, const 
   if constexpr (ACT == MOE_ACT_SILU_MUL) {
     Bf16x8 b;
     b.raw = *reinterpret_cast<const uint4*>(xu + off);
+    float av[8], bv[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = silu_mul(a.get(i), b.get(i));
+    for (int i = 0; i < 8; ++i) {
+      av[i] = a.get(i);
+      bv[i] = b.get(i);
+    }
+    silu_mul8(av, bv, v);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = a.get(i);
@@ -55,8 +60,7 @@ struct RowDiv {
   bool fast;
   __device__ __forceinline__ explicit RowDiv(float s_) : s(s_), y(1.0f / s_),
       fast(s_ >= 0x1p-64f && s_ <= 0x1p64f) {}
-  __device__ __forceinline__ float operator()(float x) const {
-    if (!fast) return x / s;
+  __device__ __forceinline__ float quick(float x) const {
     const float q0 = x * y;
     const float r = fmaf(-s, q0, x);
     const float q = fmaf(r, y, q0);
@@ -66,11 +70,19 @@ struct RowDiv {
 
 // Eight values to e4m3fn codes: clip to [-448, 448], then the gfx950 fp8
 // conversion (round to nearest even; on this clipped range it is the
-// encoder in common.hpp, bit for bit).
+// encoder in common.hpp, bit for bit).  The division takes one branch for
+// all eight values (a select per value would compute both quotients).
 __device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t off, const float v[8], const RowDiv& d) {
   float c[8];
+  if (d.fast) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(d(v[i]), -448.0f), 448.0f);
+    for (int i = 0; i < 8; ++i) c[i] = d.quick(v[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = v[i] / d.s;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(c[i], -448.0f), 448.0f);
   int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
   lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
   int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);

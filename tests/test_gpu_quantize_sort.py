@@ -121,6 +121,26 @@ def test_quantize_rows_strided_bit_exact(R, C, act, mode):
     assert_bits_equal(host(amax), ao, "strided row_amax")
 
 
+def test_silu_every_finite_bf16_gate_value():
+    """silu(a) for every finite bfloat16 a, observed exactly: row i holds a_i
+    and fifteen zeros with b = 1, so its row absmax is |silu(a_i)| in float32
+    and its first code is +-448 (the sign) -- bit for bit against the oracle.
+    The kernel's SiLU quotient uses a reciprocal, one Newton step and one
+    correction instead of the IEEE divide; this covers its whole input set."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    a_vals = bits[finite]
+    R, C = a_vals.size, 16
+    a = np.zeros((R, C), np.uint16)
+    a[:, 0] = a_vals
+    b = np.full((R, C), 0x3F80, np.uint16)          # 1.0
+    q, s, amax = gpu_quantize(a, m.MOE_SCALE_ROW_DYNAMIC, up_bits=b)
+    qo, so, ao = quantize_rows(a, SCALE_ROW_DYNAMIC, x_up_bits=b)
+    assert_bits_equal(amax, ao, "|silu(a)| over every finite bf16 a")
+    assert_bits_equal(s, so, "scale")
+    assert_bits_equal(q, qo, "codes")
+
+
 def test_empty_rows_tensor_dynamic():
     ws = m.workspace(m.MOE_OP_QUANTIZE_ROWS, 0, 32, m.MOE_SCALE_TENSOR_DYNAMIC)
     s = torch.zeros(1, dtype=torch.float32, device="cuda")
