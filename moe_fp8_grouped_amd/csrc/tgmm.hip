@@ -107,24 +107,44 @@ __global__ __launch_bounds__(256) void tgmm_kernel(const uint8_t* __restrict__ l
 // ------------------------------------------------------------------ transpose
 // AT[c, 128 * tiles_off[g] + i] = A[rows_off[g] + i, c] for i < m_g and 0 for
 // m_g <= i < the group's padded length (a multiple of 128): the rows of each
-// group become a contraction axis of its own, contiguous per column.  64 x 64
-// byte tiles through LDS (row stride 68 bytes: the column reads of 64 rows hit
-// 64 distinct banks); grid-strided over (padded 64-row block, 64-column block).
+// group become a contraction axis of its own, contiguous per column.  An
+// item is a 64-row block and up to four 64-column blocks: every thread
+// issues its four 16-byte loads before any LDS store (one memory latency per
+// item, not per tile), the tiles go through LDS (row stride 68 bytes), and
+// each thread reads 16 rows x 4 columns as dwords and transposes 4 x 4 byte
+// blocks in registers (v_perm_b32) into four 16-byte column stores.
+__device__ __forceinline__ void transpose4x4(const uint32_t* d, uint32_t* e) {
+  // d[i]: row i's four column bytes; e[c]: column c's four row bytes
+  const uint32_t lo01 = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);
+  const uint32_t hi01 = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);
+  const uint32_t lo23 = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+  e[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+  e[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  e[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+  e[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
 __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __restrict__ A, int64_t C,
                                                                const int32_t* __restrict__ group_sizes, int g0,
                                                                int El, int64_t max_rows, int64_t Mpad,
                                                                uint8_t* __restrict__ AT, int32_t* __restrict__ err) {
+  constexpr int TS = 64 * 68;                 // one 64 x 64 byte tile, rows padded to 68 bytes
   __shared__ GroupTable gt;
   __shared__ int tmp[kMaxLocal];
-  __shared__ __attribute__((aligned(16))) uint8_t tl[64 * 68];
+  __shared__ __attribute__((aligned(16))) uint8_t tl[4 * TS];
   build_groups(group_sizes, g0, El, max_rows, 1, 128, err, gt, tmp, false);
   const int64_t P = static_cast<int64_t>(gt.tiles_off[El]) * 128;    // padded rows
   const int64_t cblocks = C / 64;
-  const int64_t items = (P / 64) * cblocks;
+  const int64_t cq = (cblocks + 3) / 4;
+  const int64_t items = (P / 64) * cq;
   const int tid = threadIdx.x;
+  const int lr = tid >> 2, lc16 = (tid & 3) * 16;              // load: row, 16-byte column piece
+  const int tu = tid >> 6, rg = (tid >> 4) & 3, cg = tid & 15;  // transpose: tile, 16-row group, 4-column group
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t pb = it / cblocks, cb = it - pb * cblocks;
-    const int64_t p0 = pb * 64;
+    const int64_t pb = it / cq, q = it - pb * cq;
+    const int64_t p0 = pb * 64, cb0 = q * 4;
+    const int nb = static_cast<int>(cblocks - cb0 < 4 ? cblocks - cb0 : 4);
     // the group holding padded rows p0 .. p0 + 63 (padded lengths are multiples of 128)
     int lo = 0, hi = El - 1;
     while (lo < hi) {
@@ -134,27 +154,34 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
     const int g = lo;
     const int64_t i0 = p0 - static_cast<int64_t>(gt.tiles_off[g]) * 128;   // first local row of the block
     const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
+    const bool live = i0 + lr < m_g;
+    const uint8_t* src = A + (gt.rows_off[g] + i0 + lr) * C + cb0 * 64 + lc16;
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (u < nb && live) v[u] = *reinterpret_cast<const uint4*>(src + u * 64);
+    }
     __syncthreads();                          // the previous item's reads of tl are done
-    {
-      const int r = tid >> 2, c16 = (tid & 3) * 16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (i0 + r < m_g)
-        v = *reinterpret_cast<const uint4*>(A + (gt.rows_off[g] + i0 + r) * C + cb * 64 + c16);
-      uint32_t* d = reinterpret_cast<uint32_t*>(tl + r * 68 + c16);
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < nb) {
+        uint32_t* d = reinterpret_cast<uint32_t*>(tl + u * TS + lr * 68 + lc16);
+        d[0] = v[u].x; d[1] = v[u].y; d[2] = v[u].z; d[3] = v[u].w;
+      }
     }
     __syncthreads();
-    {
-      const int c = tid >> 2, r16 = (tid & 3) * 16;
-      uint32_t w[4];
+    if (tu < nb) {
+      const uint8_t* t = tl + tu * TS + (16 * rg) * 68 + 4 * cg;
+      uint32_t d[16], e[4][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[q] = static_cast<uint32_t>(tl[(r16 + 4 * q) * 68 + c]) |
-               (static_cast<uint32_t>(tl[(r16 + 4 * q + 1) * 68 + c]) << 8) |
-               (static_cast<uint32_t>(tl[(r16 + 4 * q + 2) * 68 + c]) << 16) |
-               (static_cast<uint32_t>(tl[(r16 + 4 * q + 3) * 68 + c]) << 24);
-      }
-      *reinterpret_cast<uint4*>(AT + (cb * 64 + c) * Mpad + p0 + r16) = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int j = 0; j < 16; ++j) d[j] = *reinterpret_cast<const uint32_t*>(t + j * 68);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) transpose4x4(d + 4 * b, e[b]);
+      uint8_t* dst = AT + ((cb0 + tu) * 64 + 4 * cg) * Mpad + p0 + 16 * rg;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<uint4*>(dst + k * Mpad) = make_uint4(e[0][k], e[1][k], e[2][k], e[3][k]);
     }
   }
 }
