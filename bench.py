@@ -71,8 +71,14 @@ def step_accounting(path, n, U):
     T, H, k, E, I = cfg.T, cfg.H, cfg.k, cfg.E, cfg.I
     M_cap = path.m_cap
     acc = {}
-    acc["quantize"] = {"bytes": (T // path.share) * H * 3 + (T // path.share) * 4, "flops": 0}
-    acc["sort"] = {"bytes": T * k * 4 + 2 * T * k * 4 + E * 4 + U * H + n * H + 8 * n, "flops": 0}
+    if path.fused_quantize:
+        # one pass: ids, perm and inv_pos, the bf16 rows of the U tokens with a local row, the fp8 rows
+        # and scales of the n local rows
+        acc["quantize_sort"] = {"bytes": T * k * 4 + 2 * T * k * 4 + E * 4 + U * H * 2 + n * H + 4 * n,
+                                "flops": 0}
+    else:
+        acc["quantize"] = {"bytes": (T // path.share) * H * 3 + (T // path.share) * 4, "flops": 0}
+        acc["sort"] = {"bytes": T * k * 4 + 2 * T * k * 4 + E * 4 + U * H + n * H + 8 * n, "flops": 0}
     gm = []
     nonempty = int(path.nonempty_local)
     # the gated FFN's two input projections run as one launch over [W0 | W1]
@@ -108,7 +114,8 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
     del data
     acc = step_accounting(path, n, U)
 
-    names = ["quantize", "sort"] + [f"gmm_{g['name']}" for g in acc["gmm"]] + \
+    names = (["quantize_sort"] if path.fused_quantize else ["quantize", "sort"]) + \
+        [f"gmm_{g['name']}" for g in acc["gmm"]] + \
         (["silu_quant"] if cfg.pipeline == "ffn" else []) + ["gather_reduce"]
     ev = {nm: [] for nm in names}
 
@@ -124,8 +131,11 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
             fn()
 
     def one_step(record):
-        timed("quantize", path.quantize, record)
-        timed("sort", path.sort, record)
+        if path.fused_quantize:
+            timed("quantize_sort", path.sort, record)
+        else:
+            timed("quantize", path.quantize, record)
+            timed("sort", path.sort, record)
         ls = path.ss if path.act_mode == m.MOE_SCALE_ROW_DYNAMIC else path.xscale
         if cfg.pipeline == "up":
             timed("gmm_w_up", lambda: path.gmm(path.xs, ls, path.act_mode, path.w["w_up"], path.y), record)
@@ -200,7 +210,7 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
         tf = gmm_flops / (gmm_us * 1e-6) / 1e12
         roof.update({"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4)})
-    sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "gather_reduce")}
+    sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "quantize_sort", "gather_reduce") if nm in kern}
     value = gmm_flops / (ms_step * 1e-3) / 1e12
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,

@@ -185,6 +185,36 @@ int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t 
                        float* ss, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_quantize_sort_by_expert -- moe_quantize_rows followed by
+ * moe_sort_by_expert in one pass over the activations, for the single-GPU
+ * path where no all-gather sits between them (the quantized activation
+ * sort of "Quantize activations before EP all gather"; the same per-token
+ * absmax scheme of "Support quantization for tokamax gmm v2").  Each token's
+ * bf16 row is read once and its e4m3fn codes go straight to its local
+ * destination rows; a token with none is not quantized (unless `scale` asks
+ * for its scale).
+ *   x        [T, H] bf16, 16-byte aligned; H > 0, a multiple of 16.
+ *   scale_mode MOE_SCALE_ROW_DYNAMIC or MOE_SCALE_TENSOR_STATIC (with
+ *            static_scale as in moe_quantize_rows); MOE_SCALE_TENSOR_DYNAMIC
+ *            needs the whole tensor before any code and is MOE_ERR_UNSUPPORTED.
+ *   expert_ids .. group_sizes, M_cap, ws, ws_bytes: as in moe_sort_by_expert
+ *            (workspace of moe_workspace_bytes(MOE_OP_SORT_BY_EXPERT, ...)).
+ *   xs       [M_cap, H] e4m3fn out: the bytes moe_quantize_rows then
+ *            moe_sort_by_expert would write (rows [n, M_cap) zero).
+ *   ss       row mode: [M_cap] f32 out, each local row's token scale (0 past
+ *            n); static mode: unused, may be NULL.
+ *   scale    optional: row mode [T] f32 out, every token's scale (then every
+ *            token is quantized); static mode [1] f32 out = static_scale.
+ * Errors as in moe_sort_by_expert; device-data errors (bad expert ids, more
+ * local rows than M_cap) set the same workspace error bits.
+ */
+int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_mode, float static_scale,
+                                const int32_t* expert_ids, int32_t k, int32_t E, int32_t group_offset,
+                                int32_t num_local_experts, int64_t M_cap, int32_t* perm, int32_t* inv_pos,
+                                int32_t* group_sizes, uint8_t* xs, float* ss, float* scale, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
  * moe_gmm_fp8 -- grouped matmul of fp8 operands, the gmm_v2 call of "Quantize
  * activations before EP all gather" (review comment on the prequantized test:
  * lhs_q, rhs_q, group_sizes, rhs_scale, group_offset, no lhs quantization in

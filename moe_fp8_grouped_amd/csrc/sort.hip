@@ -21,7 +21,7 @@
 //            it to each of its local destinations; extra waves zero rows
 //            [n, M_cap).  Coalesced 16-byte loads and stores.
 // No float atomics and no order-dependent steps: the result is deterministic.
-#include "common.hpp"
+#include "quant_common.hpp"
 
 namespace moe {
 namespace {
@@ -302,6 +302,110 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const uint8_t* __rest
   }
 }
 
+// The fused quantize-and-gather (one GPU): one wave per token reads the
+// token's bf16 row once, forms its absmax and e4m3fn codes in registers with
+// the row quantizer's own functions (same bytes as moe_quantize_rows), and
+// writes each 16-byte group of codes to every local destination row of the
+// token; a token without one is skipped unless its scale is asked for.
+// GPL 16-element groups per lane keep rows of up to GPL * 1024 elements in
+// registers; GPL = 0 reads the row twice (absmax pass, then codes).  Rows
+// [n, M_cap) get zeros.
+template <int GPL>
+__device__ __forceinline__ void load_group16(const uint16_t* __restrict__ row, int64_t gi, float v[16]) {
+  Bf16x8 a, b;
+  a.raw = *reinterpret_cast<const uint4*>(row + gi * 16);
+  b.raw = *reinterpret_cast<const uint4*>(row + gi * 16 + 8);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = a.get(i);
+    v[8 + i] = b.get(i);
+  }
+}
+
+__device__ __forceinline__ void scatter_codes(uint8_t* __restrict__ xs, int64_t H, int64_t gi, uint64_t m, int my_r,
+                                              const float v[16], const RowDiv& d) {
+  const uint2 lo = codes8(v, d), hi = codes8(v + 8, d);
+  const uint4 code = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  while (m) {
+    const int j = __builtin_ctzll(m);
+    m &= m - 1;
+    const int r = __builtin_amdgcn_readlane(my_r, j);
+    *reinterpret_cast<uint4*>(xs + static_cast<int64_t>(r) * H + gi * 16) = code;
+  }
+}
+
+template <int GPL>
+__global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* __restrict__ x, int static_mode,
+                                                               float static_scale, const int32_t* __restrict__ inv_pos,
+                                                               int64_t T, int k, int64_t H, int64_t M_cap,
+                                                               const int32_t* __restrict__ hdr, uint8_t* __restrict__ xs,
+                                                               float* __restrict__ ss, float* __restrict__ tok_scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t G = H >> 4;
+  if (static_mode && tok_scale && wid == 0 && lane == 0) tok_scale[0] = static_scale;
+  for (int64_t t = wid; t < T; t += nw) {
+    int my_r = -1;
+    if (lane < k) my_r = inv_pos[t * k + lane];
+    if (my_r >= M_cap) my_r = -1;
+    const uint64_t m = __ballot(my_r >= 0);
+    if (m == 0 && !(tok_scale && !static_mode)) continue;
+    const uint16_t* row = x + t * H;
+    float amax = 0.0f;
+    if constexpr (GPL > 0) {
+      float v[GPL][16];
+#pragma unroll
+      for (int c = 0; c < GPL; ++c) {
+        const int64_t gi = lane + 64 * c;
+        if (gi < G) {
+          load_group16<GPL>(row, gi, v[c]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+        }
+      }
+      amax = wave_max(amax);
+      const float s = static_mode ? static_scale : scale_from_amax(amax);
+      const RowDiv d(s);
+#pragma unroll
+      for (int c = 0; c < GPL; ++c) {
+        const int64_t gi = lane + 64 * c;
+        if (gi < G) scatter_codes(xs, H, gi, m, my_r, v[c], d);
+      }
+      if (!static_mode) {
+        if (my_r >= 0 && ss) ss[my_r] = s;
+        if (tok_scale && lane == 0) tok_scale[t] = s;
+      }
+    } else {
+      for (int64_t gi = lane; gi < G; gi += 64) {
+        float v[16];
+        load_group16<0>(row, gi, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      }
+      amax = wave_max(amax);
+      const float s = static_mode ? static_scale : scale_from_amax(amax);
+      const RowDiv d(s);
+      for (int64_t gi = lane; gi < G; gi += 64) {
+        float v[16];
+        load_group16<0>(row, gi, v);
+        scatter_codes(xs, H, gi, m, my_r, v, d);
+      }
+      if (!static_mode) {
+        if (my_r >= 0 && ss) ss[my_r] = s;
+        if (tok_scale && lane == 0) tok_scale[t] = s;
+      }
+    }
+  }
+  int64_t n = hdr[kN];
+  if (n > M_cap) n = M_cap;
+  for (int64_t r = n + wid; r < M_cap; r += nw) {
+    uint4* dst = reinterpret_cast<uint4*>(xs + r * H);
+    for (int64_t c = lane; c < (H >> 4); c += 64) dst[c] = make_uint4(0, 0, 0, 0);
+    if (ss && !static_mode && lane == 0) ss[r] = 0.0f;
+  }
+}
+
 }  // namespace
 
 size_t sort_ws_bytes(int64_t M, int E) {
@@ -309,6 +413,68 @@ size_t sort_ws_bytes(int64_t M, int E) {
   return kHdr + static_cast<size_t>(moe_cdiv(ntiles * (E + 1) * 4, 256) * 256);
 }
 
+}  // namespace moe
+
+namespace moe {
+namespace {
+// The sort's metadata stages (histogram, scan, stable rank) into perm,
+// inv_pos, group_sizes and the workspace header.
+int sort_metadata(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, int32_t group_offset,
+                  int32_t num_local_experts, int64_t M_cap, int32_t* perm, int32_t* inv_pos, int32_t* group_sizes,
+                  void* ws, size_t ws_bytes, hipStream_t st) {
+  const int64_t M = T * k;
+  if (!group_sizes || !ws || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
+  if (ws_bytes < sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
+  int32_t* hdr = static_cast<int32_t*>(ws);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kHdr);
+  // small tiles (more workgroups) whenever their table fits the scan's LDS
+  const bool small = moe_cdiv(M, kTileSmall) * (E + 1) <= kScanLds;
+  const int tile = small ? kTileSmall : kTile;
+  const int ntiles = static_cast<int>(moe_cdiv(M, tile));
+  const bool scan_in_lds = static_cast<int64_t>(ntiles) * (E + 1) <= kScanLds;
+  int nbits = 0;
+  while ((1 << nbits) < E + 1) ++nbits;
+  const size_t hist_lds = (E + 1) * sizeof(int);
+  if (ntiles > 0) {
+    if (small)
+      sort_hist_kernel<kTileSmall><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+    else
+      sort_hist_kernel<kTile><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+    MOE_CHECK_LAUNCH();
+  }
+  // hist -> rank with the scan fused into every rank block when the tile
+  // table fits in LDS; hist -> scan -> rank otherwise
+  const size_t rank_lds = 6 * hist_lds + static_cast<size_t>(ntiles) * (E + 1) * sizeof(int);
+  if (ntiles > 0 && scan_in_lds && rank_lds <= 64 * 1024) {
+    if (small)
+      sort_rank_kernel<kTileSmall, true><<<ntiles, 256, rank_lds, st>>>(
+          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+          perm, inv_pos);
+    else
+      sort_rank_kernel<kTile, true><<<ntiles, 256, rank_lds, st>>>(
+          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+          perm, inv_pos);
+    MOE_CHECK_LAUNCH();
+  } else {
+    const size_t scan_lds = hist_lds + (scan_in_lds ? static_cast<size_t>(ntiles) * (E + 1) * sizeof(int) : 0);
+    sort_scan_kernel<<<1, 1024, scan_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
+                                                     group_sizes, hdr, scan_in_lds ? 1 : 0);
+    MOE_CHECK_LAUNCH();
+    if (ntiles > 0) {
+      if (small)
+        sort_rank_kernel<kTileSmall, false><<<ntiles, 256, 5 * hist_lds, st>>>(
+            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+            perm, inv_pos);
+      else
+        sort_rank_kernel<kTile, false><<<ntiles, 256, 5 * hist_lds, st>>>(
+            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+            perm, inv_pos);
+      MOE_CHECK_LAUNCH();
+    }
+  }
+  return MOE_OK;
+}
+}  // namespace
 }  // namespace moe
 
 extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
@@ -332,52 +498,9 @@ extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t 
   if (ws_bytes < moe::sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* hdr = static_cast<int32_t*>(ws);
-  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + moe::kHdr);
-  // small tiles (more workgroups) whenever their table fits the scan's LDS
-  const bool small = moe_cdiv(M, moe::kTileSmall) * (E + 1) <= moe::kScanLds;
-  const int tile = small ? moe::kTileSmall : moe::kTile;
-  const int ntiles = static_cast<int>(moe_cdiv(M, tile));
-  const bool scan_in_lds = static_cast<int64_t>(ntiles) * (E + 1) <= moe::kScanLds;
-  int nbits = 0;
-  while ((1 << nbits) < E + 1) ++nbits;
-  const size_t hist_lds = (E + 1) * sizeof(int);
-  if (ntiles > 0) {
-    if (small)
-      moe::sort_hist_kernel<moe::kTileSmall><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
-    else
-      moe::sort_hist_kernel<moe::kTile><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
-    MOE_CHECK_LAUNCH();
-  }
-  // hist -> rank with the scan fused into every rank block when the tile
-  // table fits in LDS; hist -> scan -> rank otherwise
-  const size_t rank_lds = 6 * hist_lds + static_cast<size_t>(ntiles) * (E + 1) * sizeof(int);
-  if (ntiles > 0 && scan_in_lds && rank_lds <= 64 * 1024) {
-    if (small)
-      moe::sort_rank_kernel<moe::kTileSmall, true><<<ntiles, 256, rank_lds, st>>>(
-          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-          perm, inv_pos);
-    else
-      moe::sort_rank_kernel<moe::kTile, true><<<ntiles, 256, rank_lds, st>>>(
-          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-          perm, inv_pos);
-    MOE_CHECK_LAUNCH();
-  } else {
-    const size_t scan_lds = hist_lds + (scan_in_lds ? static_cast<size_t>(ntiles) * (E + 1) * sizeof(int) : 0);
-    moe::sort_scan_kernel<<<1, 1024, scan_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
-                                                     group_sizes, hdr, scan_in_lds ? 1 : 0);
-    MOE_CHECK_LAUNCH();
-    if (ntiles > 0) {
-      if (small)
-        moe::sort_rank_kernel<moe::kTileSmall, false><<<ntiles, 256, 5 * hist_lds, st>>>(
-            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-            perm, inv_pos);
-      else
-        moe::sort_rank_kernel<moe::kTile, false><<<ntiles, 256, 5 * hist_lds, st>>>(
-            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-            perm, inv_pos);
-      MOE_CHECK_LAUNCH();
-    }
-  }
+  const int rc = moe::sort_metadata(expert_ids, T, k, E, group_offset, num_local_experts, M_cap, perm, inv_pos,
+                                    group_sizes, ws, ws_bytes, st);
+  if (rc != MOE_OK) return rc;
   if (xs || ss) {
     int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
     if (waves < 4) waves = 4;
@@ -386,5 +509,48 @@ extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t 
         xq, xscale, row_scale ? 1 : 0, inv_pos, T, k, H, M_cap, hdr, xs, ss);
     MOE_CHECK_LAUNCH();
   }
+  return MOE_OK;
+}
+
+extern "C" int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_mode, float static_scale,
+                                           const int32_t* expert_ids, int32_t k, int32_t E, int32_t group_offset,
+                                           int32_t num_local_experts, int64_t M_cap, int32_t* perm, int32_t* inv_pos,
+                                           int32_t* group_sizes, uint8_t* xs, float* ss, float* scale, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  if (T < 0 || k <= 0 || k > 64 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
+  if (group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E) return MOE_ERR_SHAPE;
+  if (M_cap < 0 || T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (H <= 0 || H % 16) return MOE_ERR_SHAPE;
+  if (scale_mode == MOE_SCALE_TENSOR_DYNAMIC) return MOE_ERR_UNSUPPORTED;   // needs the whole tensor first
+  if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_STATIC) return MOE_ERR_UNSUPPORTED;
+  const bool static_mode = scale_mode == MOE_SCALE_TENSOR_STATIC;
+  if (static_mode && !(static_scale > 0.0f && static_scale < 3.0e38f)) return MOE_ERR_SHAPE;
+  const int64_t M = T * k;
+  if (!group_sizes || !ws || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
+  if (T > 0 && !x) return MOE_ERR_NULL;
+  if (M_cap > 0 && (!xs || (!static_mode && !ss))) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return MOE_ERR_SHAPE;
+  if (ws_bytes < moe::sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* hdr = static_cast<int32_t*>(ws);
+  const int rc = moe::sort_metadata(expert_ids, T, k, E, group_offset, num_local_experts, M_cap, perm, inv_pos,
+                                    group_sizes, ws, ws_bytes, st);
+  if (rc != MOE_OK) return rc;
+  int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
+  if (waves < 4) waves = 4;
+  if (waves > 65536) waves = 65536;
+  const dim3 grid(static_cast<unsigned>(moe_cdiv(waves, 4))), block(256);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const int sm = static_mode ? 1 : 0;
+  const int64_t G = H / 16, gpl = moe_cdiv(G, 64);
+#define MOE_QS(GPL) \
+  moe::quantize_scatter_kernel<GPL><<<grid, block, 0, st>>>(xb, sm, static_scale, inv_pos, T, k, H, M_cap, hdr, xs, ss, scale)
+  if (gpl <= 1) MOE_QS(1);
+  else if (gpl <= 2) MOE_QS(2);
+  else if (gpl <= 4) MOE_QS(4);
+  else if (gpl <= 8) MOE_QS(8);
+  else MOE_QS(0);
+#undef MOE_QS
+  MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

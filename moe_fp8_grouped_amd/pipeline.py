@@ -23,7 +23,7 @@ import torch
 from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_F32, MOE_OP_GMM, MOE_OP_QUANTIZE_ROWS,
                MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
                MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gmm_fp8, moe_quantize_rows, moe_quantize_rows_strided,
-               moe_quantize_weights, moe_sort_by_expert, moe_tgmm_fp8, workspace)
+               moe_quantize_sort_by_expert, moe_quantize_weights, moe_sort_by_expert, moe_tgmm_fp8, workspace)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -62,7 +62,7 @@ class ForwardPath:
     """Up-projection (``cfg.pipeline == 'up'``) or gated FFN forward."""
 
     def __init__(self, cfg, data, device="cuda", static_act=None, static_weight=None, nk=True, m_cap=None,
-                 share=1, weights_dev=None):
+                 share=1, weights_dev=None, fused_quantize=None):
         self.cfg, self.dev = cfg, device
         T, H, E, k = cfg.T, cfg.H, cfg.E, cfg.k
         self.T, self.H, self.k, self.E = T, H, k, E
@@ -72,6 +72,9 @@ class ForwardPath:
         self.act_mode = MOE_SCALE_TENSOR_STATIC if static_act is not None else MOE_SCALE_ROW_DYNAMIC
         self.static_act = static_act or 0.0
         self.share = share
+        # one GPU's own tokens: quantize and sort in one pass (moe_quantize_sort_by_expert); with an
+        # expert-parallel share the sort reads the all-gathered fp8 rows, so the two stay separate
+        self.fused_quantize = (share == 1) if fused_quantize is None else bool(fused_quantize)
         self.x = bf16_tensor(data["x"], device)
         self.ids = torch.from_numpy(np.ascontiguousarray(data["ids"], dtype=np.int32)).to(device)
         self.topk_w = torch.from_numpy(np.ascontiguousarray(data["topk_w"], dtype=np.float32)).to(device)
@@ -117,10 +120,19 @@ class ForwardPath:
                           self.xq[r0:r0 + rows], xs, None, self.ws_q)
 
     def quantize(self):
+        if self.fused_quantize:
+            return                     # done by sort()
         rows = self.T // self.share
         self._quantize(0, rows)        # this GPU's share sits in slot 0
 
     def sort(self):
+        if self.fused_quantize:
+            row = self.act_mode == MOE_SCALE_ROW_DYNAMIC
+            moe_quantize_sort_by_expert(self.x, self.T, self.H, self.act_mode, self.static_act, self.ids, self.k,
+                                        self.E, self.g0, self.El, self.m_cap, self.perm, self.inv_pos,
+                                        self.group_sizes, self.xs, self.ss if row else None,
+                                        None if row else self.xscale, self.ws_sort)
+            return
         moe_sort_by_expert(self.ids, self.T, self.k, self.E, self.g0, self.El, self.xq, self.xscale,
                            self.act_mode, self.H, self.m_cap, self.perm, self.inv_pos, self.group_sizes,
                            self.xs, self.ss if self.act_mode == MOE_SCALE_ROW_DYNAMIC else None, self.ws_sort)

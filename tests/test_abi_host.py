@@ -34,7 +34,7 @@ def lib():
 
 def test_header_declares_the_path_calls():
     names = _declared_functions()
-    for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
+    for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
                "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
                "moe_version"]:
         assert fn in names
@@ -114,6 +114,22 @@ def test_sort_validation(lib):
     assert call(gs=None) == m.MOE_ERR_NULL
     assert call(xq=one, H=32, xs=None) == m.MOE_ERR_NULL
     assert call(wsb=16) == m.MOE_ERR_WORKSPACE
+
+
+def test_quantize_sort_validation(lib):
+    f = lambda *a: _c(lib, "moe_quantize_sort_by_expert", *a)
+    al = 4096   # 16-byte aligned dummy pointer: never dereferenced on these paths
+    def call(x=al, T=4, H=32, mode=0, static=0.0, k=2, E=8, g0=0, El=8, M_cap=8, xs=al, ss=al, ws=al, wsb=1 << 20):
+        return f(x, T, H, mode, static, al, k, E, g0, El, M_cap, al, al, al, xs, ss, None, ws, wsb, None)
+    assert call(H=24) == m.MOE_ERR_SHAPE
+    assert call(mode=1) == m.MOE_ERR_UNSUPPORTED          # tensor-dynamic needs the whole tensor first
+    assert call(mode=2, static=-1.0) == m.MOE_ERR_SHAPE
+    assert call(x=None) == m.MOE_ERR_NULL
+    assert call(xs=None) == m.MOE_ERR_NULL
+    assert call(ss=None) == m.MOE_ERR_NULL                # row mode needs the row scales
+    assert call(x=al + 8) == m.MOE_ERR_SHAPE              # misaligned rows
+    assert call(wsb=16) == m.MOE_ERR_WORKSPACE
+    assert call(E=0) == m.MOE_ERR_SHAPE
 
 
 def test_gmm_validation(lib):

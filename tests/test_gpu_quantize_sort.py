@@ -141,6 +141,48 @@ def test_silu_every_finite_bf16_gate_value():
     assert_bits_equal(q, qo, "codes")
 
 
+@pytest.mark.parametrize("T,k,E,g0,El,H,mode,extra,want_scale", [
+    (4096, 8, 64, 0, 64, 2048, 0, 0, False),        # the gated FFN's routing shape
+    (2000, 8, 256, 64, 32, 7168, 0, 37, True),      # a local expert slice, zero rows after n, every token's scale
+    (500, 2, 8, 0, 8, 512, 2, 5, True),             # static scale
+    (300, 3, 5, 1, 3, 8208, 0, 3, False),           # rows too long for registers (two passes)
+    (0, 4, 8, 0, 8, 64, 0, 4, False),               # no tokens: the window is all zeros
+])
+def test_quantize_sort_fused_bit_exact(T, k, E, g0, El, H, mode, extra, want_scale):
+    """moe_quantize_sort_by_expert writes what moe_quantize_rows then
+    moe_sort_by_expert write: the oracle's quantization and stable sort."""
+    rng = np.random.default_rng(T + H + mode)
+    x = _bits(rng, (T, H), 2.0)
+    if T > 2:
+        x[1] = 0                                     # an all-zero row (scale 1)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) if T else \
+        np.zeros((0, k), np.int32)
+    static = STATIC_ACT_SCALE if mode == m.MOE_SCALE_TENSOR_STATIC else None
+    xq, xsc, _ = quantize_rows(x, mode, static_scale=static)
+    n = int(((ids >= g0) & (ids < g0 + El)).sum())
+    m_cap = n + extra
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc, xscale_mode=mode, m_cap=m_cap)
+    dev = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+    perm, inv = dev(T * k, torch.int32), dev(T * k, torch.int32)
+    gs = dev(E, torch.int32)
+    xs = torch.full((m_cap, H), 0x55, dtype=torch.uint8, device="cuda")
+    ss = torch.full((m_cap,), 7.0, dtype=torch.float32, device="cuda") if mode == m.MOE_SCALE_ROW_DYNAMIC else None
+    sc = dev((T if mode == m.MOE_SCALE_ROW_DYNAMIC else 1,), torch.float32) if want_scale else None
+    ws = m.workspace(m.MOE_OP_SORT_BY_EXPERT, T * k, 0, 0, E)
+    print(f"quantize+sort T={T} k={k} E={E} g0={g0} El={El} H={H} mode={mode} m_cap={m_cap}", flush=True)
+    m.moe_quantize_sort_by_expert(dev_bf16(x) if T else dev((0, H), torch.bfloat16), T, H, mode, static or 0.0,
+                                  dev_i32(ids), k, E, g0, El, m_cap, perm, inv, gs, xs, ss, sc, ws)
+    assert m.moe_debug_check(ws) == 0
+    assert_bits_equal(host(perm), o["perm"], "perm")
+    assert_bits_equal(host(inv), o["inv_pos"], "inv_pos")
+    assert_bits_equal(host(gs), o["group_sizes"], "group_sizes")
+    assert_bits_equal(host(xs), o["xs"], "xs")
+    if ss is not None:
+        assert_bits_equal(host(ss), o["ss"], "ss")
+    if sc is not None:
+        assert_bits_equal(host(sc), xsc, "token scales")
+
+
 def test_empty_rows_tensor_dynamic():
     ws = m.workspace(m.MOE_OP_QUANTIZE_ROWS, 0, 32, m.MOE_SCALE_TENSOR_DYNAMIC)
     s = torch.zeros(1, dtype=torch.float32, device="cuda")
