@@ -81,6 +81,13 @@
 #ifndef MOE_GMM_STREAM_BATCH
 #define MOE_GMM_STREAM_BATCH 1
 #endif
+// Cache policy of the batched (weight-gradient) product's output stores: 2 is
+// the non-temporal hint, so the float32 output, several times larger than an
+// XCD's L2, streams past the L2 instead of evicting the operand tiles that the
+// group's other output tiles still read.
+#ifndef MOE_GMM_BATCH_STORE_POLICY
+#define MOE_GMM_BATCH_STORE_POLICY 2
+#endif
 
 namespace moe {
 namespace {
@@ -743,14 +750,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(uint8_t* base, uint3
 
 // Row block i of a converted tile: voff = the byte offset of the lane's row
 // of block 0 and its first column from the tile's first row.
-template <class C, bool OUT_BF16>
+template <class C, bool OUT_BF16, int POL = 0>
 __device__ __forceinline__ void store_rows(const OutPieces<C, OUT_BF16>& o, int i, __amdgpu_buffer_rsrc_t r,
                                            uint32_t voff, uint32_t row_bytes) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int u = 0; u < OutPieces<C, OUT_BF16>::U; ++u) {   // bf16: 32 columns apart; f32: 16
     const uint4 v = o.v[i][u];
-    __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, voff + 16 * i * row_bytes + u * 64, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, voff + 16 * i * row_bytes + u * 64, 0, POL);
   }
 }
 
@@ -764,6 +771,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
   static_assert(BM == 256 && BN == 128 && NST == 3 && NW == 8 && JN == 4, "streaming layout");
   constexpr int LPS = loads_per_step<C, KBLOCKS>();
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  constexpr int SPOL = BATCH ? MOE_GMM_BATCH_STORE_POLICY : 0;   // output store cache policy
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
   __shared__ __attribute__((aligned(16))) float prm[PRM_SLOTS * PRM];
   __shared__ GroupTableN<kStreamMaxLocal> gt;
@@ -897,7 +905,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
     OutPieces<C, OUT_BF16> z;                                                                                    \
     _Pragma("unroll") for (int i = 0; i < MI; ++i) _Pragma("unroll") for (int u = 0; u < OutPieces<C, OUT_BF16>::U; ++u) \
         z.v[i][u] = make_uint4(0, 0, 0, 0);                                                                      \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(z, i, zr, zo, static_cast<uint32_t>(row_bytes)); \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16, SPOL>(z, i, zr, zo, static_cast<uint32_t>(row_bytes)); \
     drain = true;                                                                                                \
   } while (0)
   while (ct < last) {
@@ -1011,7 +1019,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
                          static_cast<uint32_t>(Cd.rows_here * row_bytes));
       p_voff = static_cast<uint32_t>((rbase + (lane & 15)) * row_bytes + (Cd.col0 + cbase) * ESZ + 16 * (lane >> 4));
 #pragma unroll
-      for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+      for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16, SPOL>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
       st_now = true;
 #pragma unroll
       for (int i = 0; i < MI; ++i)

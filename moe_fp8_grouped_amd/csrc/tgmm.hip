@@ -108,11 +108,13 @@ __global__ __launch_bounds__(256) void tgmm_kernel(const uint8_t* __restrict__ l
 // AT[c, 128 * tiles_off[g] + i] = A[rows_off[g] + i, c] for i < m_g and 0 for
 // m_g <= i < the group's padded length (a multiple of 128): the rows of each
 // group become a contraction axis of its own, contiguous per column.  An
-// item is a 64-row block and up to four 64-column blocks: every thread
-// issues its four 16-byte loads before any LDS store (one memory latency per
-// item, not per tile), the tiles go through LDS (row stride 68 bytes), and
-// each thread reads 16 rows x 4 columns as dwords and transposes 4 x 4 byte
-// blocks in registers (v_perm_b32) into four 16-byte column stores.
+// item is a 64-row block and up to four 64-column blocks.  A workgroup walks
+// its items two at a time with two register buffers: the four 16-byte loads
+// of its next item are in flight while the current one goes through LDS (row
+// stride 68 bytes) and out, and the barriers are bare (LDS counter only) so
+// they do not wait for those loads.  Each thread reads 16 rows x 4 columns of
+// a tile as dwords and transposes 4 x 4 byte blocks in registers (v_perm_b32)
+// into four 16-byte column stores.
 __device__ __forceinline__ void transpose4x4(const uint32_t* d, uint32_t* e) {
   // d[i]: row i's four column bytes; e[c]: column c's four row bytes
   const uint32_t lo01 = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);
@@ -124,6 +126,15 @@ __device__ __forceinline__ void transpose4x4(const uint32_t* d, uint32_t* e) {
   e[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
   e[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
+
+// LDS-only barrier: waits for this wave's LDS operations, not its global loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct TItem {
+  int64_t p0, cb0;   // first padded row, first 64-column block
+  int nb;            // column blocks in this item (1..4)
+  int keep;          // bit u: this thread's load u holds data (else the piece is zero)
+};
 
 __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __restrict__ A, int64_t C,
                                                                const int32_t* __restrict__ group_sizes, int g0,
@@ -141,48 +152,81 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
   const int tid = threadIdx.x;
   const int lr = tid >> 2, lc16 = (tid & 3) * 16;              // load: row, 16-byte column piece
   const int tu = tid >> 6, rg = (tid >> 4) & 3, cg = tid & 15;  // transpose: tile, 16-row group, 4-column group
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+
+  // issue the loads of item `it` (zeros for padding rows and absent column blocks)
+  auto fetch = [&](int64_t it, TItem& I, uint4 (&v)[4]) {
     const int64_t pb = it / cq, q = it - pb * cq;
-    const int64_t p0 = pb * 64, cb0 = q * 4;
-    const int nb = static_cast<int>(cblocks - cb0 < 4 ? cblocks - cb0 : 4);
-    // the group holding padded rows p0 .. p0 + 63 (padded lengths are multiples of 128)
+    I.p0 = pb * 64;
+    I.cb0 = q * 4;
+    I.nb = static_cast<int>(cblocks - I.cb0 < 4 ? cblocks - I.cb0 : 4);
+    // the group holding padded rows p0 .. p0 + 63 (padded lengths are multiples
+    // of 128); the item is the workgroup's, so the search runs on scalars
     int lo = 0, hi = El - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (static_cast<int64_t>(gt.tiles_off[mid]) * 128 <= p0) lo = mid; else hi = mid - 1;
+      if (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[mid])) * 128 <= I.p0) lo = mid;
+      else hi = mid - 1;
     }
     const int g = lo;
-    const int64_t i0 = p0 - static_cast<int64_t>(gt.tiles_off[g]) * 128;   // first local row of the block
-    const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
+    const int row0 = __builtin_amdgcn_readfirstlane(gt.rows_off[g]);
+    const int64_t i0 = I.p0 - static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[g])) * 128;
+    const int m_g = __builtin_amdgcn_readfirstlane(gt.rows_off[g + 1]) - row0;
     const bool live = i0 + lr < m_g;
-    const uint8_t* src = A + (gt.rows_off[g] + i0 + lr) * C + cb0 * 64 + lc16;
-    uint4 v[4];
+    const uint8_t* src = A + (row0 + i0 + lr) * C + I.cb0 * 64 + lc16;
+    // every load is issued (a piece with no data reads A's first bytes and is
+    // zeroed when staged), so the loads carry no branches and stay in flight
+    I.keep = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      v[u] = make_uint4(0, 0, 0, 0);
-      if (u < nb && live) v[u] = *reinterpret_cast<const uint4*>(src + u * 64);
+      const bool ok = u < I.nb && live;
+      I.keep |= ok ? 1 << u : 0;
+      v[u] = *reinterpret_cast<const uint4*>(ok ? src + u * 64 : A);
     }
-    __syncthreads();                          // the previous item's reads of tl are done
+  };
+  // stage item I's rows in LDS, transpose, store its columns
+  auto put = [&](const TItem& I, const uint4 (&v)[4]) {
+    lds_barrier();                            // the previous item's reads of tl are done
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (u < nb) {
+      if (u < I.nb) {
+        const uint4 w = (I.keep >> u) & 1 ? v[u] : make_uint4(0, 0, 0, 0);
         uint32_t* d = reinterpret_cast<uint32_t*>(tl + u * TS + lr * 68 + lc16);
-        d[0] = v[u].x; d[1] = v[u].y; d[2] = v[u].z; d[3] = v[u].w;
+        d[0] = w.x; d[1] = w.y; d[2] = w.z; d[3] = w.w;
       }
     }
-    __syncthreads();
-    if (tu < nb) {
+    lds_barrier();
+    if (tu < I.nb) {
       const uint8_t* t = tl + tu * TS + (16 * rg) * 68 + 4 * cg;
       uint32_t d[16], e[4][4];
 #pragma unroll
       for (int j = 0; j < 16; ++j) d[j] = *reinterpret_cast<const uint32_t*>(t + j * 68);
 #pragma unroll
       for (int b = 0; b < 4; ++b) transpose4x4(d + 4 * b, e[b]);
-      uint8_t* dst = AT + ((cb0 + tu) * 64 + 4 * cg) * Mpad + p0 + 16 * rg;
+      uint8_t* dst = AT + ((I.cb0 + tu) * 64 + 4 * cg) * Mpad + I.p0 + 16 * rg;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         *reinterpret_cast<uint4*>(dst + k * Mpad) = make_uint4(e[0][k], e[1][k], e[2][k], e[3][k]);
     }
+  };
+
+  // The fetch of the item after the last one re-reads the last item (never
+  // staged): every fetch is unconditional, so no register buffer is merged
+  // across a branch and the loads are never waited for early.
+  const int64_t G = gridDim.x;
+  int64_t it = blockIdx.x;
+  if (it >= items) return;
+  TItem ia, ib;
+  uint4 va[4], vb[4];
+  fetch(it, ia, va);
+  for (;;) {
+    fetch(it + G < items ? it + G : items - 1, ib, vb);
+    put(ia, va);
+    it += G;
+    if (it >= items) break;
+    fetch(it + G < items ? it + G : items - 1, ia, va);
+    put(ib, vb);
+    it += G;
+    if (it >= items) break;
   }
 }
 
