@@ -108,13 +108,16 @@ __global__ __launch_bounds__(256) void tgmm_kernel(const uint8_t* __restrict__ l
 // AT[c, 128 * tiles_off[g] + i] = A[rows_off[g] + i, c] for i < m_g and 0 for
 // m_g <= i < the group's padded length (a multiple of 128): the rows of each
 // group become a contraction axis of its own, contiguous per column.  An
-// item is a 64-row block and up to four 64-column blocks.  A workgroup walks
-// its items two at a time with two register buffers: the four 16-byte loads
-// of its next item are in flight while the current one goes through LDS (row
-// stride 68 bytes) and out, and the barriers are bare (LDS counter only) so
-// they do not wait for those loads.  Each thread reads 16 rows x 4 columns of
-// a tile as dwords and transposes 4 x 4 byte blocks in registers (v_perm_b32)
-// into four 16-byte column stores.
+// item is a 128-row block (inside one group, as padded lengths are multiples
+// of 128) and up to two 64-column blocks, so every store instruction writes
+// whole 128-byte lines: eight lanes cover the 128 rows of one column.  A
+// workgroup walks its items with two register buffers: the four 16-byte
+// loads of its next item are in flight while the current one goes through
+// LDS and out, behind bare barriers that do not wait for those loads.  The
+// staged rows are 128 bytes with 16-byte piece p of row r at slot
+// p ^ ((r / 16) & 7), which keeps the dword reads of the transpose (16 rows
+// x 4 columns per thread, 4 x 4 byte blocks transposed in registers with
+// v_perm_b32) at the minimum two LDS cycles per instruction.
 __device__ __forceinline__ void transpose4x4(const uint32_t* d, uint32_t* e) {
   // d[i]: row i's four column bytes; e[c]: column c's four row bytes
   const uint32_t lo01 = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);
@@ -132,7 +135,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 struct TItem {
   int64_t p0, cb0;   // first padded row, first 64-column block
-  int nb;            // column blocks in this item (1..4)
+  int nb;            // column blocks in this item (1..2)
   int keep;          // bit u: this thread's load u holds data (else the piece is zero)
 };
 
@@ -140,27 +143,29 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
                                                                const int32_t* __restrict__ group_sizes, int g0,
                                                                int El, int64_t max_rows, int64_t Mpad,
                                                                uint8_t* __restrict__ AT, int32_t* __restrict__ err) {
-  constexpr int TS = 64 * 68;                 // one 64 x 64 byte tile, rows padded to 68 bytes
+  constexpr int IR = 128;                     // rows per item
   __shared__ GroupTable gt;
   __shared__ int tmp[kMaxLocal];
-  __shared__ __attribute__((aligned(16))) uint8_t tl[4 * TS];
+  __shared__ __attribute__((aligned(16))) uint8_t tl[IR * 128];
   build_groups(group_sizes, g0, El, max_rows, 1, 128, err, gt, tmp, false);
   const int64_t P = static_cast<int64_t>(gt.tiles_off[El]) * 128;    // padded rows
   const int64_t cblocks = C / 64;
-  const int64_t cq = (cblocks + 3) / 4;
-  const int64_t items = (P / 64) * cq;
+  const int64_t cq = (cblocks + 1) / 2;
+  const int64_t items = (P / IR) * cq;
   const int tid = threadIdx.x;
-  const int lr = tid >> 2, lc16 = (tid & 3) * 16;              // load: row, 16-byte column piece
-  const int tu = tid >> 6, rg = (tid >> 4) & 3, cg = tid & 15;  // transpose: tile, 16-row group, 4-column group
+  const int lr = tid >> 3, pc = tid & 7;       // load: rows lr + 32 u, 16-byte piece pc of 128 bytes
+  const int rg = tid & 7, cg = tid >> 3;       // transpose: 16-row group rg, 4-column group cg
 
-  // issue the loads of item `it` (zeros for padding rows and absent column blocks)
+  // issue the loads of item `it`; every load is issued (a piece with no data
+  // reads A's first bytes and is zeroed when staged), so the loads carry no
+  // branches and stay in flight
   auto fetch = [&](int64_t it, TItem& I, uint4 (&v)[4]) {
     const int64_t pb = it / cq, q = it - pb * cq;
-    I.p0 = pb * 64;
-    I.cb0 = q * 4;
-    I.nb = static_cast<int>(cblocks - I.cb0 < 4 ? cblocks - I.cb0 : 4);
-    // the group holding padded rows p0 .. p0 + 63 (padded lengths are multiples
-    // of 128); the item is the workgroup's, so the search runs on scalars
+    I.p0 = pb * IR;
+    I.cb0 = q * 2;
+    I.nb = static_cast<int>(cblocks - I.cb0 < 2 ? cblocks - I.cb0 : 2);
+    // the group holding padded rows p0 .. p0 + 127; the item is the
+    // workgroup's, so the search runs on scalars
     int lo = 0, hi = El - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -171,16 +176,14 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
     const int row0 = __builtin_amdgcn_readfirstlane(gt.rows_off[g]);
     const int64_t i0 = I.p0 - static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[g])) * 128;
     const int m_g = __builtin_amdgcn_readfirstlane(gt.rows_off[g + 1]) - row0;
-    const bool live = i0 + lr < m_g;
-    const uint8_t* src = A + (row0 + i0 + lr) * C + I.cb0 * 64 + lc16;
-    // every load is issued (a piece with no data reads A's first bytes and is
-    // zeroed when staged), so the loads carry no branches and stay in flight
+    const bool col_ok = (pc >> 2) < I.nb;
+    const uint8_t* src = A + (row0 + i0 + lr) * C + I.cb0 * 64 + 16 * pc;
     I.keep = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool ok = u < I.nb && live;
+      const bool ok = col_ok && i0 + lr + 32 * u < m_g;
       I.keep |= ok ? 1 << u : 0;
-      v[u] = *reinterpret_cast<const uint4*>(ok ? src + u * 64 : A);
+      v[u] = *reinterpret_cast<const uint4*>(ok ? src + 32 * u * C : A);
     }
   };
   // stage item I's rows in LDS, transpose, store its columns
@@ -188,21 +191,19 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
     lds_barrier();                            // the previous item's reads of tl are done
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (u < I.nb) {
-        const uint4 w = (I.keep >> u) & 1 ? v[u] : make_uint4(0, 0, 0, 0);
-        uint32_t* d = reinterpret_cast<uint32_t*>(tl + u * TS + lr * 68 + lc16);
-        d[0] = w.x; d[1] = w.y; d[2] = w.z; d[3] = w.w;
-      }
+      const int r = lr + 32 * u;
+      const uint4 w = (I.keep >> u) & 1 ? v[u] : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(tl + r * 128 + 16 * (pc ^ ((r >> 4) & 7))) = w;
     }
     lds_barrier();
-    if (tu < I.nb) {
-      const uint8_t* t = tl + tu * TS + (16 * rg) * 68 + 4 * cg;
+    if ((cg >> 4) < I.nb) {
+      const uint8_t* t = tl + (16 * rg) * 128 + 16 * ((cg >> 2) ^ rg) + 4 * (cg & 3);
       uint32_t d[16], e[4][4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) d[j] = *reinterpret_cast<const uint32_t*>(t + j * 68);
+      for (int j = 0; j < 16; ++j) d[j] = *reinterpret_cast<const uint32_t*>(t + j * 128);
 #pragma unroll
       for (int b = 0; b < 4; ++b) transpose4x4(d + 4 * b, e[b]);
-      uint8_t* dst = AT + ((I.cb0 + tu) * 64 + 4 * cg) * Mpad + I.p0 + 16 * rg;
+      uint8_t* dst = AT + (I.cb0 * 64 + 4 * cg) * Mpad + I.p0 + 16 * rg;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         *reinterpret_cast<uint4*>(dst + k * Mpad) = make_uint4(e[0][k], e[1][k], e[2][k], e[3][k]);
