@@ -108,6 +108,50 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   }
 }
 
+// Few long rows (up to 2048 rows of 2056..8192 elements, e.g. one GPU's own
+// tokens of an expert-parallel layer): one workgroup of four waves per row,
+// so that four times as many waves hide the memory latency.  Thread t owns
+// chunks t, t + 256, ...; the row absmax is a wave reduction and a max over
+// the four waves' results through LDS (max is exact in any order, so the
+// scale and the codes equal the one-wave kernel's).
+template <int CPL, int ACT, int MODE>
+__global__ __launch_bounds__(256) void quantize_row_wg_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu, int64_t C, int64_t ldx,
+    const float* __restrict__ given_scale, uint8_t* __restrict__ q, float* __restrict__ scale,
+    float* __restrict__ row_amax) {
+  __shared__ float wmax[4];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t nchunks = C >> 3;
+  const int64_t base = row * C, xbase = row * ldx;
+  float v[CPL][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t ch = tid + 256 * c;
+    if (ch < nchunks) {
+      load_vals<ACT>(x, xu, xbase + ch * 8, v[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+    }
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
+  const RowDiv div(s);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t ch = tid + 256 * c;
+    if (ch < nchunks) store_codes(q, base + ch * 8, v[c], div);
+  }
+  if (tid == 0) {
+    if (MODE == MODE_ROW) scale[row] = s;
+    if (row_amax) row_amax[row] = amax;
+  }
+}
+
 // First pass of the tensor-dynamic mode: each block reduces the absmax of a
 // grid-strided set of rows into partial[blockIdx.x] (no atomics, so the
 // result does not depend on scheduling; max is exact in any order).
@@ -151,6 +195,8 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restri
 
 __global__ void fill_scale_kernel(float* scale, float v) { *scale = v; }
 
+constexpr int64_t kWgRowsMax = 2048;   // up to here a row gets a workgroup when it is long
+
 template <int ACT, int MODE>
 hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t C, int64_t ldx, const float* given,
                        uint8_t* q, float* scale, float* row_amax, hipStream_t st) {
@@ -166,6 +212,15 @@ hipError_t launch_rows(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t
       quantize_rows_kernel<3, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
     else
       quantize_rows_kernel<5, ACT, MODE, 32><<<grid2, block, 0, st>>>(x, xu, R, C, ldx, given, q, scale, row_amax);
+    return hipGetLastError();
+  }
+  // few long rows: a workgroup per row (at 1024 rows of 7168, 4 waves per SIMD instead of 1)
+  if (R <= kWgRowsMax && nch > 256 && nch <= 1024) {
+    const dim3 gridr(static_cast<unsigned>(R));
+    if (nch <= 512)
+      quantize_row_wg_kernel<2, ACT, MODE><<<gridr, block, 0, st>>>(x, xu, C, ldx, given, q, scale, row_amax);
+    else
+      quantize_row_wg_kernel<4, ACT, MODE><<<gridr, block, 0, st>>>(x, xu, C, ldx, given, q, scale, row_amax);
     return hipGetLastError();
   }
   // Keep the row in registers when it fits (the SiLU variant holds float32).

@@ -35,7 +35,7 @@ def _bits(rng, shape, scale=1.0):
 
 
 @pytest.mark.parametrize("R,C", [(1, 16), (7, 48), (256, 512), (300, 2048), (33, 7168), (5, 8192), (3, 8208),
-                                 (5, 256), (9, 768), (3, 1280)])
+                                 (5, 256), (9, 768), (3, 1280), (1024, 2064), (2048, 4112), (2049, 4112)])
 def test_row_quantize_bit_exact(R, C):
     rng = np.random.default_rng(R * 7 + C)
     x = _bits(rng, (R, C), 3.0)
@@ -82,7 +82,7 @@ def test_tensor_and_static_modes():
     assert_bits_equal(s, so, "static scale")
 
 
-@pytest.mark.parametrize("R,C", [(64, 768), (33, 768), (7, 256), (37, 2048), (2, 16)])
+@pytest.mark.parametrize("R,C", [(64, 768), (33, 768), (7, 256), (37, 2048), (2, 16), (37, 4096), (3, 8192)])
 def test_silu_mul_requantize_bit_exact(R, C):
     rng = np.random.default_rng(R + C)
     a = _bits(rng, (R, C), 4.0)
@@ -95,7 +95,8 @@ def test_silu_mul_requantize_bit_exact(R, C):
 
 
 @pytest.mark.parametrize("R,C,act,mode", [(37, 768, 1, 0), (4, 256, 1, 0), (9, 2048, 1, 0), (5, 256, 0, 0),
-                                          (300, 512, 0, 1), (70, 96 * 8, 0, 2)])
+                                          (300, 512, 0, 1), (70, 96 * 8, 0, 2), (5, 3072, 1, 0), (100, 4096, 0, 1),
+                                          (64, 7168, 0, 2)])
 def test_quantize_rows_strided_bit_exact(R, C, act, mode):
     """Rows read 2C elements apart out of one [R, 2C] buffer (a | b, the
     gated FFN's fused input-projection output): the same bits as the
