@@ -38,6 +38,58 @@ __device__ __forceinline__ void load_vals(const uint16_t* __restrict__ x, const 
   }
 }
 
+// The raw 16-byte chunks lane + LPR * c of a row (x, and x_up for SiLU*mul),
+// all loads issued before any is used; chunks past the row's end re-read its
+// last chunk and are ignored by the caller.
+template <int CPL, int ACT, int LPR>
+__device__ __forceinline__ void load_row_share(const uint16_t* __restrict__ x, const uint16_t* __restrict__ xu,
+                                               int64_t xbase, int64_t nchunks, int lane, Bf16x8 (&ra)[CPL],
+                                               Bf16x8 (&rb)[CPL]) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int64_t ch = lane + LPR * c;
+    const int64_t cl = ch < nchunks ? ch : nchunks - 1;
+    ra[c].raw = *reinterpret_cast<const uint4*>(x + xbase + cl * 8);
+    if constexpr (ACT == MOE_ACT_SILU_MUL) rb[c].raw = *reinterpret_cast<const uint4*>(xu + xbase + cl * 8);
+  }
+}
+
+// Absolute maximum of one chunk's values; for SiLU*mul the values
+// h = silu(a) * b are formed here and kept in h.
+template <int ACT>
+__device__ __forceinline__ float chunk_absmax(const Bf16x8& a, const Bf16x8& b, float (&h)[8]) {
+  float m = 0.0f;
+  if constexpr (ACT == MOE_ACT_SILU_MUL) {
+    float av[8], bv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      av[i] = a.get(i);
+      bv[i] = b.get(i);
+    }
+    silu_mul8(av, bv, h);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(h[i]));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(a.get(i)));
+  }
+  return m;
+}
+
+// The e4m3fn codes of one chunk (from h for SiLU*mul, else from the bf16 words).
+template <int ACT>
+__device__ __forceinline__ void store_chunk(uint8_t* __restrict__ q, int64_t off, const Bf16x8& a, const float (&h)[8],
+                                            const RowDiv& div) {
+  if constexpr (ACT == MOE_ACT_SILU_MUL) {
+    store_codes(q, off, h, div);
+  } else {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = a.get(i);
+    store_codes(q, off, v, div);
+  }
+}
+
 // MODE_ROW: compute each row's scale; MODE_GIVEN: use *given_scale (tensor
 // modes; computed by the first pass for the dynamic one).
 constexpr int MODE_ROW = 0;
@@ -64,15 +116,15 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   const int64_t base = row * C, xbase = row * ldx;
   float amax = 0.0f;
   if constexpr (CPL > 0) {
-    float v[CPL][8];
+    // every load of the lane's share first (chunk index clamped into the
+    // row), so one memory latency covers the whole share; the bf16 words
+    // stay packed until used (the SiLU values are kept as float32)
+    Bf16x8 ra[CPL], rb[CPL];
+    load_row_share<CPL, ACT, LPR>(x, xu, xbase, nchunks, lane, ra, rb);
+    float h[ACT == MOE_ACT_SILU_MUL ? CPL : 1][8];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int64_t ch = lane + LPR * c;
-      if (ch < nchunks) {
-        load_vals<ACT>(x, xu, xbase + ch * 8, v[c]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
-      }
+      if (lane + LPR * c < nchunks) amax = fmaxf(amax, chunk_absmax<ACT>(ra[c], rb[c], h[ACT == MOE_ACT_SILU_MUL ? c : 0]));
     }
     amax = row_max<LPR>(amax);
     const float s = (MODE == MODE_ROW) ? scale_from_amax(amax) : *given_scale;
@@ -80,7 +132,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int64_t ch = lane + LPR * c;
-      if (ch < nchunks) store_codes(q, base + ch * 8, v[c], div);
+      if (ch < nchunks) store_chunk<ACT>(q, base + ch * 8, ra[c], h[ACT == MOE_ACT_SILU_MUL ? c : 0], div);
     }
     if (lane == 0) {
       if (MODE == MODE_ROW) scale[row] = s;
@@ -124,16 +176,13 @@ __global__ __launch_bounds__(256) void quantize_row_wg_kernel(
   const int64_t row = blockIdx.x;
   const int64_t nchunks = C >> 3;
   const int64_t base = row * C, xbase = row * ldx;
-  float v[CPL][8];
+  Bf16x8 ra[CPL], rb[CPL];
+  load_row_share<CPL, ACT, 256>(x, xu, xbase, nchunks, tid, ra, rb);
+  float h[ACT == MOE_ACT_SILU_MUL ? CPL : 1][8];
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int64_t ch = tid + 256 * c;
-    if (ch < nchunks) {
-      load_vals<ACT>(x, xu, xbase + ch * 8, v[c]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
-    }
+    if (tid + 256 * c < nchunks) amax = fmaxf(amax, chunk_absmax<ACT>(ra[c], rb[c], h[ACT == MOE_ACT_SILU_MUL ? c : 0]));
   }
   amax = wave_max(amax);
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
@@ -144,7 +193,7 @@ __global__ __launch_bounds__(256) void quantize_row_wg_kernel(
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int64_t ch = tid + 256 * c;
-    if (ch < nchunks) store_codes(q, base + ch * 8, v[c], div);
+    if (ch < nchunks) store_chunk<ACT>(q, base + ch * 8, ra[c], h[ACT == MOE_ACT_SILU_MUL ? c : 0], div);
   }
   if (tid == 0) {
     if (MODE == MODE_ROW) scale[row] = s;

@@ -346,12 +346,24 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* _
   const int64_t G = H >> 4;
   if (static_mode && tok_scale && wid == 0 && lane == 0) tok_scale[0] = static_scale;
   for (int64_t t = wid; t < T; t += nw) {
+    const uint16_t* row = x + t * H;
+    // the row's groups (index clamped into the row) are loaded together
+    // with the token's destinations: one memory latency, not one per load
+    Bf16x8 ra[GPL > 0 ? GPL : 1][2];
+    if constexpr (GPL > 0) {
+#pragma unroll
+      for (int c = 0; c < GPL; ++c) {
+        const int64_t gi = lane + 64 * c;
+        const int64_t gl = gi < G ? gi : G - 1;
+        ra[c][0].raw = *reinterpret_cast<const uint4*>(row + gl * 16);
+        ra[c][1].raw = *reinterpret_cast<const uint4*>(row + gl * 16 + 8);
+      }
+    }
     int my_r = -1;
     if (lane < k) my_r = inv_pos[t * k + lane];
     if (my_r >= M_cap) my_r = -1;
     const uint64_t m = __ballot(my_r >= 0);
     if (m == 0 && !(tok_scale && !static_mode)) continue;
-    const uint16_t* row = x + t * H;
     float amax = 0.0f;
     if constexpr (GPL > 0) {
       float v[GPL][16];
@@ -359,7 +371,11 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* _
       for (int c = 0; c < GPL; ++c) {
         const int64_t gi = lane + 64 * c;
         if (gi < G) {
-          load_group16<GPL>(row, gi, v[c]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            v[c][i] = ra[c][0].get(i);
+            v[c][8 + i] = ra[c][1].get(i);
+          }
 #pragma unroll
           for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
         }
