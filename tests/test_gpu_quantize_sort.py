@@ -288,6 +288,23 @@ def test_sort_edge_cases(T, k, E, g0, El, extra):
     _check_sort(g, o)
 
 
+@pytest.mark.parametrize("H", [16, 1040, 3088, 8192, 8208])
+def test_sort_row_widths(H):
+    """Rows of 1 .. 9 16-byte segments per lane (the register-staged scatter and
+    its loop fallback past 8192 bytes), a local slice and spare capacity."""
+    rng = np.random.default_rng(H)
+    T, k, E, g0, El = 300, 4, 16, 4, 8
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    xq = rng.integers(0, 256, (T, H)).astype(np.uint8)
+    xsc = rng.uniform(0.1, 1.0, T).astype(np.float32)
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc)
+    m_cap = o["n"] + 40
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc, m_cap=m_cap)
+    print(f"sort H={H} n={o['n']} m_cap={m_cap}", flush=True)
+    g = gpu_sort(ids, E, g0, El, xq, xsc, m.MOE_SCALE_ROW_DYNAMIC, m_cap)
+    _check_sort(g, o)
+
+
 def test_sort_tensor_scale_and_metadata_only():
     rng = np.random.default_rng(9)
     ids = rng.integers(0, 6, (50, 2)).astype(np.int32)
