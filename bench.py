@@ -314,6 +314,47 @@ def secondary_ep_slice(steps, warmup):
     return res
 
 
+def secondary_up_proj(cid, static, steps, warmup):
+    """An up-projection workload (quantize and sort in one pass, one grouped
+    matmul, gather-reduce): configs 1 and 3 at their real, launch-bound
+    shapes, and config 6 -- config 3's Zipf-skewed routing with empty experts
+    and [E, K/128, 1, N] weight scales at the expert slice's matmul shape
+    (8192 routed rows, K=7168, N=2048, 32 experts)."""
+    from moe_fp8_grouped_amd.pipeline import ForwardPath
+    from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate
+
+    cfg = CONFIGS[cid]
+    data = generate(cfg)
+    ids = data["ids"]
+    gs = np.bincount(ids.ravel(), minlength=cfg.E)
+    n, U = int(ids.size), int(len(ids))
+    path = ForwardPath(cfg, data, static_act=STATIC_ACT_SCALE if static else None,
+                       static_weight=STATIC_WEIGHT_SCALE if static else None)
+    path.nonempty_local = int((gs > 0).sum())
+    del data
+    acc = step_accounting(path, n, U)
+    g = acc["gmm"][0]
+    calls = [("quantize_sort", path.sort), ("gmm_w_up", path.experts), ("gather_reduce", path.combine)]
+    t, ms_eager = _time_calls(calls, steps, warmup)
+    kern = {nm: _kern_entry(us, us_min, g["bytes"] if nm == "gmm_w_up" else acc[nm]["bytes"],
+                            g["flops"] if nm == "gmm_w_up" else 0) for nm, (us, us_min) in t.items()}
+    path.capture_graph(warmup=1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        path.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    res = {"workload": f"{cfg.name}{' static scales' if static else ''}: T={cfg.T} H={cfg.H} E={cfg.E} "
+                       f"top-{cfg.k} N={cfg.I}" + (", [E, K/128, 1, N] weight scales" if cfg.weight_block_k else ""),
+           "routed_rows": n, "empty_experts": int((gs == 0).sum()), "largest_group": int(gs.max()),
+           "ms_per_step": round(ms, 4), "ms_per_step_eager": round(ms_eager, 4),
+           "gmm_TFLOP_s_whole_step": round(g["flops"] / (ms * 1e-3) / 1e12, 1), "kernels": kern}
+    del path
+    torch.cuda.empty_cache()
+    return res
+
+
 def secondary_backward(steps, warmup):
     """Config 5: the backward of an up projection (T=8192 H=4096 E=64 top-4
     I=1536, static scales): dX = gmm(dY, W^T) and dW = tgmm(X_sorted, dY)."""
@@ -392,7 +433,12 @@ def main():
     if not a.no_secondary:
         torch.cuda.empty_cache()
         res["secondary"] = {"ep_slice_forward": secondary_ep_slice(min(a.steps, 10), 2),
-                            "backward": secondary_backward(min(a.steps, 10), 2)}
+                            "backward": secondary_backward(min(a.steps, 10), 2),
+                            "tiny_up_proj": secondary_up_proj(1, False, a.steps, a.warmup),
+                            "tiny_zipf_blockwise": secondary_up_proj(3, False, a.steps, a.warmup),
+                            "tiny_zipf_blockwise_static": secondary_up_proj(3, True, a.steps, a.warmup),
+                            "skewed_large_blockwise": secondary_up_proj(6, False, min(a.steps, 10), 2),
+                            "skewed_large_blockwise_static": secondary_up_proj(6, True, min(a.steps, 10), 2)}
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, a.cpu_tokens)
     print(json.dumps(res), flush=True)

@@ -130,6 +130,18 @@ def test_gmm_config4_expert_slice_sampled():
              "config 4 wi_0")
 
 
+@pytest.mark.parametrize("static", [False, True])
+def test_gmm_skewed_large_blockwise_sampled(static):
+    """Config 3's skewed routing and [E, K/128, 1, N] scales at the large
+    matmul shape (8192 rows, K=7168, N=2048, 32 experts, 17 of them empty)."""
+    cfg, srt, wq, ws_, mode = _config_stage(6, static=static)
+    assert ws_.shape == (32, 56, 1, 2048)
+    gs = srt["group_sizes"]
+    assert (gs == 0).sum() >= 2 and gs.max() >= 512 and (gs[gs > 0] < 128).any()
+    _sampled(srt["xs"], srt["ss"], mode, wq, ws_, gs, cfg.E, 0, cfg.E, 1, 6000, 6 + static,
+             "skewed large" + (" static" if static else ""))
+
+
 def test_gmm_config5_input_gradient_sampled():
     cfg = CONFIGS[5]
     d = generate(cfg, with_weights=["w_up"])

@@ -21,6 +21,13 @@ configurations stand in for them:
 5. MoE backward: T=8192, H=4096, E=64, top-4, I=1536, uniform routing,
    dY ~ N(0, 1e-3) in sorted-row space, static activation/weight scales.
 
+A sixth, derived workload carries config 3's structure to the large-matmul
+shapes of config 4, so the ragged tile scheduler is measured where matrix-core
+rate means something: T=1024 tokens, H=7168, E=32 experts (all local), top-8
+(8192 routed rows, as config 4's local slice), N=2048, the same Zipf-skewed
+routing (15 experts receive 2..1024 rows, 17 receive none), [E, K/128, 1, N]
+weight scales, and the static-scale variant.
+
 Generator: every tensor has its own stream, ``numpy.random.default_rng([1000
 + c, s])`` with s = 0 routing (logits, then the Zipf rank permutation), 1
 activations x, 2 outlier rows, 3 dY, 10 + i the i-th weight (wi_0, wi_1, wo,
@@ -100,6 +107,8 @@ CONFIGS = {
                  outlier_frac=0.01, outlier_mult=50.0),
     5: MoEConfig(5, "moe-bwd", T=8192, H=4096, E=64, k=4, I=1536, pipeline="bwd",
                  routing="uniform", static=True),
+    6: MoEConfig(6, "skewed-up-proj-large", T=1024, H=7168, E=32, k=8, I=2048, pipeline="up",
+                 routing="zipf", weight_block_k=128),
 }
 
 
