@@ -39,11 +39,11 @@ from .quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STA
                        pinned_exp_f32, quantize_rows, quantize_weights, silu_mul_f32)
 from .sort import sort_by_expert
 from .gmm import gmm, tgmm
-from .gather_reduce import gather_reduce
+from .gather_reduce import gather_reduce, gather_reduce_backward
 
 __all__ = [
     "E4M3_MAX", "bf16_decode", "bf16_rne_from_f32", "bf16_rne_from_f64", "e4m3_decode",
     "e4m3_rne", "SCALE_ROW_DYNAMIC", "SCALE_TENSOR_DYNAMIC", "SCALE_TENSOR_STATIC",
     "pinned_exp_f32", "quantize_rows", "quantize_weights", "silu_mul_f32",
-    "sort_by_expert", "gmm", "tgmm", "gather_reduce",
+    "sort_by_expert", "gmm", "tgmm", "gather_reduce", "gather_reduce_backward",
 ]
