@@ -210,7 +210,10 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
         tf = gmm_flops / (gmm_us * 1e-6) / 1e12
         roof.update({"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4)})
-    sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "quantize_sort", "gather_reduce") if nm in kern}
+    if cfg.pipeline == "ffn":
+        kern["gather_reduce_backward"] = combine_backward(path, n, steps, warmup)
+    sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "quantize_sort", "gather_reduce",
+                                                   "gather_reduce_backward") if nm in kern}
     value = gmm_flops / (ms_step * 1e-3) / 1e12
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
@@ -230,6 +233,25 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
         "device": torch.cuda.get_device_name(0),
     }
     return res, cfg
+
+
+def combine_backward(path, n, steps, warmup):
+    """The combine's backward on the step's own expert outputs: dy = w * dout
+    to the sorted rows, dw = dout . y per slot (a synthetic bf16 dout)."""
+    import moe_fp8_grouped_amd as m
+    cfg = path.cfg
+    T, k, N, M_cap = cfg.T, cfg.k, path.N_out, path.m_cap
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    dout = (torch.randn((T, N), generator=g, device="cuda") * 1e-2).to(torch.bfloat16)
+    dy = torch.empty((M_cap, N), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    call = lambda: m.moe_gather_reduce_backward(dout, path.y, path.inv_pos, path.topk_w, T, k, N, path.group_sizes,
+                                                cfg.E, cfg.group_offset, cfg.E_loc, M_cap, dy, dw)
+    t, _ = _time_calls([("b", call)], steps, warmup)
+    us, us_min = t["b"]
+    nbytes = T * N * 2 + n * N * 2 + M_cap * N * 2 + T * k * 12
+    return {"avg_us": round(us, 2), "min_us": round(us_min, 2), "alg_bytes": int(nbytes),
+            "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def _time_calls(calls, steps, warmup):

@@ -287,6 +287,33 @@ int moe_gather_reduce(const void* y, int y_dtype, const int32_t* inv_pos, const 
                       int64_t T, int32_t k, int64_t N, int out_dtype, void* out, void* stream);
 
 /*
+ * moe_gather_reduce_backward -- the backward of moe_gather_reduce, for the
+ * layer backward that "Support quantization for tokamax gmm v2" splits into
+ * gmm / tgmm calls ("What this does"; its accuracy tables compare gradients
+ * as well as outputs).  With out[t] = sum_j w[t, j] * y[inv_pos[t, j]]:
+ *   dy[inv_pos[t, j], :] = bf16(w[t, j] * dout[t, :])   (one float32
+ *                           product, rounded to nearest even)
+ *   dw[t, j]             = sum_c dout[t, c] * y[inv_pos[t, j], c]  (float32)
+ * for every slot whose inverse position is in [0, M_cap); other slots get
+ * dw = 0.  Rows [n, M_cap) of dy are zero, n = sum of
+ * group_sizes[group_offset .. group_offset + num_local_experts).
+ *
+ *   dout     [T, N] bf16, the gradient of the combined token rows.
+ *   y        [M_cap, N] bf16, the expert outputs the forward combined.
+ *   inv_pos  [T, k] int32 and group_sizes [E] int32, from moe_sort_by_expert
+ *            (every local row is the image of exactly one slot).
+ *   topk_weights [T, k] f32.
+ *   dy       [M_cap, N] bf16 out; dw [T, k] f32 out.
+ * N a multiple of 8, k <= 64.  Needs no workspace.  Errors: MOE_ERR_SHAPE,
+ * MOE_ERR_NULL; T = 0 with M_cap = 0 returns MOE_OK.
+ */
+int moe_gather_reduce_backward(const void* dout, const void* y, const int32_t* inv_pos,
+                               const float* topk_weights, int64_t T, int32_t k, int64_t N,
+                               const int32_t* group_sizes, int32_t E, int32_t group_offset,
+                               int32_t num_local_experts, int64_t M_cap, void* dy, float* dw,
+                               void* stream);
+
+/*
  * moe_workspace_bytes -- workspace size (host out `bytes`) for `op` with
  * problem sizes d0, d1, d2 and E:
  *   MOE_OP_QUANTIZE_ROWS   d0 = R, d1 = C, d2 = scale_mode

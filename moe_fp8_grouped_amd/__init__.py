@@ -42,6 +42,8 @@ SIGNATURES = {
     "moe_tgmm_fp8": (_I, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                           ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_gather_reduce": (_I, [_P, _I, _P, _P, _I64, ctypes.c_int32, _I64, _I, _P, _P]),
+    "moe_gather_reduce_backward": (_I, [_P, _P, _P, _P, _I64, ctypes.c_int32, _I64, _P, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, _I64, _P, _P, _P]),
     "moe_workspace_bytes": (_I, [_I, _I64, _I64, _I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_debug_check": (_I, [_P, _P, ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -184,6 +186,12 @@ def moe_tgmm_fp8(lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, g
 def moe_gather_reduce(y, y_dtype, inv_pos, topk_weights, T, k, N, out_dtype, out, stream=None):
     return _call("moe_gather_reduce", _ptr(y), y_dtype, _ptr(inv_pos), _ptr(topk_weights), T, k, N, out_dtype,
                  _ptr(out), _stream(stream))
+
+
+def moe_gather_reduce_backward(dout, y, inv_pos, topk_weights, T, k, N, group_sizes, E, group_offset,
+                               num_local_experts, M_cap, dy, dw, stream=None):
+    return _call("moe_gather_reduce_backward", _ptr(dout), _ptr(y), _ptr(inv_pos), _ptr(topk_weights), T, k, N,
+                 _ptr(group_sizes), E, group_offset, num_local_experts, M_cap, _ptr(dy), _ptr(dw), _stream(stream))
 
 
 def moe_debug_check(ws, stream=None):

@@ -162,6 +162,87 @@ __global__ __launch_bounds__(256) void gather_reduce_kernel(const void* __restri
   }
 }
 
+// ---------------------------------------------------------------- backward
+// One 16-byte chunk of the backward: dy = bf16(w * d) for its eight values
+// (one float32 product, one rounding) and the chunk's share of dout . y as an
+// FMA chain.
+__device__ __forceinline__ float bwd_chunk(const uint4 d, const uint4 yv, float w, uint4& out) {
+  const uint32_t dd[4] = {d.x, d.y, d.z, d.w}, yy[4] = {yv.x, yv.y, yv.z, yv.w};
+  uint32_t o[4];
+  float p = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float d0 = __uint_as_float(dd[i] << 16), d1 = __uint_as_float(dd[i] & 0xffff0000u);
+    const float y0 = __uint_as_float(yy[i] << 16), y1 = __uint_as_float(yy[i] & 0xffff0000u);
+    p = fmaf(d0, y0, p);
+    p = fmaf(d1, y1, p);
+    o[i] = f32_to_bf16(w * d0) | (static_cast<uint32_t>(f32_to_bf16(w * d1)) << 16);
+  }
+  out = make_uint4(o[0], o[1], o[2], o[3]);
+  return p;
+}
+
+// The combine's backward, one wave per routed slot f = t*k + j: the token's
+// upstream-gradient row and the slot's expert-output row are loaded together
+// (CPL 16-byte chunks per lane, index clamped into the row; CPL = 0 streams
+// longer rows), dy[r] = bf16(w * dout[t]) is written to the slot's sorted row
+// r, and dw[f] = dout[t] . y[r] is summed in float32 -- eight-term FMA chains
+// per chunk, the chunks of a lane, then a wave tree: at most
+// (8 + chunks per lane + 6) float32 roundings deep.  A token's k waves are
+// neighbours, so its dout row comes from HBM once.  Slots without a local row
+// get dw = 0; extra waves zero dy's rows [n, M_cap), n = the local rows.
+template <int CPL>
+__global__ __launch_bounds__(256) void gather_reduce_bwd_kernel(
+    const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y, const int32_t* __restrict__ inv,
+    const float* __restrict__ wts, int64_t S, int k, int64_t N, int64_t M_cap, const int32_t* __restrict__ gs,
+    int g0, int El, uint16_t* __restrict__ dy, float* __restrict__ dw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t nch = N >> 3;
+  for (int64_t f = wid; f < S; f += nw) {
+    int r = inv[f];
+    const float w = wts[f];
+    if (r >= M_cap) r = -1;
+    if (r < 0) {
+      if (lane == 0) dw[f] = 0.0f;
+      continue;
+    }
+    const uint4* drow = reinterpret_cast<const uint4*>(dout + (f / k) * N);
+    const uint4* yrow = reinterpret_cast<const uint4*>(y + static_cast<int64_t>(r) * N);
+    uint4* dyrow = reinterpret_cast<uint4*>(dy + static_cast<int64_t>(r) * N);
+    float part = 0.0f;
+    if constexpr (CPL > 0) {
+      uint4 dv[CPL], yv[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int64_t ch = lane + 64 * c;
+        const int64_t cl = ch < nch ? ch : nch - 1;
+        dv[c] = drow[cl];
+        yv[c] = yrow[cl];
+      }
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int64_t ch = lane + 64 * c;
+        if (ch < nch) part += bwd_chunk(dv[c], yv[c], w, dyrow[ch]);
+      }
+    } else {
+      for (int64_t ch = lane; ch < nch; ch += 64) part += bwd_chunk(drow[ch], yrow[ch], w, dyrow[ch]);
+    }
+    part = wave_sum(part);
+    if (lane == 0) dw[f] = part;
+  }
+  // rows [n, M_cap) of dy are zero (n from the local group sizes; negative ones count as 0)
+  int own = 0;
+  for (int g = lane; g < El; g += 64) own += max(gs[g0 + g], 0);
+  int64_t n = wave_sum_int(own);
+  if (n > M_cap) n = M_cap;
+  for (int64_t r = n + wid; r < M_cap; r += nw) {
+    uint4* row = reinterpret_cast<uint4*>(dy + r * N);
+    for (int64_t ch = lane; ch < nch; ch += 64) row[ch] = make_uint4(0, 0, 0, 0);
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -187,6 +268,43 @@ extern "C" int moe_gather_reduce(const void* y, int y_dtype, const int32_t* inv_
   else
     k <= 8 ? moe::gather_reduce_k8_kernel<0, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out)
            : moe::gather_reduce_kernel<0, 0><<<grid, block, 0, st>>>(y, inv_pos, topk_weights, T, k, N, out);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_gather_reduce_backward(const void* dout, const void* y, const int32_t* inv_pos,
+                                          const float* topk_weights, int64_t T, int32_t k, int64_t N,
+                                          const int32_t* group_sizes, int32_t E, int32_t group_offset,
+                                          int32_t num_local_experts, int64_t M_cap, void* dy, float* dw,
+                                          void* stream) {
+  if (T < 0 || k <= 0 || k > 64 || N <= 0 || N % 8 || M_cap < 0) return MOE_ERR_SHAPE;
+  if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E)
+    return MOE_ERR_SHAPE;
+  if (T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (T == 0 && M_cap == 0) return MOE_OK;
+  if (!group_sizes) return MOE_ERR_NULL;
+  if (T > 0 && (!dout || !inv_pos || !topk_weights || !dw)) return MOE_ERR_NULL;
+  if (M_cap > 0 && (!y || !dy)) return MOE_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t S = T * k;
+  int64_t waves = S > M_cap / 4 ? S : M_cap / 4;
+  if (waves < 4) waves = 4;
+  if (waves > 262144) waves = 262144;
+  const unsigned grid = static_cast<unsigned>(moe_cdiv(waves, 4));
+  const int64_t cpl = moe_cdiv(N / 8, 64);
+  const uint16_t* d = static_cast<const uint16_t*>(dout);
+  const uint16_t* yy = static_cast<const uint16_t*>(y);
+  uint16_t* o = static_cast<uint16_t*>(dy);
+#define MOE_GRB(CPL)                                                                                          \
+  moe::gather_reduce_bwd_kernel<CPL><<<grid, 256, 0, st>>>(d, yy, inv_pos, topk_weights, S, k, N, M_cap,      \
+                                                             group_sizes, group_offset, num_local_experts, o, dw)
+  if (cpl <= 1) MOE_GRB(1);
+  else if (cpl <= 2) MOE_GRB(2);
+  else if (cpl <= 4) MOE_GRB(4);
+  else if (cpl <= 8) MOE_GRB(8);
+  else if (cpl <= 16) MOE_GRB(16);
+  else MOE_GRB(0);
+#undef MOE_GRB
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

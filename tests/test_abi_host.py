@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_path_calls():
     names = _declared_functions()
     for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
-               "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
+               "moe_gather_reduce_backward", "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
                "moe_version"]:
         assert fn in names
 
@@ -167,6 +167,20 @@ def test_tgmm_and_gather_reduce_validation(lib):
     assert g(one, 0, one, one, 4, 0, 16, 0, one, None) == m.MOE_ERR_SHAPE
     assert g(None, 0, one, one, 4, 2, 16, 0, one, None) == m.MOE_ERR_NULL
     assert g(None, 0, None, None, 0, 2, 16, 0, None, None) == m.MOE_OK             # T = 0
+
+
+def test_gather_reduce_backward_validation(lib):
+    b = lambda *a: _c(lib, "moe_gather_reduce_backward", *a)
+    one = 1
+    # dout, y, inv_pos, w, T, k, N, group_sizes, E, g0, El, M_cap, dy, dw, stream
+    assert b(one, one, one, one, 4, 2, 12, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_SHAPE     # N % 8
+    assert b(one, one, one, one, 4, 0, 16, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_SHAPE     # k = 0
+    assert b(one, one, one, one, 4, 2, 16, one, 8, 4, 8, 8, one, one, None) == m.MOE_ERR_SHAPE     # window > E
+    assert b(one, one, one, one, 4, 2, 16, one, 8, 0, 8, -1, one, one, None) == m.MOE_ERR_SHAPE    # M_cap < 0
+    assert b(None, one, one, one, 4, 2, 16, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
+    assert b(one, one, one, one, 4, 2, 16, None, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
+    assert b(one, None, one, one, 4, 2, 16, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
+    assert b(None, None, None, None, 0, 2, 16, None, 8, 0, 8, 0, None, None, None) == m.MOE_OK  # nothing to do
 
 
 def test_weight_quantizer_validation(lib):

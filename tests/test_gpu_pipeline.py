@@ -8,7 +8,7 @@ import torch
 
 import moe_fp8_grouped_amd as m
 from moe_fp8_grouped_amd.pipeline import BackwardPath, ForwardPath
-from oracle.gather_reduce import gather_reduce
+from oracle.gather_reduce import gather_reduce, gather_reduce_backward
 from oracle.gmm import gmm, tgmm
 from oracle.pipeline import dense_bf16_reference, rel_norm_diff
 from oracle.quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STATIC, quantize_rows,
@@ -64,6 +64,41 @@ def test_gather_reduce_k1_is_exact_unsort():
     y = to_bf16_bits(rng.standard_normal((T, N)).astype(np.float32))
     g = gpu_gather_reduce(y, True, srt["inv_pos"].reshape(T, 1), np.ones((T, 1), np.float32))
     assert_bits_equal(g, y[srt["inv_pos"]], "k=1 unsort")
+
+
+def gpu_gather_reduce_backward(dout, y, inv, w, gs, E, g0, El, m_cap):
+    T, k = inv.shape
+    N = dout.shape[1]
+    dy = torch.full((m_cap, N), 9.0, dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((T, k), 7.0, dtype=torch.float32, device="cuda")
+    print(f"gather_reduce_backward T={T} k={k} N={N} E={E} g0={g0} El={El} m_cap={m_cap}", flush=True)
+    m.moe_gather_reduce_backward(dev_bf16(dout), dev_bf16(y), dev_i32(inv), dev_f32(w), T, k, N, dev_i32(gs), E, g0,
+                                 El, m_cap, dy, dw)
+    torch.cuda.synchronize()
+    return host(dy), host(dw)
+
+
+@pytest.mark.parametrize("T,k,E,g0,El,N,extra", [(256, 2, 8, 0, 8, 1024, 0), (4096, 8, 64, 0, 64, 2048, 0),
+                                                 (600, 8, 256, 64, 32, 7168, 40), (33, 3, 5, 1, 2, 8, 5),
+                                                 (90, 4, 16, 0, 16, 520, 0), (40, 2, 4, 0, 4, 16384, 3)])
+def test_gather_reduce_backward(T, k, E, g0, El, N, extra):
+    """dy bit-exact (one float32 product, one bf16 rounding), dw under the
+    float32 rule; rows past the local ones zero; non-local slots dw = 0."""
+    rng = np.random.default_rng(T + N + k)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    srt = sort_by_expert(ids, E, g0, El)
+    inv = srt["inv_pos"].reshape(T, k)
+    n = int(srt["n"])
+    m_cap = n + extra
+    y = to_bf16_bits(rng.standard_normal((max(m_cap, 1), N)).astype(np.float32))[:m_cap]
+    dout = to_bf16_bits((rng.standard_normal((T, N)) * 1e-2).astype(np.float32))
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    o = gather_reduce_backward(dout, y, inv, w, m_cap, n)
+    gdy, gdw = gpu_gather_reduce_backward(dout, y, inv, w, srt["group_sizes"], E, g0, El, m_cap)
+    assert_bits_equal(gdy, o["dy"], "dy")
+    st = check_f32(gdw, o["dw64"], o["dw_abs"], 0.0, "dw")
+    assert (gdw[inv < 0] == 0).all()
+    print("dw", st)
 
 
 # ------------------------------------------------------------------ pipelines
