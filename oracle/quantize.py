@@ -32,7 +32,7 @@ Readings where the pages are silent (each is listed in the design notes):
 
 import numpy as np
 
-from .codec import E4M3_MAX, bf16_decode, e4m3_rne
+from .codec import E4M3_MAX, bf16_decode, bf16_rne_from_f32, e4m3_rne
 
 SCALE_ROW_DYNAMIC = 0
 SCALE_TENSOR_DYNAMIC = 1
@@ -107,6 +107,41 @@ def silu_mul_f32(a, b) -> np.ndarray:
     den = (np.float32(1.0) + pinned_exp_f32(-a)).astype(np.float32)
     silu = (a / den).astype(np.float32)
     return (silu * b).astype(np.float32)
+
+
+def silu_mul_backward_f32(a, b, dh):
+    """Gradients of h = silu(a) * b for an upstream gradient dh (float32 arrays
+    of decoded bf16 values), by a pinned float32 recipe, one rounding per step
+    and no fused multiply-add:
+
+      den = 1 + e(-a)     (the pinned exp, as in the forward)
+      s   = 1 / den       (the logistic sigmoid of a)
+      q   = a / den       (silu(a), the forward's quotient)
+      db  = dh * q
+      da  = (dh * b) * (s * (1 + a * (1 - s)))
+
+    The pages do not discuss the activation (a gated FFN is the plain reading
+    of the gated layer); the derivative is silu'(a) = s * (1 + a * (1 - s)).
+    Returns (da, db) float32.
+    """
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    dh = np.asarray(dh, dtype=np.float32)
+    one = np.float32(1.0)
+    den = (one + pinned_exp_f32(-a)).astype(np.float32)
+    s = (one / den).astype(np.float32)
+    q = (a / den).astype(np.float32)
+    db = (dh * q).astype(np.float32)
+    ds = (s * (one + (a * (one - s).astype(np.float32)).astype(np.float32)).astype(np.float32)).astype(np.float32)
+    da = ((dh * b).astype(np.float32) * ds).astype(np.float32)
+    return da, db
+
+
+def silu_mul_backward(a_bits, b_bits, dh_bits):
+    """silu_mul_backward_f32 on bf16 bit patterns; (da, db) as bf16 bit
+    patterns, each rounded once to nearest even from float32."""
+    da, db = silu_mul_backward_f32(bf16_decode(a_bits), bf16_decode(b_bits), bf16_decode(dh_bits))
+    return bf16_rne_from_f32(da), bf16_rne_from_f32(db)
 
 
 def quantize_rows(x_bits, mode, static_scale=None, x_up_bits=None):
