@@ -212,6 +212,7 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4)})
     if cfg.pipeline == "ffn":
         kern["gather_reduce_backward"] = combine_backward(path, n, steps, warmup)
+        kern["silu_mul_backward"] = silu_backward(path, steps, warmup)
     sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "quantize_sort", "gather_reduce",
                                                    "gather_reduce_backward") if nm in kern}
     value = gmm_flops / (ms_step * 1e-3) / 1e12
@@ -250,6 +251,24 @@ def combine_backward(path, n, steps, warmup):
     t, _ = _time_calls([("b", call)], steps, warmup)
     us, us_min = t["b"]
     nbytes = T * N * 2 + n * N * 2 + M_cap * N * 2 + T * k * 12
+    return {"avg_us": round(us, 2), "min_us": round(us_min, 2), "alg_bytes": int(nbytes),
+            "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def silu_backward(path, steps, warmup):
+    """The activation's backward on the step's own gate / up values (the
+    halves of the fused input-projection output) and a synthetic bf16 dh;
+    da and db go to the halves of one [M, 2I] buffer."""
+    import moe_fp8_grouped_amd as m
+    R, I = path.m_cap, path.cfg.I
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    dh = (torch.randn((R, I), generator=g, device="cuda") * 1e-2).to(torch.bfloat16)
+    dab = torch.empty((R, 2 * I), dtype=torch.bfloat16, device="cuda")
+    call = lambda: m.moe_silu_mul_backward(path.ab[:, :I], path.ab[:, I:], 2 * I, dh, R, I, dab[:, :I], dab[:, I:],
+                                           2 * I)
+    t, _ = _time_calls([("b", call)], steps, warmup)
+    us, us_min = t["b"]
+    nbytes = R * I * 10
     return {"avg_us": round(us, 2), "min_us": round(us_min, 2), "alg_bytes": int(nbytes),
             "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
 

@@ -314,6 +314,28 @@ int moe_gather_reduce_backward(const void* dout, const void* y, const int32_t* i
                                void* stream);
 
 /*
+ * moe_silu_mul_backward -- gradients of the gated FFN's activation
+ * h = silu(a) * b for an upstream gradient dh, the activation step of the
+ * layer backward that "Support quantization for tokamax gmm v2" splits into
+ * gmm / tgmm calls ("What this does").  A pinned float32 recipe, one
+ * rounding per step, no fused multiply-add:
+ *   den = 1 + e(-a) (the forward's pinned exp), s = 1 / den, q = a / den,
+ *   db = dh * q,  da = (dh * b) * (s * (1 + a * (1 - s)))
+ * each result rounded to bf16 (nearest even).
+ *
+ *   a, b     [R, C] bf16 with row stride lda elements (e.g. the two column
+ *            halves of the fused input-projection output, lda = 2C).
+ *   dh       [R, C] bf16, dense.
+ *   da, db   [R, C] bf16 out with row stride ldo (e.g. the halves of one
+ *            [R, 2C] buffer that the input-gradient gmm over [W0 | W1]^T
+ *            reads as its lhs).
+ * C, lda, ldo multiples of 8, lda >= C, ldo >= C.  Needs no workspace.
+ * Errors: MOE_ERR_SHAPE, MOE_ERR_NULL; R = 0 returns MOE_OK.
+ */
+int moe_silu_mul_backward(const void* a, const void* b, int64_t lda, const void* dh, int64_t R, int64_t C,
+                          void* da, void* db, int64_t ldo, void* stream);
+
+/*
  * moe_workspace_bytes -- workspace size (host out `bytes`) for `op` with
  * problem sizes d0, d1, d2 and E:
  *   MOE_OP_QUANTIZE_ROWS   d0 = R, d1 = C, d2 = scale_mode

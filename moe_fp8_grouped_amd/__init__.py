@@ -44,6 +44,7 @@ SIGNATURES = {
     "moe_gather_reduce": (_I, [_P, _I, _P, _P, _I64, ctypes.c_int32, _I64, _I, _P, _P]),
     "moe_gather_reduce_backward": (_I, [_P, _P, _P, _P, _I64, ctypes.c_int32, _I64, _P, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, _I64, _P, _P, _P]),
+    "moe_silu_mul_backward": (_I, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I64, _P]),
     "moe_workspace_bytes": (_I, [_I, _I64, _I64, _I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_debug_check": (_I, [_P, _P, ctypes.POINTER(ctypes.c_int32)]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -192,6 +193,12 @@ def moe_gather_reduce_backward(dout, y, inv_pos, topk_weights, T, k, N, group_si
                                num_local_experts, M_cap, dy, dw, stream=None):
     return _call("moe_gather_reduce_backward", _ptr(dout), _ptr(y), _ptr(inv_pos), _ptr(topk_weights), T, k, N,
                  _ptr(group_sizes), E, group_offset, num_local_experts, M_cap, _ptr(dy), _ptr(dw), _stream(stream))
+
+
+def moe_silu_mul_backward(a, b, lda, dh, R, C, da, db, ldo, stream=None):
+    """a, b, da, db may be column slices of wider buffers (row strides lda, ldo)."""
+    return _call("moe_silu_mul_backward", _ptr_rows(a, lda), _ptr_rows(b, lda), lda, _ptr(dh), R, C,
+                 _ptr_rows(da, ldo), _ptr_rows(db, ldo), ldo, _stream(stream))
 
 
 def moe_debug_check(ws, stream=None):

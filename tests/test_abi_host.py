@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_path_calls():
     names = _declared_functions()
     for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
-               "moe_gather_reduce_backward", "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
+               "moe_gather_reduce_backward", "moe_silu_mul_backward", "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
                "moe_version"]:
         assert fn in names
 
@@ -181,6 +181,18 @@ def test_gather_reduce_backward_validation(lib):
     assert b(one, one, one, one, 4, 2, 16, None, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
     assert b(one, None, one, one, 4, 2, 16, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
     assert b(None, None, None, None, 0, 2, 16, None, 8, 0, 8, 0, None, None, None) == m.MOE_OK  # nothing to do
+
+
+def test_silu_mul_backward_validation(lib):
+    f = lambda *a: _c(lib, "moe_silu_mul_backward", *a)
+    one = 1
+    # a, b, lda, dh, R, C, da, db, ldo, stream
+    assert f(one, one, 16, one, 4, 12, one, one, 16, None) == m.MOE_ERR_SHAPE      # C % 8
+    assert f(one, one, 8, one, 4, 16, one, one, 16, None) == m.MOE_ERR_SHAPE       # lda < C
+    assert f(one, one, 32, one, 4, 16, one, one, 20, None) == m.MOE_ERR_SHAPE      # ldo % 8
+    assert f(one, one, 16, one, -1, 16, one, one, 16, None) == m.MOE_ERR_SHAPE
+    assert f(one, None, 16, one, 4, 16, one, one, 16, None) == m.MOE_ERR_NULL
+    assert f(None, None, 16, None, 0, 16, None, None, 16, None) == m.MOE_OK        # R = 0
 
 
 def test_weight_quantizer_validation(lib):

@@ -122,6 +122,33 @@ def test_quantize_rows_strided_bit_exact(R, C, act, mode):
     assert_bits_equal(host(amax), ao, "strided row_amax")
 
 
+def test_silu_mul_backward_every_finite_bf16_gate_value():
+    """da, db bit-exact against the oracle for every finite bfloat16 gate a
+    (with random b and dh), read from and written to the column halves of
+    [R, 2C] buffers as the layer backward lays them out."""
+    from oracle.quantize import silu_mul_backward
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    a = bits[(bits & 0x7f80) != 0x7f80]                 # finite values only
+    C = 256
+    R = -(-a.size // C)
+    a = np.concatenate([a, np.zeros(R * C - a.size, np.uint16)]).reshape(R, C)
+    rng = np.random.default_rng(21)
+    b = _bits(rng, (R, C), 1.0)
+    dh = _bits(rng, (R, C), 1e-2)
+    dh[0, :8] = to_bf16_bits(np.array([1e-38, -1e-38, 3e38, 0.0, -0.0, 1.0, 1e-30, 5e-39], np.float32))
+    ab = np.concatenate([a, b], axis=1)
+    d_ab = dev_bf16(ab)
+    d_dh = dev_bf16(dh)
+    out = torch.full((R, 2 * C), 7, dtype=torch.bfloat16, device="cuda")
+    print(f"silu_mul_backward R={R} C={C} lda={2 * C} ldo={2 * C}", flush=True)
+    m.moe_silu_mul_backward(d_ab[:, :C], d_ab[:, C:], 2 * C, d_dh, R, C, out[:, :C], out[:, C:], 2 * C)
+    torch.cuda.synchronize()
+    got = host(out)
+    da, db = silu_mul_backward(a, b, dh)
+    assert_bits_equal(got[:, :C], da, "da")
+    assert_bits_equal(got[:, C:], db, "db")
+
+
 def test_silu_every_finite_bf16_gate_value():
     """silu(a) for every finite bfloat16 a, observed exactly: row i holds a_i
     and fifteen zeros with b = 1, so its row absmax is |silu(a_i)| in float32
