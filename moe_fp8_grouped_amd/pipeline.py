@@ -22,8 +22,9 @@ import torch
 
 from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_F32, MOE_OP_GMM, MOE_OP_QUANTIZE_ROWS,
                MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
-               MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gmm_fp8, moe_quantize_rows, moe_quantize_rows_strided,
-               moe_quantize_sort_by_expert, moe_quantize_weights, moe_sort_by_expert, moe_tgmm_fp8, workspace)
+               MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gather_reduce_backward, moe_gmm_fp8, moe_quantize_rows,
+               moe_quantize_rows_strided, moe_quantize_sort_by_expert, moe_quantize_weights, moe_silu_mul_backward,
+               moe_sort_by_expert, moe_tgmm_fp8, workspace)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -257,3 +258,141 @@ class BackwardPath:
         self.quantize_dy()
         self.grad_input()
         self.grad_weight()
+
+
+class FFNBackwardPath:
+    """The gated FFN's backward after a forward step of ``fwd`` (a
+    ForwardPath with ``pipeline == 'ffn'``), for an upstream gradient
+    ``dout`` [T, H] bf16 of the combined token rows:
+
+      combine backward  dy = w * dout to the sorted rows, dw_router per slot
+      dh   = gmm(dy, wo^T)            per-row dy scales, wo^T quantized per channel
+      dwo  = tgmm(h, dy)              h requantized with one tensor scale
+      da, db = SiLU*mul backward(a, b, dh), written as [da | db]
+      dxs  = gmm([da | db], [W0 | W1]^T)   one launch, K = 2I
+      dw01 = tgmm(x, [da | db])       x requantized with one tensor scale
+      dx   = unit-weight gather-reduce of dxs back to token rows
+
+    The forward's per-output-channel weight scales vary along the backward's
+    contraction, so the backward quantizes the transposed weights with scales
+    per its own output channel; tgmm needs scales constant along the
+    contracted rows, so its operands use per-tensor dynamic scales (per-row
+    scales serve the gmm inputs).  Weight gradients come out in float32
+    ([E, I, H] for wo, [E, H, 2I] for [W0 | W1])."""
+
+    def __init__(self, fwd, data, dout: torch.Tensor, device="cuda"):
+        cfg = fwd.cfg
+        assert cfg.pipeline == "ffn"
+        T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+        self.fwd, self.cfg = fwd, cfg
+        self.T, self.H, self.E, self.k, self.I = T, H, E, k, I
+        Mc = fwd.m_cap
+        self.m_cap = Mc
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        self.dout = dout
+        # backward weights (set-up): transposed, quantized per channel of the backward's output
+        wo = bf16_tensor(data["weights"]["wo"], device)                       # [E, I, H]
+        self.woT = QuantizedWeight(wo.transpose(1, 2).contiguous(), 1, I)      # as [E, K=H, N=I]
+        del wo
+        w01 = torch.cat([bf16_tensor(data["weights"]["wi_0"], device), bf16_tensor(data["weights"]["wi_1"], device)],
+                        dim=2)                                                  # [E, H, 2I]
+        self.w01T = QuantizedWeight(w01.transpose(1, 2).contiguous(), 1, H)    # as [E, K=2I, N=H]
+        del w01
+        self.ones = torch.ones((T, k), dtype=f32, device=device)
+        self.dy = torch.empty((Mc, H), dtype=bf, device=device)
+        self.dw_router = torch.empty((T, k), dtype=f32, device=device)
+        self.dyq_r = torch.empty((Mc, H), dtype=u8, device=device)
+        self.dys_r = torch.empty((Mc,), dtype=f32, device=device)
+        self.dyq_t = torch.empty((Mc, H), dtype=u8, device=device)
+        self.dys_t = torch.empty((1,), dtype=f32, device=device)
+        self.dh = torch.empty((Mc, I), dtype=bf, device=device)
+        self.hq_t = torch.empty((Mc, I), dtype=u8, device=device)
+        self.hs_t = torch.empty((1,), dtype=f32, device=device)
+        self.dwo = torch.empty((cfg.E_loc, I, H), dtype=f32, device=device)
+        self.dab = torch.empty((Mc, 2 * I), dtype=bf, device=device)
+        self.dabq_r = torch.empty((Mc, 2 * I), dtype=u8, device=device)
+        self.dabs_r = torch.empty((Mc,), dtype=f32, device=device)
+        self.dabq_t = torch.empty((Mc, 2 * I), dtype=u8, device=device)
+        self.dabs_t = torch.empty((1,), dtype=f32, device=device)
+        self.dxs = torch.empty((Mc, H), dtype=bf, device=device)
+        self.xq_t = torch.empty((T, H), dtype=u8, device=device)
+        self.xs_scale = torch.empty((1,), dtype=f32, device=device)
+        self.perm = torch.empty(T * k, dtype=torch.int32, device=device)
+        self.inv_pos = torch.empty(T * k, dtype=torch.int32, device=device)
+        self.group_sizes = torch.empty(E, dtype=torch.int32, device=device)
+        self.xs_t = torch.empty((Mc, H), dtype=u8, device=device)
+        self.dw01 = torch.empty((cfg.E_loc, H, 2 * I), dtype=f32, device=device)
+        self.dx = torch.empty((T, H), dtype=bf, device=device)
+        C = max(H, 2 * I)
+        self.ws_q = workspace(MOE_OP_QUANTIZE_ROWS, Mc, C, MOE_SCALE_TENSOR_DYNAMIC, device=device)
+        self.ws_qx = workspace(MOE_OP_QUANTIZE_ROWS, T, H, MOE_SCALE_TENSOR_DYNAMIC, device=device)
+        self.ws_sort = workspace(MOE_OP_SORT_BY_EXPERT, T * k, 0, 0, E, device=device)
+        self.ws_gmm_h = workspace(MOE_OP_GMM, Mc, H, I, E, device=device)
+        self.ws_gmm_x = workspace(MOE_OP_GMM, Mc, 2 * I, H, E, device=device)
+        self.ws_tgmm_o = workspace(MOE_OP_TGMM, Mc, I, H, E, device=device)
+        self.ws_tgmm_01 = workspace(MOE_OP_TGMM, Mc, H, 2 * I, E, device=device)
+
+    def _gmm(self, lhs, ls, w: QuantizedWeight, out, ws):
+        f = self.fwd
+        moe_gmm_fp8(lhs, ls, MOE_SCALE_ROW_DYNAMIC, w.q, w.scale, w.kb, w.nb, 1, f.group_sizes, self.E, f.g0, f.El,
+                    self.m_cap, w.K, w.N, MOE_BF16, out, ws)
+
+    def _tgmm(self, lhs, ls, rhs, rs, K, N, out, ws):
+        f = self.fwd
+        moe_tgmm_fp8(lhs, ls, 1, rhs, rs, 1, f.group_sizes, self.E, f.g0, f.El, self.m_cap, K, N, MOE_F32, out, ws)
+
+    # -- steps -------------------------------------------------------------
+    def combine_backward(self):
+        f = self.fwd
+        moe_gather_reduce_backward(self.dout, f.y, f.inv_pos, f.topk_w, self.T, self.k, self.H, f.group_sizes,
+                                   self.E, f.g0, f.El, self.m_cap, self.dy, self.dw_router)
+
+    def quantize_dy(self):
+        Mc, H = self.m_cap, self.H
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r, self.dys_r)
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.dyq_t, self.dys_t,
+                          None, self.ws_q)
+
+    def grad_h(self):
+        self._gmm(self.dyq_r, self.dys_r, self.woT, self.dh, self.ws_gmm_h)
+
+    def grad_wo(self):
+        f, I = self.fwd, self.I
+        moe_quantize_rows_strided(f.a, f.b, 2 * I, MOE_ACT_SILU_MUL, self.m_cap, I, MOE_SCALE_TENSOR_DYNAMIC, 0.0,
+                                  self.hq_t, self.hs_t, None, self.ws_q)
+        self._tgmm(self.hq_t, self.hs_t, self.dyq_t, self.dys_t, I, self.H, self.dwo, self.ws_tgmm_o)
+
+    def silu_backward(self):
+        f, I = self.fwd, self.I
+        moe_silu_mul_backward(f.a, f.b, 2 * I, self.dh, self.m_cap, I, self.dab[:, :I], self.dab[:, I:], 2 * I)
+
+    def quantize_dab(self):
+        Mc, C = self.m_cap, 2 * self.I
+        moe_quantize_rows(self.dab, None, MOE_ACT_NONE, Mc, C, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dabq_r, self.dabs_r)
+        moe_quantize_rows(self.dab, None, MOE_ACT_NONE, Mc, C, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.dabq_t,
+                          self.dabs_t, None, self.ws_q)
+
+    def grad_x_sorted(self):
+        self._gmm(self.dabq_r, self.dabs_r, self.w01T, self.dxs, self.ws_gmm_x)
+
+    def grad_w01(self):
+        f, T, H = self.fwd, self.T, self.H
+        moe_quantize_rows(f.x, None, MOE_ACT_NONE, T, H, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.xq_t, self.xs_scale,
+                          None, self.ws_qx)
+        moe_sort_by_expert(f.ids, T, self.k, self.E, f.g0, f.El, self.xq_t, self.xs_scale, MOE_SCALE_TENSOR_DYNAMIC,
+                           H, self.m_cap, self.perm, self.inv_pos, self.group_sizes, self.xs_t, None, self.ws_sort)
+        self._tgmm(self.xs_t, self.xs_scale, self.dabq_t, self.dabs_t, H, 2 * self.I, self.dw01, self.ws_tgmm_01)
+
+    def grad_x(self):
+        moe_gather_reduce(self.dxs, MOE_BF16, self.fwd.inv_pos, self.ones, self.T, self.k, self.H, MOE_BF16, self.dx)
+
+    def step(self):
+        self.combine_backward()
+        self.quantize_dy()
+        self.grad_h()
+        self.grad_wo()
+        self.silu_backward()
+        self.quantize_dab()
+        self.grad_x_sorted()
+        self.grad_w01()
+        self.grad_x()

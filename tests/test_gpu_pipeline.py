@@ -7,12 +7,12 @@ import pytest
 import torch
 
 import moe_fp8_grouped_amd as m
-from moe_fp8_grouped_amd.pipeline import BackwardPath, ForwardPath
+from moe_fp8_grouped_amd.pipeline import BackwardPath, FFNBackwardPath, ForwardPath
 from oracle.gather_reduce import gather_reduce, gather_reduce_backward
 from oracle.gmm import gmm, tgmm
 from oracle.pipeline import dense_bf16_reference, rel_norm_diff
 from oracle.quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STATIC, quantize_rows,
-                             quantize_weights)
+                             quantize_weights, silu_mul_backward)
 from oracle.sort import sort_by_expert
 from tests.golden import accuracy_tables
 from tests.parity import (assert_bits_equal, check_bf16, check_f32, dev_bf16, dev_f32, dev_i32, gmm_allowance, host,
@@ -254,6 +254,106 @@ def test_backward_pipeline_config5_stagewise():
     o = tgmm(srt["xs"], xsc, dq_t, ds_t, gs, 0, cfg.E, sample=(gi, ki, ci))
     B = lambda idx: tgmm_allowance(srt["xs"], xsc, dq_t, ds_t, gs, 0, cfg.E, gi[idx], ki[idx], ci[idx])
     check_f32(host(path.dw)[gi, ki, ci], o["out"], o["abs_sum"], B, "dW")
+
+
+def _sampled_gmm(lhs, ls, wq_kn, ws_, gs, El, got, seed, P, what):
+    rng = np.random.default_rng(seed)
+    n = int(np.asarray(gs)[:El].sum())
+    rows, cols = rng.integers(0, max(n, 1), P), rng.integers(0, wq_kn.shape[2], P)
+    o = gmm(lhs, ls, wq_kn, ws_, gs, 0, El, sample=(rows, cols))
+    B = lambda idx: gmm_allowance(lhs, ls, wq_kn, ws_, gs, 0, El, rows[idx], cols[idx])
+    check_bf16(got[rows, cols], o["out"], o["abs_sum"], B, what)
+
+
+def _sampled_tgmm(x, xs, d, ds, gs, El, got, seed, P, what):
+    rng = np.random.default_rng(seed)
+    gi, ki, ci = rng.integers(0, El, P), rng.integers(0, x.shape[1], P), rng.integers(0, d.shape[1], P)
+    o = tgmm(x, xs, d, ds, gs, 0, El, sample=(gi, ki, ci))
+    B = lambda idx: tgmm_allowance(x, xs, d, ds, gs, 0, El, gi[idx], ki[idx], ci[idx])
+    check_f32(got[gi, ki, ci], o["out"], o["abs_sum"], B, what)
+
+
+@pytest.mark.parametrize("shape", ["small", "config2"])
+def test_gated_ffn_backward_stagewise(shape):
+    """The gated FFN's backward after a forward step, every stage against the
+    oracle fed the GPU's own inputs for that stage: the combine backward, the
+    quantizations and the activation backward bit-exact, the grouped matmuls
+    under the float32 / bf16 rules."""
+    cfg = scaled_config(2, T=384, H=512, E=8, k=2, I=256) if shape == "small" else CONFIGS[2]
+    data = generate(cfg)
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    fwd = ForwardPath(cfg, data)
+    rng = np.random.default_rng(77)
+    dout_bits = to_bf16_bits((rng.standard_normal((T, H)) * 1e-2).astype(np.float32))
+    bwd = FFNBackwardPath(fwd, data, dev_bf16(dout_bits))
+    print(f"gated ffn backward {shape} T={T} H={H} E={E} k={k} I={I}", flush=True)
+    fwd.step()
+    bwd.step()
+    torch.cuda.synchronize()
+    for ws in (bwd.ws_q, bwd.ws_qx, bwd.ws_sort, bwd.ws_gmm_h, bwd.ws_gmm_x, bwd.ws_tgmm_o, bwd.ws_tgmm_01):
+        assert m.moe_debug_check(ws) == 0
+    inv = host(fwd.inv_pos).reshape(T, k)
+    gs = host(fwd.group_sizes)
+    Mc, n = fwd.m_cap, int(gs.sum())
+    P = 20000 if shape == "small" else 4000
+    # combine backward from the GPU's forward output y
+    o = gather_reduce_backward(dout_bits, host(fwd.y), inv, data["topk_w"], Mc, n)
+    dy = host(bwd.dy)
+    assert_bits_equal(dy, o["dy"], "dy")
+    check_f32(host(bwd.dw_router), o["dw64"], o["dw_abs"], 0.0, "dw_router")
+    # dy quantized per row and per tensor
+    q, s_, _ = quantize_rows(dy, SCALE_ROW_DYNAMIC)
+    assert_bits_equal(host(bwd.dyq_r), q, "dy row q")
+    assert_bits_equal(host(bwd.dys_r), s_, "dy row scale")
+    qt, st_, _ = quantize_rows(dy, SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(host(bwd.dyq_t), qt, "dy tensor q")
+    assert_bits_equal(host(bwd.dys_t), st_, "dy tensor scale")
+    # backward weights: wo^T and [W0 | W1]^T quantized per channel of the backward's output
+    # (all experts on the small shape, the first two at full size; the later stages' oracles then take the
+    # GPU's weights, verified here)
+    ne = E if shape == "small" else 2
+    woT_q, woT_s = np.ascontiguousarray(host(bwd.woT.q).transpose(0, 2, 1)), host(bwd.woT.scale)   # [E, H, I]
+    oq, os_ = quantize_weights(np.ascontiguousarray(data["weights"]["wo"][:ne].transpose(0, 2, 1)), 1, I)
+    assert_bits_equal(woT_q[:ne], oq, "wo^T q")
+    assert_bits_equal(woT_s[:ne], os_, "wo^T scale")
+    w01T_q, w01T_s = np.ascontiguousarray(host(bwd.w01T.q).transpose(0, 2, 1)), host(bwd.w01T.scale)  # [E, 2I, H]
+    w01 = np.concatenate([data["weights"]["wi_0"][:ne], data["weights"]["wi_1"][:ne]], axis=2)
+    oq, os_ = quantize_weights(np.ascontiguousarray(w01.transpose(0, 2, 1)), 1, H)
+    assert_bits_equal(w01T_q[:ne], oq, "[W0|W1]^T q")
+    assert_bits_equal(w01T_s[:ne], os_, "[W0|W1]^T scale")
+    # dh = dy wo^T
+    dh = host(bwd.dh)
+    _sampled_gmm(q, s_, woT_q, woT_s, gs, E, dh, 1, P, "dh")
+    assert not dh[n:].any()
+    # dwo = h^T dy, h requantized with one tensor scale from the GPU's a and b
+    a, b = host(fwd.a), host(fwd.b)
+    hq, hs, _ = quantize_rows(a, SCALE_TENSOR_DYNAMIC, x_up_bits=b)
+    assert_bits_equal(host(bwd.hq_t), hq, "h tensor q")
+    assert_bits_equal(host(bwd.hs_t), hs, "h tensor scale")
+    _sampled_tgmm(hq, hs, qt, st_, gs, E, host(bwd.dwo), 2, P, "dwo")
+    # activation backward
+    da, db = silu_mul_backward(a, b, dh)
+    dab = host(bwd.dab)
+    assert_bits_equal(dab[:, :I], da, "da")
+    assert_bits_equal(dab[:, I:], db, "db")
+    q2, s2, _ = quantize_rows(dab, SCALE_ROW_DYNAMIC)
+    assert_bits_equal(host(bwd.dabq_r), q2, "[da|db] row q")
+    assert_bits_equal(host(bwd.dabs_r), s2, "[da|db] row scale")
+    q2t, s2t, _ = quantize_rows(dab, SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(host(bwd.dabq_t), q2t, "[da|db] tensor q")
+    assert_bits_equal(host(bwd.dabs_t), s2t, "[da|db] tensor scale")
+    # dxs = [da|db] [W0|W1]^T
+    dxs = host(bwd.dxs)
+    _sampled_gmm(q2, s2, w01T_q, w01T_s, gs, E, dxs, 3, P, "dx sorted")
+    # dw01 = x^T [da|db], x requantized with one tensor scale and sorted
+    xq, xsc, _ = quantize_rows(data["x"], SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(host(bwd.xq_t), xq, "x tensor q")
+    srt = sort_by_expert(data["ids"], E, 0, E, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_DYNAMIC, m_cap=Mc)
+    assert_bits_equal(host(bwd.xs_t), srt["xs"], "x sorted")
+    _sampled_tgmm(srt["xs"], xsc, q2t, s2t, gs, E, host(bwd.dw01), 4, P, "dw01")
+    # dx: unit-weight un-sort of dxs
+    o = gather_reduce(dxs, True, inv, np.ones((T, k), np.float32))
+    check_bf16(host(bwd.dx), o["out"], o["abs_sum"], 0.0, "dx")
 
 
 @pytest.mark.parametrize("cid", [2, 4])
