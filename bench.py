@@ -111,6 +111,7 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
     path = ForwardPath(cfg, data, m_cap=m_cap_for(cfg, n), share=share)
     gs = np.bincount(ids.ravel(), minlength=cfg.E)[cfg.group_offset:cfg.group_offset + cfg.E_loc]
     path.nonempty_local = int((gs > 0).sum())
+    bwd_weights = dict(data["weights"]) if cfg.pipeline == "ffn" else None
     del data
     acc = step_accounting(path, n, U)
 
@@ -210,9 +211,12 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
         tf = gmm_flops / (gmm_us * 1e-6) / 1e12
         roof.update({"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4)})
+    ffn_bwd = None
     if cfg.pipeline == "ffn":
         kern["gather_reduce_backward"] = combine_backward(path, n, steps, warmup)
         kern["silu_mul_backward"] = silu_backward(path, steps, warmup)
+        ffn_bwd = ffn_backward_step(path, bwd_weights, n, steps, warmup)
+        del bwd_weights
     sort_gather = {nm: kern[nm]["GB_s"] for nm in ("quantize", "sort", "quantize_sort", "gather_reduce",
                                                    "gather_reduce_backward") if nm in kern}
     value = gmm_flops / (ms_step * 1e-3) / 1e12
@@ -231,6 +235,7 @@ def run_gpu(cfg_id, steps, warmup, calib_mib=0):
         "sort_gather_GB_s": sort_gather,
         "roofline": roof,
         "kernels": kern,
+        "ffn_backward": ffn_bwd,
         "device": torch.cuda.get_device_name(0),
     }
     return res, cfg
@@ -271,6 +276,36 @@ def silu_backward(path, steps, warmup):
     nbytes = R * I * 10
     return {"avg_us": round(us, 2), "min_us": round(us_min, 2), "alg_bytes": int(nbytes),
             "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def ffn_backward_step(path, weights, n, steps, warmup):
+    """The gated FFN's whole backward after the forward step (FFNBackwardPath):
+    every call timed eagerly with HIP events; matmul flops per call.  grad_wo
+    and grad_w01 include the per-tensor requantization (and, for x, the sort)
+    that feeds their tgmm."""
+    from moe_fp8_grouped_amd.pipeline import FFNBackwardPath
+    cfg = path.cfg
+    T, H, I = cfg.T, cfg.H, cfg.I
+    g = torch.Generator(device="cuda").manual_seed(99)
+    dout = (torch.randn((T, H), generator=g, device="cuda") * 1e-2).to(torch.bfloat16)
+    b = FFNBackwardPath(path, {"weights": weights}, dout)
+    calls = [(nm, getattr(b, nm)) for nm in ("combine_backward", "quantize_dy", "grad_h", "grad_wo", "silu_backward",
+                                            "quantize_dab", "grad_x_sorted", "grad_w01", "grad_x")]
+    t, ms_eager = _time_calls(calls, min(steps, 10), warmup)
+    fl = {"grad_h": 2 * n * H * I, "grad_wo": 2 * n * I * H, "grad_x_sorted": 2 * n * 2 * I * H,
+          "grad_w01": 2 * n * H * 2 * I}
+    kern = {}
+    for nm, (us, us_min) in t.items():
+        e = {"avg_us": round(us, 2), "min_us": round(us_min, 2)}
+        if nm in fl:
+            e["alg_flops"] = int(fl[nm])
+            e["TFLOP_s"] = round(fl[nm] / (us * 1e-6) / 1e12, 1)
+        kern[nm] = e
+    total = sum(fl.values())
+    del b
+    torch.cuda.empty_cache()
+    return {"ms_per_step_eager": round(ms_eager, 4), "gmm_tgmm_flops": int(total),
+            "gmm_TFLOP_s_whole_step": round(total / (ms_eager * 1e-3) / 1e12, 1), "kernels": kern}
 
 
 def _time_calls(calls, steps, warmup):
