@@ -396,3 +396,23 @@ class FFNBackwardPath:
         self.grad_x_sorted()
         self.grad_w01()
         self.grad_x()
+
+    OUTPUTS = ("dy", "dw_router", "dyq_r", "dys_r", "dyq_t", "dys_t", "dh", "hq_t", "hs_t", "dwo", "dab", "dabq_r",
+               "dabs_r", "dabq_t", "dabs_t", "dxs", "xq_t", "xs_scale", "perm", "inv_pos", "group_sizes", "xs_t",
+               "dw01", "dx")
+
+    def capture_graph(self, warmup=1):
+        """Record one backward step into a HIP graph (every buffer it writes is
+        fully rewritten by it, so replays equal eager steps)."""
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()

@@ -356,6 +356,34 @@ def test_gated_ffn_backward_stagewise(shape):
     check_bf16(host(bwd.dx), o["out"], o["abs_sum"], 0.0, "dx")
 
 
+def test_gated_ffn_backward_hip_graph_replays_match_eager():
+    """The backward step as a HIP graph: every replay, with scribbled outputs
+    and eager steps between replays, leaves the eager step's bits in every
+    buffer the step writes."""
+    cfg = scaled_config(2, T=384, H=512, E=8, k=2, I=256)
+    data = generate(cfg)
+    fwd = ForwardPath(cfg, data)
+    rng = np.random.default_rng(5)
+    dout = dev_bf16(to_bf16_bits((rng.standard_normal((cfg.T, cfg.H)) * 1e-2).astype(np.float32)))
+    bwd = FFNBackwardPath(fwd, data, dout)
+    print("gated ffn backward graph replays", flush=True)
+    fwd.step()
+    bwd.step()
+    torch.cuda.synchronize()
+    ref = {k: getattr(bwd, k).clone() for k in bwd.OUTPUTS}
+    bwd.capture_graph(warmup=1)
+    for rep in range(3):
+        for k in bwd.OUTPUTS:
+            getattr(bwd, k).view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        bwd.replay()
+        torch.cuda.synchronize()
+        for k in bwd.OUTPUTS:
+            assert torch.equal(getattr(bwd, k).view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+        bwd.step()
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("cid", [2, 4])
 def test_forward_step_hip_graph_replays_match_eager(cid):
     """The bench's timed step is a HIP graph of the forward step: every
