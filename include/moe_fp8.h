@@ -65,6 +65,7 @@ extern "C" {
 #define MOE_SCALE_ROW_DYNAMIC 0     /* one scale per row, from the row's absmax: [R] */
 #define MOE_SCALE_TENSOR_DYNAMIC 1  /* one scale from the whole tensor's absmax: [1] */
 #define MOE_SCALE_TENSOR_STATIC 2   /* one fixed scale given by the caller: [1] */
+#define MOE_SCALE_TENSOR_FROM_ROW_AMAX 3 /* one scale from caller-given row maxima: [1] */
 
 /* activation applied before quantization */
 #define MOE_ACT_NONE 0
@@ -104,7 +105,12 @@ extern "C" {
  *            subnormals kept).
  *   scale    out: [R] f32 (row mode) or [1] f32 (tensor modes);
  *            s = f32(amax / 448), or 1.0 when amax is 0.
- *   row_amax optional [R] f32 out (may be NULL): each row's absmax.
+ *   row_amax optional [R] f32 out (may be NULL): each row's absmax.  With
+ *            MOE_SCALE_TENSOR_FROM_ROW_AMAX it is an INPUT instead (required):
+ *            the rows' absmax as an earlier row-mode call on the same rows
+ *            wrote it; the scale is then f32(max(row_amax) / 448) (1.0 when
+ *            that is 0), which equals MOE_SCALE_TENSOR_DYNAMIC's result
+ *            without its absmax pass over x.
  *   ws       needed only for MOE_SCALE_TENSOR_DYNAMIC (may be NULL otherwise).
  * R >= 0; C > 0 and a multiple of 16.  Inputs must be finite.
  */

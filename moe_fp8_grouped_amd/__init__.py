@@ -22,6 +22,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "moe_fp8.h")
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
 MOE_DTYPE_DEFAULT, MOE_BF16, MOE_F32, MOE_E4M3FN = -1, 0, 1, 2
 MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC, MOE_SCALE_TENSOR_STATIC = 0, 1, 2
+MOE_SCALE_TENSOR_FROM_ROW_AMAX = 3
 MOE_ACT_NONE, MOE_ACT_SILU_MUL = 0, 1
 (MOE_OP_QUANTIZE_ROWS, MOE_OP_SORT_BY_EXPERT, MOE_OP_GMM, MOE_OP_TGMM, MOE_OP_GATHER_REDUCE,
  MOE_OP_QUANTIZE_WEIGHTS) = range(6)

@@ -242,6 +242,33 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restri
   if (threadIdx.x == 0) *scale = scale_from_amax(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
 }
 
+// The tensor scale from caller-given row maxima (MOE_SCALE_TENSOR_FROM_ROW_AMAX):
+// one workgroup of 16 waves, eight independent loads per thread and round,
+// then a wave and an LDS reduction (max is exact in any order).
+__global__ __launch_bounds__(1024) void amax_scale_kernel(const float* __restrict__ v, int64_t n,
+                                                          float* __restrict__ scale) {
+  __shared__ float red[16];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 1024 * 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = i + 1024 * u;
+      t[u] = j < n ? v[j] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, t[u]);
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < 16; ++w) r = fmaxf(r, red[w]);
+    *scale = scale_from_amax(r);
+  }
+}
+
 __global__ void fill_scale_kernel(float* scale, float v) { *scale = v; }
 
 constexpr int64_t kWgRowsMax = 2048;   // up to here a row gets a workgroup when it is long
@@ -308,6 +335,18 @@ int quantize_rows_impl(const uint16_t* x, const uint16_t* xu, int64_t R, int64_t
     return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, ldx, scale, q, scale, row_amax, st) == hipSuccess
                ? MOE_OK : MOE_ERR_HIP;
   }
+  if (mode == MOE_SCALE_TENSOR_FROM_ROW_AMAX) {
+    // the maximum of the caller's row maxima, then the quantize pass (row_amax is an input here)
+    if (R == 0) {
+      fill_scale_kernel<<<1, 1, 0, st>>>(scale, 1.0f);
+      MOE_CHECK_LAUNCH();
+      return MOE_OK;
+    }
+    amax_scale_kernel<<<1, 1024, 0, st>>>(row_amax, R, scale);
+    MOE_CHECK_LAUNCH();
+    return launch_rows<ACT, MODE_GIVEN>(x, xu, R, C, ldx, scale, q, scale, nullptr, st) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
+  }
   // tensor dynamic: partial maxima in the workspace after the error word
   float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + 256);
   const int nblk = static_cast<int>(R == 0 ? 1 : (moe_cdiv(R, 4) < kTensorBlocks ? moe_cdiv(R, 4) : kTensorBlocks));
@@ -340,11 +379,12 @@ extern "C" int moe_quantize_rows_strided(const void* x, const void* x_up, int64_
   if (ldx < C || ldx % 8 != 0) return MOE_ERR_SHAPE;
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_UNSUPPORTED;
   if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
-      scale_mode != MOE_SCALE_TENSOR_STATIC)
+      scale_mode != MOE_SCALE_TENSOR_STATIC && scale_mode != MOE_SCALE_TENSOR_FROM_ROW_AMAX)
     return MOE_ERR_UNSUPPORTED;
   if (scale_mode == MOE_SCALE_TENSOR_STATIC && !(static_scale > 0.0f && static_scale < 3.0e38f))
     return MOE_ERR_SHAPE;
   if (!scale || (R > 0 && (!x || !q))) return MOE_ERR_NULL;
+  if (scale_mode == MOE_SCALE_TENSOR_FROM_ROW_AMAX && R > 0 && !row_amax) return MOE_ERR_NULL;
   if (act == MOE_ACT_SILU_MUL && R > 0 && !x_up) return MOE_ERR_NULL;
   if (act == MOE_ACT_NONE && x_up) return MOE_ERR_UNSUPPORTED;
   if (scale_mode == MOE_SCALE_TENSOR_DYNAMIC) {

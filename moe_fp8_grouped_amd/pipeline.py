@@ -22,7 +22,7 @@ import torch
 
 from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_F32, MOE_OP_GMM, MOE_OP_QUANTIZE_ROWS,
                MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
-               MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gather_reduce_backward, moe_gmm_fp8, moe_quantize_rows,
+               MOE_SCALE_TENSOR_FROM_ROW_AMAX, MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gather_reduce_backward, moe_gmm_fp8, moe_quantize_rows,
                moe_quantize_rows_strided, moe_quantize_sort_by_expert, moe_quantize_weights, moe_silu_mul_backward,
                moe_sort_by_expert, moe_tgmm_fp8, workspace)
 
@@ -104,6 +104,7 @@ class ForwardPath:
             self.a, self.b = self.ab[:, :cfg.I], self.ab[:, cfg.I:]
             self.hq = torch.empty((self.m_cap, cfg.I), dtype=u8, device=device)
             self.hs = torch.empty((self.m_cap,), dtype=f32, device=device)
+            self.hamax = torch.empty((self.m_cap,), dtype=f32, device=device)   # rows' absmax of h
         self.y = torch.empty((self.m_cap, N_out), dtype=bf, device=device)
         self.out = torch.empty((T, N_out), dtype=bf, device=device)
         self.ws_q = workspace(MOE_OP_QUANTIZE_ROWS, T, H, self.act_mode, device=device)
@@ -158,7 +159,7 @@ class ForwardPath:
     def silu_quant(self):
         I = self.cfg.I
         moe_quantize_rows_strided(self.a, self.b, 2 * I, MOE_ACT_SILU_MUL, self.m_cap, I, MOE_SCALE_ROW_DYNAMIC,
-                                  0.0, self.hq, self.hs, None, None)
+                                  0.0, self.hq, self.hs, self.hamax, None)
 
     def combine(self):
         moe_gather_reduce(self.y, MOE_BF16, self.inv_pos, self.topk_w, self.T, self.k, self.N_out, MOE_BF16,
@@ -223,6 +224,7 @@ class BackwardPath:
         self.dys_r = torch.empty(self.M, dtype=f32, device=device)
         self.dyq_t = torch.empty((self.M, I), dtype=u8, device=device)
         self.dys_t = torch.empty(1, dtype=f32, device=device)
+        self.dy_amax = torch.empty(self.M, dtype=f32, device=device)
         self.dx = torch.empty((self.M, H), dtype=bf, device=device)
         self.dw_dtype = dw_dtype
         self.dw = torch.empty((self.El, H, I), dtype=f32 if dw_dtype == MOE_F32 else bf, device=device)
@@ -239,10 +241,11 @@ class BackwardPath:
                            self.xs, None, self.ws_sort)
 
     def quantize_dy(self):
+        # per-row codes (for dX), then per-tensor codes (for dW) scaled from the row pass's maxima
         moe_quantize_rows(self.dy, None, MOE_ACT_NONE, self.M, self.I, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r,
-                          self.dys_r, None, None)
-        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, self.M, self.I, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.dyq_t,
-                          self.dys_t, None, self.ws_q)
+                          self.dys_r, self.dy_amax, None)
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, self.M, self.I, MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0,
+                          self.dyq_t, self.dys_t, self.dy_amax, None)
 
     def grad_input(self):
         moe_gmm_fp8(self.dyq_r, self.dys_r, MOE_SCALE_ROW_DYNAMIC, self.w.q, self.w.scale, 1, 1, 1,
@@ -305,6 +308,7 @@ class FFNBackwardPath:
         self.dys_r = torch.empty((Mc,), dtype=f32, device=device)
         self.dyq_t = torch.empty((Mc, H), dtype=u8, device=device)
         self.dys_t = torch.empty((1,), dtype=f32, device=device)
+        self.dy_amax = torch.empty((Mc,), dtype=f32, device=device)
         self.dh = torch.empty((Mc, I), dtype=bf, device=device)
         self.hq_t = torch.empty((Mc, I), dtype=u8, device=device)
         self.hs_t = torch.empty((1,), dtype=f32, device=device)
@@ -314,6 +318,7 @@ class FFNBackwardPath:
         self.dabs_r = torch.empty((Mc,), dtype=f32, device=device)
         self.dabq_t = torch.empty((Mc, 2 * I), dtype=u8, device=device)
         self.dabs_t = torch.empty((1,), dtype=f32, device=device)
+        self.dab_amax = torch.empty((Mc,), dtype=f32, device=device)
         self.dxs = torch.empty((Mc, H), dtype=bf, device=device)
         self.xq_t = torch.empty((T, H), dtype=u8, device=device)
         self.xs_scale = torch.empty((1,), dtype=f32, device=device)
@@ -348,18 +353,22 @@ class FFNBackwardPath:
                                    self.E, f.g0, f.El, self.m_cap, self.dy, self.dw_router)
 
     def quantize_dy(self):
+        """Per-row codes, then per-tensor codes whose scale comes from the row
+        pass's maxima (the tensor-dynamic result without a second absmax pass)."""
         Mc, H = self.m_cap, self.H
-        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r, self.dys_r)
-        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.dyq_t, self.dys_t,
-                          None, self.ws_q)
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r, self.dys_r,
+                          self.dy_amax)
+        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0, self.dyq_t,
+                          self.dys_t, self.dy_amax)
 
     def grad_h(self):
         self._gmm(self.dyq_r, self.dys_r, self.woT, self.dh, self.ws_gmm_h)
 
     def grad_wo(self):
         f, I = self.fwd, self.I
-        moe_quantize_rows_strided(f.a, f.b, 2 * I, MOE_ACT_SILU_MUL, self.m_cap, I, MOE_SCALE_TENSOR_DYNAMIC, 0.0,
-                                  self.hq_t, self.hs_t, None, self.ws_q)
+        # h with one tensor scale, from the row maxima of h that the forward's requantization wrote
+        moe_quantize_rows_strided(f.a, f.b, 2 * I, MOE_ACT_SILU_MUL, self.m_cap, I, MOE_SCALE_TENSOR_FROM_ROW_AMAX,
+                                  0.0, self.hq_t, self.hs_t, f.hamax)
         self._tgmm(self.hq_t, self.hs_t, self.dyq_t, self.dys_t, I, self.H, self.dwo, self.ws_tgmm_o)
 
     def silu_backward(self):
@@ -368,9 +377,10 @@ class FFNBackwardPath:
 
     def quantize_dab(self):
         Mc, C = self.m_cap, 2 * self.I
-        moe_quantize_rows(self.dab, None, MOE_ACT_NONE, Mc, C, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dabq_r, self.dabs_r)
-        moe_quantize_rows(self.dab, None, MOE_ACT_NONE, Mc, C, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.dabq_t,
-                          self.dabs_t, None, self.ws_q)
+        moe_quantize_rows(self.dab, None, MOE_ACT_NONE, Mc, C, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dabq_r, self.dabs_r,
+                          self.dab_amax)
+        moe_quantize_rows(self.dab, None, MOE_ACT_NONE, Mc, C, MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0, self.dabq_t,
+                          self.dabs_t, self.dab_amax)
 
     def grad_x_sorted(self):
         self._gmm(self.dabq_r, self.dabs_r, self.w01T, self.dxs, self.ws_gmm_x)
@@ -397,9 +407,9 @@ class FFNBackwardPath:
         self.grad_w01()
         self.grad_x()
 
-    OUTPUTS = ("dy", "dw_router", "dyq_r", "dys_r", "dyq_t", "dys_t", "dh", "hq_t", "hs_t", "dwo", "dab", "dabq_r",
-               "dabs_r", "dabq_t", "dabs_t", "dxs", "xq_t", "xs_scale", "perm", "inv_pos", "group_sizes", "xs_t",
-               "dw01", "dx")
+    OUTPUTS = ("dy", "dw_router", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax", "dh", "hq_t", "hs_t", "dwo", "dab",
+               "dabq_r", "dabs_r", "dabq_t", "dabs_t", "dab_amax", "dxs", "xq_t", "xs_scale", "perm", "inv_pos",
+               "group_sizes", "xs_t", "dw01", "dx")
 
     def capture_graph(self, warmup=1):
         """Record one backward step into a HIP graph (every buffer it writes is

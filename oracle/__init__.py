@@ -35,7 +35,7 @@ rational arithmetic and the invariants the pages state.
 
 from .codec import (E4M3_MAX, bf16_decode, bf16_rne_from_f32, bf16_rne_from_f64,
                     e4m3_decode, e4m3_rne)
-from .quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STATIC,
+from .quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_FROM_ROW_AMAX, SCALE_TENSOR_STATIC,
                        pinned_exp_f32, quantize_rows, quantize_weights, silu_mul_backward, silu_mul_backward_f32,
                        silu_mul_f32)
 from .sort import sort_by_expert
@@ -44,7 +44,7 @@ from .gather_reduce import gather_reduce, gather_reduce_backward
 
 __all__ = [
     "E4M3_MAX", "bf16_decode", "bf16_rne_from_f32", "bf16_rne_from_f64", "e4m3_decode",
-    "e4m3_rne", "SCALE_ROW_DYNAMIC", "SCALE_TENSOR_DYNAMIC", "SCALE_TENSOR_STATIC",
+    "e4m3_rne", "SCALE_ROW_DYNAMIC", "SCALE_TENSOR_DYNAMIC", "SCALE_TENSOR_STATIC", "SCALE_TENSOR_FROM_ROW_AMAX",
     "pinned_exp_f32", "quantize_rows", "quantize_weights", "silu_mul_f32", "silu_mul_backward",
     "silu_mul_backward_f32",
     "sort_by_expert", "gmm", "tgmm", "gather_reduce", "gather_reduce_backward",

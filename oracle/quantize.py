@@ -37,6 +37,7 @@ from .codec import E4M3_MAX, bf16_decode, bf16_rne_from_f32, e4m3_rne
 SCALE_ROW_DYNAMIC = 0
 SCALE_TENSOR_DYNAMIC = 1
 SCALE_TENSOR_STATIC = 2
+SCALE_TENSOR_FROM_ROW_AMAX = 3
 
 _F448 = np.float32(E4M3_MAX)
 
@@ -144,12 +145,15 @@ def silu_mul_backward(a_bits, b_bits, dh_bits):
     return bf16_rne_from_f32(da), bf16_rne_from_f32(db)
 
 
-def quantize_rows(x_bits, mode, static_scale=None, x_up_bits=None):
+def quantize_rows(x_bits, mode, static_scale=None, x_up_bits=None, row_amax_in=None):
     """Quantize a [R, C] bf16 matrix to e4m3fn.
 
     mode: SCALE_ROW_DYNAMIC (scale per row, shape [R]), SCALE_TENSOR_DYNAMIC
-    (one scale from the whole tensor's absmax, shape [1]) or
-    SCALE_TENSOR_STATIC (the given ``static_scale``, shape [1]).
+    (one scale from the whole tensor's absmax, shape [1]),
+    SCALE_TENSOR_STATIC (the given ``static_scale``, shape [1]) or
+    SCALE_TENSOR_FROM_ROW_AMAX (one scale from the maximum of the given row
+    maxima ``row_amax_in``, shape [1]; the tensor-dynamic scale when those
+    are the rows' own maxima).
     With ``x_up_bits`` the quantized matrix is silu_mul_f32(x, x_up) instead
     of x (the gated FFN's activation).
 
@@ -171,6 +175,11 @@ def quantize_rows(x_bits, mode, static_scale=None, x_up_bits=None):
         q = _quantize_with_scale(xf, s[0])
     elif mode == SCALE_TENSOR_STATIC:
         s = np.array([static_scale], dtype=np.float32)
+        q = _quantize_with_scale(xf, s[0])
+    elif mode == SCALE_TENSOR_FROM_ROW_AMAX:
+        given = np.asarray(row_amax_in, dtype=np.float32)
+        amax = np.max(given) if R else np.float32(0.0)
+        s = _scale_from_amax(np.array([amax], dtype=np.float32))
         q = _quantize_with_scale(xf, s[0])
     else:
         raise ValueError("quantize_rows: unknown scale mode")

@@ -88,6 +88,14 @@ def test_quantize_rows_validation(lib):
     assert f(one, None, 0, 4, 32, 1, 0.0, one, one, None, one, 16, None) == m.MOE_ERR_WORKSPACE
 
 
+def test_quantize_rows_tensor_from_row_amax_validation(lib):
+    f = lambda *a: _c(lib, "moe_quantize_rows", *a)
+    one = 1
+    mode = m.MOE_SCALE_TENSOR_FROM_ROW_AMAX
+    assert f(one, None, 0, 4, 32, mode, 0.0, one, one, None, None, 0, None) == m.MOE_ERR_NULL     # row maxima needed
+    assert f(one, None, 0, 4, 32, 4, 0.0, one, one, one, None, 0, None) == m.MOE_ERR_UNSUPPORTED  # unknown mode
+
+
 def test_quantize_rows_strided_validation(lib):
     f = lambda *a: _c(lib, "moe_quantize_rows_strided", *a)
     al = 4096   # 16-byte aligned dummy pointer: never dereferenced on these paths

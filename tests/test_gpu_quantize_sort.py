@@ -82,6 +82,27 @@ def test_tensor_and_static_modes():
     assert_bits_equal(s, so, "static scale")
 
 
+@pytest.mark.parametrize("R,C,act", [(4096, 1536, 0), (300, 7168, 0), (999, 768, 1), (5, 16, 0)])
+def test_tensor_scale_from_row_maxima(R, C, act):
+    """MOE_SCALE_TENSOR_FROM_ROW_AMAX fed the GPU's own row-mode maxima: the
+    tensor-dynamic codes and scale of the oracle, bit for bit."""
+    rng = np.random.default_rng(R + C)
+    x = _bits(rng, (R, C), 2.0)
+    x[R // 2] = 0
+    up = _bits(rng, (R, C), 1.0) if act else None
+    _, _, amax = gpu_quantize(x, m.MOE_SCALE_ROW_DYNAMIC, up_bits=up)
+    xd = dev_bf16(x)
+    ud = dev_bf16(up) if act else None
+    q = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((1,), dtype=torch.float32, device="cuda")
+    print(f"quantize tensor-from-row-amax R={R} C={C} act={act}", flush=True)
+    m.moe_quantize_rows(xd, ud, act, R, C, m.MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0, q, sc, dev_f32(amax), None)
+    torch.cuda.synchronize()
+    qo, so, _ = quantize_rows(x, SCALE_TENSOR_DYNAMIC, x_up_bits=up)
+    assert_bits_equal(host(q), qo, "q")
+    assert_bits_equal(host(sc), so, "scale")
+
+
 @pytest.mark.parametrize("R,C", [(64, 768), (33, 768), (7, 256), (37, 2048), (2, 16), (37, 4096), (3, 8192)])
 def test_silu_mul_requantize_bit_exact(R, C):
     rng = np.random.default_rng(R + C)

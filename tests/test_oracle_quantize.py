@@ -205,3 +205,22 @@ def test_weight_quantizer_static_scale():
     assert np.all(s == np.float32(st))
     v = np.clip((bf16_decode(w) / np.float32(st)).astype(np.float32), -448, 448)
     assert np.array_equal(q, e4m3_rne(v))
+
+
+def test_tensor_scale_from_row_maxima_is_the_tensor_dynamic_result():
+    """The tensor scale from a row-mode call's row maxima gives the tensor-dynamic
+    codes and scale bit for bit (max is exact in any grouping), also for the
+    SiLU*mul activation; rows of zeros and an all-zero matrix keep scale 1."""
+    from oracle.quantize import SCALE_TENSOR_FROM_ROW_AMAX
+    rng = np.random.default_rng(12)
+    x = to_bf16_bits((rng.standard_normal((40, 96)) * 2.0).astype(np.float32))
+    x[3] = 0
+    up = to_bf16_bits(rng.standard_normal((40, 96)).astype(np.float32))
+    for xu in (None, up):
+        _, _, ra = quantize_rows(x, SCALE_ROW_DYNAMIC, x_up_bits=xu)
+        q1, s1, _ = quantize_rows(x, SCALE_TENSOR_DYNAMIC, x_up_bits=xu)
+        q2, s2, _ = quantize_rows(x, SCALE_TENSOR_FROM_ROW_AMAX, x_up_bits=xu, row_amax_in=ra)
+        assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    z = np.zeros((5, 32), np.uint16)
+    q, s, _ = quantize_rows(z, SCALE_TENSOR_FROM_ROW_AMAX, row_amax_in=np.zeros(5, np.float32))
+    assert s[0] == 1.0 and not q.any()
