@@ -310,14 +310,20 @@ int moe_gather_reduce(const void* y, int y_dtype, const int32_t* inv_pos, const 
  *            (every local row is the image of exactly one slot).
  *   topk_weights [T, k] f32.
  *   dy       [M_cap, N] bf16 out; dw [T, k] f32 out.
+ *   dy_q, dy_scale, dy_amax  optional (all NULL, or all set; N <= 8192):
+ *            [M_cap, N] e4m3fn, [M_cap] f32, [M_cap] f32 out -- dy quantized
+ *            per row exactly as moe_quantize_rows(dy, MOE_SCALE_ROW_DYNAMIC)
+ *            would (codes, scales and row absmax), formed while the row is in
+ *            registers instead of in a second pass over dy.
  * N a multiple of 8, k <= 64.  Needs no workspace.  Errors: MOE_ERR_SHAPE,
- * MOE_ERR_NULL; T = 0 with M_cap = 0 returns MOE_OK.
+ * MOE_ERR_NULL, MOE_ERR_UNSUPPORTED (dy_q with N > 8192); T = 0 with
+ * M_cap = 0 returns MOE_OK.
  */
 int moe_gather_reduce_backward(const void* dout, const void* y, const int32_t* inv_pos,
                                const float* topk_weights, int64_t T, int32_t k, int64_t N,
                                const int32_t* group_sizes, int32_t E, int32_t group_offset,
                                int32_t num_local_experts, int64_t M_cap, void* dy, float* dw,
-                               void* stream);
+                               uint8_t* dy_q, float* dy_scale, float* dy_amax, void* stream);
 
 /*
  * moe_silu_mul_backward -- gradients of the gated FFN's activation

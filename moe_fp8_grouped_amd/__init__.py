@@ -44,7 +44,7 @@ SIGNATURES = {
                           ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_gather_reduce": (_I, [_P, _I, _P, _P, _I64, ctypes.c_int32, _I64, _I, _P, _P]),
     "moe_gather_reduce_backward": (_I, [_P, _P, _P, _P, _I64, ctypes.c_int32, _I64, _P, ctypes.c_int32,
-                                        ctypes.c_int32, ctypes.c_int32, _I64, _P, _P, _P]),
+                                        ctypes.c_int32, ctypes.c_int32, _I64, _P, _P, _P, _P, _P, _P]),
     "moe_silu_mul_backward": (_I, [_P, _P, _I64, _P, _I64, _I64, _P, _P, _I64, _P]),
     "moe_workspace_bytes": (_I, [_I, _I64, _I64, _I64, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_debug_check": (_I, [_P, _P, ctypes.POINTER(ctypes.c_int32)]),
@@ -191,9 +191,10 @@ def moe_gather_reduce(y, y_dtype, inv_pos, topk_weights, T, k, N, out_dtype, out
 
 
 def moe_gather_reduce_backward(dout, y, inv_pos, topk_weights, T, k, N, group_sizes, E, group_offset,
-                               num_local_experts, M_cap, dy, dw, stream=None):
+                               num_local_experts, M_cap, dy, dw, dy_q=None, dy_scale=None, dy_amax=None, stream=None):
     return _call("moe_gather_reduce_backward", _ptr(dout), _ptr(y), _ptr(inv_pos), _ptr(topk_weights), T, k, N,
-                 _ptr(group_sizes), E, group_offset, num_local_experts, M_cap, _ptr(dy), _ptr(dw), _stream(stream))
+                 _ptr(group_sizes), E, group_offset, num_local_experts, M_cap, _ptr(dy), _ptr(dw), _ptr(dy_q),
+                 _ptr(dy_scale), _ptr(dy_amax), _stream(stream))
 
 
 def moe_silu_mul_backward(a, b, lda, dh, R, C, da, db, ldo, stream=None):

@@ -7,7 +7,7 @@
 // (inverse position, router weight), then sweep the row in 16-byte chunks,
 // loading the k expert-output rows and accumulating in float32 in slot order.
 // HBM-bound: reads n*N*2 (each sorted row once) + T*k*8, writes T*N*2 bytes.
-#include "common.hpp"
+#include "quant_common.hpp"
 
 namespace moe {
 namespace {
@@ -191,11 +191,17 @@ __device__ __forceinline__ float bwd_chunk(const uint4 d, const uint4 yv, float 
 // (8 + chunks per lane + 6) float32 roundings deep.  A token's k waves are
 // neighbours, so its dout row comes from HBM once.  Slots without a local row
 // get dw = 0; extra waves zero dy's rows [n, M_cap), n = the local rows.
-template <int CPL>
+// QUANT (CPL > 0 only): the wave holds the whole dy row, so it also writes the
+// row's e4m3fn codes, scale and absmax with the row quantizer's own functions
+// (the bytes moe_quantize_rows gives for dy in row mode); zero rows get codes
+// 0, scale 1 and absmax 0.
+template <int CPL, bool QUANT>
 __global__ __launch_bounds__(256) void gather_reduce_bwd_kernel(
     const uint16_t* __restrict__ dout, const uint16_t* __restrict__ y, const int32_t* __restrict__ inv,
     const float* __restrict__ wts, int64_t S, int k, int64_t N, int64_t M_cap, const int32_t* __restrict__ gs,
-    int g0, int El, uint16_t* __restrict__ dy, float* __restrict__ dw) {
+    int g0, int El, uint16_t* __restrict__ dy, float* __restrict__ dw, uint8_t* __restrict__ dyq,
+    float* __restrict__ dys, float* __restrict__ dyamax) {
+  static_assert(!QUANT || CPL > 0, "row quantization keeps the row in registers");
   const int lane = threadIdx.x & 63;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256) void gather_reduce_bwd_kernel(
     uint4* dyrow = reinterpret_cast<uint4*>(dy + static_cast<int64_t>(r) * N);
     float part = 0.0f;
     if constexpr (CPL > 0) {
-      uint4 dv[CPL], yv[CPL];
+      uint4 dv[CPL], yv[CPL], ov[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int64_t ch = lane + 64 * c;
@@ -221,13 +227,48 @@ __global__ __launch_bounds__(256) void gather_reduce_bwd_kernel(
         dv[c] = drow[cl];
         yv[c] = yrow[cl];
       }
+      float amax = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int64_t ch = lane + 64 * c;
-        if (ch < nch) part += bwd_chunk(dv[c], yv[c], w, dyrow[ch]);
+        if (ch < nch) {
+          part += bwd_chunk(dv[c], yv[c], w, ov[c]);
+          dyrow[ch] = ov[c];
+          if constexpr (QUANT) {
+            Bf16x8 o;
+            o.raw = ov[c];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(o.get(i)));
+          }
+        }
+      }
+      if constexpr (QUANT) {
+        amax = wave_max(amax);
+        const float sc = scale_from_amax(amax);
+        const RowDiv div(sc);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int64_t ch = lane + 64 * c;
+          if (ch < nch) {
+            Bf16x8 o;
+            o.raw = ov[c];
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = o.get(i);
+            store_codes(dyq, static_cast<int64_t>(r) * N + ch * 8, v, div);
+          }
+        }
+        if (lane == 0) {
+          dys[r] = sc;
+          dyamax[r] = amax;
+        }
       }
     } else {
-      for (int64_t ch = lane; ch < nch; ch += 64) part += bwd_chunk(drow[ch], yrow[ch], w, dyrow[ch]);
+      for (int64_t ch = lane; ch < nch; ch += 64) {
+        uint4 o;
+        part += bwd_chunk(drow[ch], yrow[ch], w, o);
+        dyrow[ch] = o;
+      }
     }
     part = wave_sum(part);
     if (lane == 0) dw[f] = part;
@@ -240,6 +281,14 @@ __global__ __launch_bounds__(256) void gather_reduce_bwd_kernel(
   for (int64_t r = n + wid; r < M_cap; r += nw) {
     uint4* row = reinterpret_cast<uint4*>(dy + r * N);
     for (int64_t ch = lane; ch < nch; ch += 64) row[ch] = make_uint4(0, 0, 0, 0);
+    if constexpr (QUANT) {
+      uint2* qrow = reinterpret_cast<uint2*>(dyq + r * N);
+      for (int64_t ch = lane; ch < nch; ch += 64) qrow[ch] = make_uint2(0, 0);
+      if (lane == 0) {
+        dys[r] = 1.0f;
+        dyamax[r] = 0.0f;
+      }
+    }
   }
 }
 
@@ -276,7 +325,7 @@ extern "C" int moe_gather_reduce_backward(const void* dout, const void* y, const
                                           const float* topk_weights, int64_t T, int32_t k, int64_t N,
                                           const int32_t* group_sizes, int32_t E, int32_t group_offset,
                                           int32_t num_local_experts, int64_t M_cap, void* dy, float* dw,
-                                          void* stream) {
+                                          uint8_t* dy_q, float* dy_scale, float* dy_amax, void* stream) {
   if (T < 0 || k <= 0 || k > 64 || N <= 0 || N % 8 || M_cap < 0) return MOE_ERR_SHAPE;
   if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E)
     return MOE_ERR_SHAPE;
@@ -285,6 +334,9 @@ extern "C" int moe_gather_reduce_backward(const void* dout, const void* y, const
   if (!group_sizes) return MOE_ERR_NULL;
   if (T > 0 && (!dout || !inv_pos || !topk_weights || !dw)) return MOE_ERR_NULL;
   if (M_cap > 0 && (!y || !dy)) return MOE_ERR_NULL;
+  const bool quant = dy_q != nullptr;
+  if (quant && (!dy_scale || !dy_amax)) return MOE_ERR_NULL;
+  if (quant && N / 8 > 16 * 64) return MOE_ERR_UNSUPPORTED;      // rows above 8192 elements
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t S = T * k;
   int64_t waves = S > M_cap / 4 ? S : M_cap / 4;
@@ -295,15 +347,18 @@ extern "C" int moe_gather_reduce_backward(const void* dout, const void* y, const
   const uint16_t* d = static_cast<const uint16_t*>(dout);
   const uint16_t* yy = static_cast<const uint16_t*>(y);
   uint16_t* o = static_cast<uint16_t*>(dy);
-#define MOE_GRB(CPL)                                                                                          \
-  moe::gather_reduce_bwd_kernel<CPL><<<grid, 256, 0, st>>>(d, yy, inv_pos, topk_weights, S, k, N, M_cap,      \
-                                                             group_sizes, group_offset, num_local_experts, o, dw)
-  if (cpl <= 1) MOE_GRB(1);
-  else if (cpl <= 2) MOE_GRB(2);
-  else if (cpl <= 4) MOE_GRB(4);
-  else if (cpl <= 8) MOE_GRB(8);
-  else if (cpl <= 16) MOE_GRB(16);
-  else MOE_GRB(0);
+#define MOE_GRB(CPL, Q)                                                                                      \
+  moe::gather_reduce_bwd_kernel<CPL, Q><<<grid, 256, 0, st>>>(d, yy, inv_pos, topk_weights, S, k, N, M_cap,  \
+                                                                group_sizes, group_offset, num_local_experts, o, \
+                                                                dw, dy_q, dy_scale, dy_amax)
+#define MOE_GRB_Q(CPL) do { if (quant) MOE_GRB(CPL, true); else MOE_GRB(CPL, false); } while (0)
+  if (cpl <= 1) MOE_GRB_Q(1);
+  else if (cpl <= 2) MOE_GRB_Q(2);
+  else if (cpl <= 4) MOE_GRB_Q(4);
+  else if (cpl <= 8) MOE_GRB_Q(8);
+  else if (cpl <= 16) MOE_GRB_Q(16);
+  else MOE_GRB(0, false);
+#undef MOE_GRB_Q
 #undef MOE_GRB
   MOE_CHECK_LAUNCH();
   return MOE_OK;

@@ -283,9 +283,11 @@ class FFNBackwardPath:
     scales serve the gmm inputs).  Weight gradients come out in float32
     ([E, I, H] for wo, [E, H, 2I] for [W0 | W1])."""
 
-    def __init__(self, fwd, data, dout: torch.Tensor, device="cuda"):
+    def __init__(self, fwd, data, dout: torch.Tensor, device="cuda", fuse_dy_quant=True):
         cfg = fwd.cfg
         assert cfg.pipeline == "ffn"
+        # dy's per-row quantization formed by the combine backward (True) or as a pass of its own
+        self.fuse_dy_quant = fuse_dy_quant
         T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
         self.fwd, self.cfg = fwd, cfg
         self.T, self.H, self.E, self.k, self.I = T, H, E, k, I
@@ -349,15 +351,21 @@ class FFNBackwardPath:
     # -- steps -------------------------------------------------------------
     def combine_backward(self):
         f = self.fwd
+        fq = self.fuse_dy_quant
+        # dy, and (fused) its per-row codes, scales and row maxima from the same registers
         moe_gather_reduce_backward(self.dout, f.y, f.inv_pos, f.topk_w, self.T, self.k, self.H, f.group_sizes,
-                                   self.E, f.g0, f.El, self.m_cap, self.dy, self.dw_router)
+                                   self.E, f.g0, f.El, self.m_cap, self.dy, self.dw_router,
+                                   self.dyq_r if fq else None, self.dys_r if fq else None,
+                                   self.dy_amax if fq else None)
 
     def quantize_dy(self):
-        """Per-row codes, then per-tensor codes whose scale comes from the row
-        pass's maxima (the tensor-dynamic result without a second absmax pass)."""
+        """Per-row codes of dy unless the combine backward formed them, then
+        per-tensor codes whose scale comes from the row maxima (the
+        tensor-dynamic result without an absmax pass)."""
         Mc, H = self.m_cap, self.H
-        moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r, self.dys_r,
-                          self.dy_amax)
+        if not self.fuse_dy_quant:
+            moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_ROW_DYNAMIC, 0.0, self.dyq_r, self.dys_r,
+                              self.dy_amax)
         moe_quantize_rows(self.dy, None, MOE_ACT_NONE, Mc, H, MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0, self.dyq_t,
                           self.dys_t, self.dy_amax)
 

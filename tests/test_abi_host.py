@@ -178,9 +178,10 @@ def test_tgmm_and_gather_reduce_validation(lib):
 
 
 def test_gather_reduce_backward_validation(lib):
-    b = lambda *a: _c(lib, "moe_gather_reduce_backward", *a)
+    g = lambda *a: _c(lib, "moe_gather_reduce_backward", *a)
+    b = lambda *a: g(*a[:14], None, None, None, a[14])
     one = 1
-    # dout, y, inv_pos, w, T, k, N, group_sizes, E, g0, El, M_cap, dy, dw, stream
+    # dout, y, inv_pos, w, T, k, N, group_sizes, E, g0, El, M_cap, dy, dw, [dy_q, dy_scale, dy_amax,] stream
     assert b(one, one, one, one, 4, 2, 12, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_SHAPE     # N % 8
     assert b(one, one, one, one, 4, 0, 16, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_SHAPE     # k = 0
     assert b(one, one, one, one, 4, 2, 16, one, 8, 4, 8, 8, one, one, None) == m.MOE_ERR_SHAPE     # window > E
@@ -189,6 +190,9 @@ def test_gather_reduce_backward_validation(lib):
     assert b(one, one, one, one, 4, 2, 16, None, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
     assert b(one, None, one, one, 4, 2, 16, one, 8, 0, 8, 8, one, one, None) == m.MOE_ERR_NULL
     assert b(None, None, None, None, 0, 2, 16, None, 8, 0, 8, 0, None, None, None) == m.MOE_OK  # nothing to do
+    # the fused row quantization: all three outputs or none, rows of at most 8192 elements
+    assert g(one, one, one, one, 4, 2, 16, one, 8, 0, 8, 8, one, one, one, None, one, None) == m.MOE_ERR_NULL
+    assert g(one, one, one, one, 4, 2, 8200, one, 8, 0, 8, 8, one, one, one, one, one, None) == m.MOE_ERR_UNSUPPORTED
 
 
 def test_silu_mul_backward_validation(lib):

@@ -71,11 +71,15 @@ def gpu_gather_reduce_backward(dout, y, inv, w, gs, E, g0, El, m_cap):
     N = dout.shape[1]
     dy = torch.full((m_cap, N), 9.0, dtype=torch.bfloat16, device="cuda")
     dw = torch.full((T, k), 7.0, dtype=torch.float32, device="cuda")
-    print(f"gather_reduce_backward T={T} k={k} N={N} E={E} g0={g0} El={El} m_cap={m_cap}", flush=True)
+    quant = N <= 8192
+    q = torch.full((m_cap, N), 0x55, dtype=torch.uint8, device="cuda") if quant else None
+    qs = torch.full((m_cap,), 5.0, dtype=torch.float32, device="cuda") if quant else None
+    qa = torch.full((m_cap,), 5.0, dtype=torch.float32, device="cuda") if quant else None
+    print(f"gather_reduce_backward T={T} k={k} N={N} E={E} g0={g0} El={El} m_cap={m_cap} quant={quant}", flush=True)
     m.moe_gather_reduce_backward(dev_bf16(dout), dev_bf16(y), dev_i32(inv), dev_f32(w), T, k, N, dev_i32(gs), E, g0,
-                                 El, m_cap, dy, dw)
+                                 El, m_cap, dy, dw, q, qs, qa)
     torch.cuda.synchronize()
-    return host(dy), host(dw)
+    return host(dy), host(dw), ((host(q), host(qs), host(qa)) if quant else None)
 
 
 @pytest.mark.parametrize("T,k,E,g0,El,N,extra", [(256, 2, 8, 0, 8, 1024, 0), (4096, 8, 64, 0, 64, 2048, 0),
@@ -94,8 +98,13 @@ def test_gather_reduce_backward(T, k, E, g0, El, N, extra):
     dout = to_bf16_bits((rng.standard_normal((T, N)) * 1e-2).astype(np.float32))
     w = rng.uniform(0, 1, (T, k)).astype(np.float32)
     o = gather_reduce_backward(dout, y, inv, w, m_cap, n)
-    gdy, gdw = gpu_gather_reduce_backward(dout, y, inv, w, srt["group_sizes"], E, g0, El, m_cap)
+    gdy, gdw, gq = gpu_gather_reduce_backward(dout, y, inv, w, srt["group_sizes"], E, g0, El, m_cap)
     assert_bits_equal(gdy, o["dy"], "dy")
+    if gq is not None:      # dy's row quantization formed in the same pass: moe_quantize_rows' bytes
+        q, s_, a = quantize_rows(o["dy"], SCALE_ROW_DYNAMIC)
+        assert_bits_equal(gq[0], q, "dy row q")
+        assert_bits_equal(gq[1], s_, "dy row scale")
+        assert_bits_equal(gq[2], a, "dy row amax")
     st = check_f32(gdw, o["dw64"], o["dw_abs"], 0.0, "dw")
     assert (gdw[inv < 0] == 0).all()
     print("dw", st)
@@ -279,8 +288,8 @@ def _sampled_tgmm(x, xs, d, ds, gs, El, got, seed, P, what):
     check_f32(got[gi, ki, ci], o["out"], o["abs_sum"], B, what)
 
 
-@pytest.mark.parametrize("shape", ["small", "config2"])
-def test_gated_ffn_backward_stagewise(shape):
+@pytest.mark.parametrize("shape,fuse", [("small", True), ("small", False), ("config2", True)])
+def test_gated_ffn_backward_stagewise(shape, fuse):
     """The gated FFN's backward after a forward step, every stage against the
     oracle fed the GPU's own inputs for that stage: the combine backward, the
     quantizations and the activation backward bit-exact, the grouped matmuls
@@ -291,8 +300,8 @@ def test_gated_ffn_backward_stagewise(shape):
     fwd = ForwardPath(cfg, data)
     rng = np.random.default_rng(77)
     dout_bits = to_bf16_bits((rng.standard_normal((T, H)) * 1e-2).astype(np.float32))
-    bwd = FFNBackwardPath(fwd, data, dev_bf16(dout_bits))
-    print(f"gated ffn backward {shape} T={T} H={H} E={E} k={k} I={I}", flush=True)
+    bwd = FFNBackwardPath(fwd, data, dev_bf16(dout_bits), fuse_dy_quant=fuse)
+    print(f"gated ffn backward {shape} fuse_dy_quant={fuse} T={T} H={H} E={E} k={k} I={I}", flush=True)
     fwd.step()
     bwd.step()
     torch.cuda.synchronize()
