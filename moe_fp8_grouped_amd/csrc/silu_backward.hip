@@ -18,11 +18,21 @@
 namespace moe {
 namespace {
 
+// The two quotients 1 / den and a / den by the forward's reciprocal-and-
+// correction sequence (silu_quotient, correctly rounded for these operands --
+// the GPU test over every finite bfloat16 gate compares both results bit for
+// bit with IEEE division), the IEEE divide when den exceeds 2^126.
 __device__ __forceinline__ void silu_bwd1(float a, float b, float dh, float& da, float& db) {
 #pragma clang fp contract(off)
   const float den = 1.0f + pinned_exp(-a);
-  const float s = 1.0f / den;
-  const float q = a / den;
+  float s, q;
+  if (den <= 0x1p126f) {
+    s = silu_quotient(1.0f, den);
+    q = silu_quotient(a, den);
+  } else {
+    s = 1.0f / den;
+    q = a / den;
+  }
   db = dh * q;
   const float ds = s * (1.0f + a * (1.0f - s));
   da = (dh * b) * ds;
