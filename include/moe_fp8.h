@@ -200,9 +200,12 @@ int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t 
  * destination rows; a token with none is not quantized (unless `scale` asks
  * for its scale).
  *   x        [T, H] bf16, 16-byte aligned; H > 0, a multiple of 16.
- *   scale_mode MOE_SCALE_ROW_DYNAMIC or MOE_SCALE_TENSOR_STATIC (with
- *            static_scale as in moe_quantize_rows); MOE_SCALE_TENSOR_DYNAMIC
- *            needs the whole tensor before any code and is MOE_ERR_UNSUPPORTED.
+ *   scale_mode MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_STATIC (with
+ *            static_scale as in moe_quantize_rows) or
+ *            MOE_SCALE_TENSOR_FROM_ROW_AMAX (the tensor scale from the token
+ *            maxima in row_amax, as in moe_quantize_rows);
+ *            MOE_SCALE_TENSOR_DYNAMIC needs the whole tensor before any code
+ *            and is MOE_ERR_UNSUPPORTED.
  *   expert_ids .. group_sizes, M_cap, ws, ws_bytes: as in moe_sort_by_expert
  *            (workspace of moe_workspace_bytes(MOE_OP_SORT_BY_EXPERT, ...)).
  *   xs       [M_cap, H] e4m3fn out: the bytes moe_quantize_rows then
@@ -210,15 +213,20 @@ int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t 
  *   ss       row mode: [M_cap] f32 out, each local row's token scale (0 past
  *            n); static mode: unused, may be NULL.
  *   scale    optional: row mode [T] f32 out, every token's scale (then every
- *            token is quantized); static mode [1] f32 out = static_scale.
+ *            token is quantized); static mode [1] f32 out = static_scale;
+ *            required in MOE_SCALE_TENSOR_FROM_ROW_AMAX mode, [1] f32 out.
+ *   row_amax row mode: optional [T] f32 out, every token's absmax (then every
+ *            token is quantized); MOE_SCALE_TENSOR_FROM_ROW_AMAX: required
+ *            [T] f32 input, the tokens' absmax as a row-mode pass wrote it;
+ *            ignored in static mode.
  * Errors as in moe_sort_by_expert; device-data errors (bad expert ids, more
  * local rows than M_cap) set the same workspace error bits.
  */
 int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_mode, float static_scale,
                                 const int32_t* expert_ids, int32_t k, int32_t E, int32_t group_offset,
                                 int32_t num_local_experts, int64_t M_cap, int32_t* perm, int32_t* inv_pos,
-                                int32_t* group_sizes, uint8_t* xs, float* ss, float* scale, void* ws,
-                                size_t ws_bytes, void* stream);
+                                int32_t* group_sizes, uint8_t* xs, float* ss, float* scale, float* row_amax,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_gmm_fp8 -- grouped matmul of fp8 operands, the gmm_v2 call of "Quantize

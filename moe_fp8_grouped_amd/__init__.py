@@ -37,7 +37,7 @@ SIGNATURES = {
     "moe_sort_by_expert": (_I, [_P, _I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                 _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_sort_by_expert": (_I, [_P, _I64, _I64, _I, _F, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                         ctypes.c_int32, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                         ctypes.c_int32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_gmm_fp8": (_I, [_P, _P, _I, _P, _P, ctypes.c_int32, ctypes.c_int32, _I, _P, ctypes.c_int32, ctypes.c_int32,
                          ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_tgmm_fp8": (_I, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
@@ -165,10 +165,11 @@ def moe_sort_by_expert(expert_ids, T, k, E, group_offset, num_local_experts, xq,
 
 
 def moe_quantize_sort_by_expert(x, T, H, scale_mode, static_scale, expert_ids, k, E, group_offset, num_local_experts,
-                                M_cap, perm, inv_pos, group_sizes, xs, ss, scale=None, ws=None, stream=None):
+                                M_cap, perm, inv_pos, group_sizes, xs, ss, scale=None, ws=None, stream=None,
+                                row_amax=None):
     return _call("moe_quantize_sort_by_expert", _ptr(x), T, H, scale_mode, float(static_scale), _ptr(expert_ids), k,
                  E, group_offset, num_local_experts, M_cap, _ptr(perm), _ptr(inv_pos), _ptr(group_sizes), _ptr(xs),
-                 _ptr(ss), _ptr(scale), _ptr(ws), _nbytes(ws), _stream(stream))
+                 _ptr(ss), _ptr(scale), _ptr(row_amax), _ptr(ws), _nbytes(ws), _stream(stream))
 
 
 def moe_gmm_fp8(lhs, lhs_scale, lhs_scale_mode, rhs, rhs_scale, Kb, Nb, transpose_rhs, group_sizes, E,

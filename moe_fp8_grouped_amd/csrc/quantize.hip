@@ -242,33 +242,6 @@ __global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restri
   if (threadIdx.x == 0) *scale = scale_from_amax(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
 }
 
-// The tensor scale from caller-given row maxima (MOE_SCALE_TENSOR_FROM_ROW_AMAX):
-// one workgroup of 16 waves, eight independent loads per thread and round,
-// then a wave and an LDS reduction (max is exact in any order).
-__global__ __launch_bounds__(1024) void amax_scale_kernel(const float* __restrict__ v, int64_t n,
-                                                          float* __restrict__ scale) {
-  __shared__ float red[16];
-  float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < n; i += 1024 * 8) {
-    float t[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t j = i + 1024 * u;
-      t[u] = j < n ? v[j] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = fmaxf(m, t[u]);
-  }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int w = 1; w < 16; ++w) r = fmaxf(r, red[w]);
-    *scale = scale_from_amax(r);
-  }
-}
-
 __global__ void fill_scale_kernel(float* scale, float v) { *scale = v; }
 
 constexpr int64_t kWgRowsMax = 2048;   // up to here a row gets a workgroup when it is long

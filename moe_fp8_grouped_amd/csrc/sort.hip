@@ -334,16 +334,23 @@ __device__ __forceinline__ void scatter_codes(uint8_t* __restrict__ xs, int64_t 
   }
 }
 
+// given_scale (device [1], the tensor scale from row maxima) or static_mode
+// make it a tensor mode: one scale, no per-row scales; in row mode row_amax
+// (optional) receives every token's absmax.
 template <int GPL>
 __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* __restrict__ x, int static_mode,
-                                                               float static_scale, const int32_t* __restrict__ inv_pos,
+                                                               float static_scale, const float* __restrict__ given_scale,
+                                                               const int32_t* __restrict__ inv_pos,
                                                                int64_t T, int k, int64_t H, int64_t M_cap,
                                                                const int32_t* __restrict__ hdr, uint8_t* __restrict__ xs,
-                                                               float* __restrict__ ss, float* __restrict__ tok_scale) {
+                                                               float* __restrict__ ss, float* __restrict__ tok_scale,
+                                                               float* __restrict__ row_amax) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * 4;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int64_t G = H >> 4;
+  const bool tensor = static_mode || given_scale;
+  const bool every = !tensor && (tok_scale || row_amax);   // every token's scale or absmax is asked for
   if (static_mode && tok_scale && wid == 0 && lane == 0) tok_scale[0] = static_scale;
   for (int64_t t = wid; t < T; t += nw) {
     const uint16_t* row = x + t * H;
@@ -363,7 +370,7 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* _
     if (lane < k) my_r = inv_pos[t * k + lane];
     if (my_r >= M_cap) my_r = -1;
     const uint64_t m = __ballot(my_r >= 0);
-    if (m == 0 && !(tok_scale && !static_mode)) continue;
+    if (m == 0 && !every) continue;
     float amax = 0.0f;
     if constexpr (GPL > 0) {
       float v[GPL][16];
@@ -381,16 +388,17 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* _
         }
       }
       amax = wave_max(amax);
-      const float s = static_mode ? static_scale : scale_from_amax(amax);
+      const float s = given_scale ? *given_scale : static_mode ? static_scale : scale_from_amax(amax);
       const RowDiv d(s);
 #pragma unroll
       for (int c = 0; c < GPL; ++c) {
         const int64_t gi = lane + 64 * c;
         if (gi < G) scatter_codes(xs, H, gi, m, my_r, v[c], d);
       }
-      if (!static_mode) {
+      if (!tensor) {
         if (my_r >= 0 && ss) ss[my_r] = s;
         if (tok_scale && lane == 0) tok_scale[t] = s;
+        if (row_amax && lane == 0) row_amax[t] = amax;
       }
     } else {
       for (int64_t gi = lane; gi < G; gi += 64) {
@@ -400,16 +408,17 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* _
         for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
       }
       amax = wave_max(amax);
-      const float s = static_mode ? static_scale : scale_from_amax(amax);
+      const float s = given_scale ? *given_scale : static_mode ? static_scale : scale_from_amax(amax);
       const RowDiv d(s);
       for (int64_t gi = lane; gi < G; gi += 64) {
         float v[16];
         load_group16<0>(row, gi, v);
         scatter_codes(xs, H, gi, m, my_r, v, d);
       }
-      if (!static_mode) {
+      if (!tensor) {
         if (my_r >= 0 && ss) ss[my_r] = s;
         if (tok_scale && lane == 0) tok_scale[t] = s;
+        if (row_amax && lane == 0) row_amax[t] = amax;
       }
     }
   }
@@ -418,7 +427,7 @@ __global__ __launch_bounds__(256) void quantize_scatter_kernel(const uint16_t* _
   for (int64_t r = n + wid; r < M_cap; r += nw) {
     uint4* dst = reinterpret_cast<uint4*>(xs + r * H);
     for (int64_t c = lane; c < (H >> 4); c += 64) dst[c] = make_uint4(0, 0, 0, 0);
-    if (ss && !static_mode && lane == 0) ss[r] = 0.0f;
+    if (ss && !tensor && lane == 0) ss[r] = 0.0f;
   }
 }
 
@@ -531,20 +540,25 @@ extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t 
 extern "C" int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_mode, float static_scale,
                                            const int32_t* expert_ids, int32_t k, int32_t E, int32_t group_offset,
                                            int32_t num_local_experts, int64_t M_cap, int32_t* perm, int32_t* inv_pos,
-                                           int32_t* group_sizes, uint8_t* xs, float* ss, float* scale, void* ws,
-                                           size_t ws_bytes, void* stream) {
+                                           int32_t* group_sizes, uint8_t* xs, float* ss, float* scale,
+                                           float* row_amax, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || k <= 0 || k > 64 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
   if (group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E) return MOE_ERR_SHAPE;
   if (M_cap < 0 || T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
   if (H <= 0 || H % 16) return MOE_ERR_SHAPE;
   if (scale_mode == MOE_SCALE_TENSOR_DYNAMIC) return MOE_ERR_UNSUPPORTED;   // needs the whole tensor first
-  if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_STATIC) return MOE_ERR_UNSUPPORTED;
+  if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_STATIC &&
+      scale_mode != MOE_SCALE_TENSOR_FROM_ROW_AMAX)
+    return MOE_ERR_UNSUPPORTED;
   const bool static_mode = scale_mode == MOE_SCALE_TENSOR_STATIC;
+  const bool from_rows = scale_mode == MOE_SCALE_TENSOR_FROM_ROW_AMAX;
+  const bool tensor = static_mode || from_rows;
   if (static_mode && !(static_scale > 0.0f && static_scale < 3.0e38f)) return MOE_ERR_SHAPE;
   const int64_t M = T * k;
   if (!group_sizes || !ws || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
   if (T > 0 && !x) return MOE_ERR_NULL;
-  if (M_cap > 0 && (!xs || (!static_mode && !ss))) return MOE_ERR_NULL;
+  if (M_cap > 0 && (!xs || (!tensor && !ss))) return MOE_ERR_NULL;
+  if (from_rows && (!scale || (T > 0 && !row_amax))) return MOE_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(x) % 16 != 0) return MOE_ERR_SHAPE;
   if (ws_bytes < moe::sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -559,8 +573,16 @@ extern "C" int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, 
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const int sm = static_mode ? 1 : 0;
   const int64_t G = H / 16, gpl = moe_cdiv(G, 64);
+  if (from_rows) {        // the tensor scale from the given token maxima, into scale[0]
+    moe::amax_scale_kernel<<<1, 1024, 0, st>>>(row_amax, T, scale);
+    MOE_CHECK_LAUNCH();
+  }
+  const float* given = from_rows ? scale : nullptr;
+  float* tok = from_rows ? nullptr : scale;
+  float* amax_out = tensor ? nullptr : row_amax;
 #define MOE_QS(GPL) \
-  moe::quantize_scatter_kernel<GPL><<<grid, block, 0, st>>>(xb, sm, static_scale, inv_pos, T, k, H, M_cap, hdr, xs, ss, scale)
+  moe::quantize_scatter_kernel<GPL><<<grid, block, 0, st>>>(xb, sm, static_scale, given, inv_pos, T, k, H, M_cap, \
+                                                             hdr, xs, ss, tok, amax_out)
   if (gpl <= 1) MOE_QS(1);
   else if (gpl <= 2) MOE_QS(2);
   else if (gpl <= 4) MOE_QS(4);

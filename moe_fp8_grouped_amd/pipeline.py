@@ -97,6 +97,7 @@ class ForwardPath:
         self.group_sizes = torch.empty(E, dtype=i32, device=device)
         self.xs = torch.empty((self.m_cap, H), dtype=u8, device=device)
         self.ss = torch.empty((self.m_cap,), dtype=f32, device=device)
+        self.xamax = torch.empty((T,), dtype=f32, device=device)      # tokens' absmax (fused row-mode pass)
         if cfg.pipeline == "ffn":
             # a and b are the column halves of one [m_cap, 2I] output
             self.w01 = concat_columns(self.w["wi_0"], self.w["wi_1"])
@@ -133,7 +134,8 @@ class ForwardPath:
             moe_quantize_sort_by_expert(self.x, self.T, self.H, self.act_mode, self.static_act, self.ids, self.k,
                                         self.E, self.g0, self.El, self.m_cap, self.perm, self.inv_pos,
                                         self.group_sizes, self.xs, self.ss if row else None,
-                                        None if row else self.xscale, self.ws_sort)
+                                        None if row else self.xscale, self.ws_sort,
+                                        row_amax=self.xamax if row else None)
             return
         moe_sort_by_expert(self.ids, self.T, self.k, self.E, self.g0, self.El, self.xq, self.xscale,
                            self.act_mode, self.H, self.m_cap, self.perm, self.inv_pos, self.group_sizes,
@@ -395,10 +397,18 @@ class FFNBackwardPath:
 
     def grad_w01(self):
         f, T, H = self.fwd, self.T, self.H
-        moe_quantize_rows(f.x, None, MOE_ACT_NONE, T, H, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.xq_t, self.xs_scale,
-                          None, self.ws_qx)
-        moe_sort_by_expert(f.ids, T, self.k, self.E, f.g0, f.El, self.xq_t, self.xs_scale, MOE_SCALE_TENSOR_DYNAMIC,
-                           H, self.m_cap, self.perm, self.inv_pos, self.group_sizes, self.xs_t, None, self.ws_sort)
+        if f.fused_quantize and f.act_mode == MOE_SCALE_ROW_DYNAMIC:
+            # x with one tensor scale (from the token maxima the forward's fused pass wrote), quantized
+            # straight into the sorted rows
+            moe_quantize_sort_by_expert(f.x, T, H, MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0, f.ids, self.k, self.E, f.g0,
+                                        f.El, self.m_cap, self.perm, self.inv_pos, self.group_sizes, self.xs_t, None,
+                                        self.xs_scale, self.ws_sort, row_amax=f.xamax)
+        else:
+            moe_quantize_rows(f.x, None, MOE_ACT_NONE, T, H, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.xq_t, self.xs_scale,
+                              None, self.ws_qx)
+            moe_sort_by_expert(f.ids, T, self.k, self.E, f.g0, f.El, self.xq_t, self.xs_scale,
+                               MOE_SCALE_TENSOR_DYNAMIC, H, self.m_cap, self.perm, self.inv_pos, self.group_sizes,
+                               self.xs_t, None, self.ws_sort)
         self._tgmm(self.xs_t, self.xs_scale, self.dabq_t, self.dabs_t, H, 2 * self.I, self.dw01, self.ws_tgmm_01)
 
     def grad_x(self):
@@ -416,7 +426,7 @@ class FFNBackwardPath:
         self.grad_x()
 
     OUTPUTS = ("dy", "dw_router", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax", "dh", "hq_t", "hs_t", "dwo", "dab",
-               "dabq_r", "dabs_r", "dabq_t", "dabs_t", "dab_amax", "dxs", "xq_t", "xs_scale", "perm", "inv_pos",
+               "dabq_r", "dabs_r", "dabq_t", "dabs_t", "dab_amax", "dxs", "xs_scale", "perm", "inv_pos",
                "group_sizes", "xs_t", "dw01", "dx")
 
     def capture_graph(self, warmup=1):

@@ -127,14 +127,17 @@ def test_sort_validation(lib):
 def test_quantize_sort_validation(lib):
     f = lambda *a: _c(lib, "moe_quantize_sort_by_expert", *a)
     al = 4096   # 16-byte aligned dummy pointer: never dereferenced on these paths
-    def call(x=al, T=4, H=32, mode=0, static=0.0, k=2, E=8, g0=0, El=8, M_cap=8, xs=al, ss=al, ws=al, wsb=1 << 20):
-        return f(x, T, H, mode, static, al, k, E, g0, El, M_cap, al, al, al, xs, ss, None, ws, wsb, None)
+    def call(x=al, T=4, H=32, mode=0, static=0.0, k=2, E=8, g0=0, El=8, M_cap=8, xs=al, ss=al, ws=al, wsb=1 << 20,
+             scale=None, amax=None):
+        return f(x, T, H, mode, static, al, k, E, g0, El, M_cap, al, al, al, xs, ss, scale, amax, ws, wsb, None)
     assert call(H=24) == m.MOE_ERR_SHAPE
     assert call(mode=1) == m.MOE_ERR_UNSUPPORTED          # tensor-dynamic needs the whole tensor first
     assert call(mode=2, static=-1.0) == m.MOE_ERR_SHAPE
     assert call(x=None) == m.MOE_ERR_NULL
     assert call(xs=None) == m.MOE_ERR_NULL
     assert call(ss=None) == m.MOE_ERR_NULL                # row mode needs the row scales
+    assert call(mode=3, scale=al) == m.MOE_ERR_NULL       # the tokens' maxima are needed
+    assert call(mode=3, amax=al) == m.MOE_ERR_NULL        # and somewhere to put the tensor scale
     assert call(x=al + 8) == m.MOE_ERR_SHAPE              # misaligned rows
     assert call(wsb=16) == m.MOE_ERR_WORKSPACE
     assert call(E=0) == m.MOE_ERR_SHAPE

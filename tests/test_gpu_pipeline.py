@@ -361,8 +361,9 @@ def test_gated_ffn_backward_stagewise(shape, fuse):
     dxs = host(bwd.dxs)
     _sampled_gmm(q2, s2, w01T_q, w01T_s, gs, E, dxs, 3, P, "dx sorted")
     # dw01 = x^T [da|db], x requantized with one tensor scale and sorted
-    xq, xsc, _ = quantize_rows(data["x"], SCALE_TENSOR_DYNAMIC)
-    assert_bits_equal(host(bwd.xq_t), xq, "x tensor q")
+    xq, xsc, xam = quantize_rows(data["x"], SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(host(fwd.xamax), xam, "x token maxima (forward's fused pass)")
+    assert_bits_equal(host(bwd.xs_scale), xsc, "x tensor scale")
     srt = sort_by_expert(data["ids"], E, 0, E, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_DYNAMIC, m_cap=Mc)
     assert_bits_equal(host(bwd.xs_t), srt["xs"], "x sorted")
     _sampled_tgmm(srt["xs"], xsc, q2t, s2t, gs, E, host(bwd.dw01), 4, P, "dw01")

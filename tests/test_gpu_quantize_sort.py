@@ -196,6 +196,8 @@ def test_silu_every_finite_bf16_gate_value():
     (500, 2, 8, 0, 8, 512, 2, 5, True),             # static scale
     (300, 3, 5, 1, 3, 8208, 0, 3, False),           # rows too long for registers (two passes)
     (0, 4, 8, 0, 8, 64, 0, 4, False),               # no tokens: the window is all zeros
+    (4096, 8, 64, 0, 64, 2048, 3, 0, True),         # one tensor scale from the tokens' maxima
+    (2000, 8, 256, 64, 32, 7168, 3, 37, True),      # the same on a local slice
 ])
 def test_quantize_sort_fused_bit_exact(T, k, E, g0, El, H, mode, extra, want_scale):
     """moe_quantize_sort_by_expert writes what moe_quantize_rows then
@@ -207,20 +209,25 @@ def test_quantize_sort_fused_bit_exact(T, k, E, g0, El, H, mode, extra, want_sca
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32) if T else \
         np.zeros((0, k), np.int32)
     static = STATIC_ACT_SCALE if mode == m.MOE_SCALE_TENSOR_STATIC else None
-    xq, xsc, _ = quantize_rows(x, mode, static_scale=static)
+    from_rows = mode == m.MOE_SCALE_TENSOR_FROM_ROW_AMAX
+    xq, xsc, xam = quantize_rows(x, SCALE_TENSOR_DYNAMIC if from_rows else mode, static_scale=static)
     n = int(((ids >= g0) & (ids < g0 + El)).sum())
     m_cap = n + extra
-    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc, xscale_mode=mode, m_cap=m_cap)
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_DYNAMIC if from_rows else mode,
+                       m_cap=m_cap)
     dev = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
     perm, inv = dev(T * k, torch.int32), dev(T * k, torch.int32)
     gs = dev(E, torch.int32)
     xs = torch.full((m_cap, H), 0x55, dtype=torch.uint8, device="cuda")
     ss = torch.full((m_cap,), 7.0, dtype=torch.float32, device="cuda") if mode == m.MOE_SCALE_ROW_DYNAMIC else None
     sc = dev((T if mode == m.MOE_SCALE_ROW_DYNAMIC else 1,), torch.float32) if want_scale else None
+    amax = dev((T,), torch.float32) if mode == m.MOE_SCALE_ROW_DYNAMIC and want_scale else None
+    if from_rows:
+        amax = dev_f32(xam)                          # the tokens' maxima, as a row-mode pass writes them
     ws = m.workspace(m.MOE_OP_SORT_BY_EXPERT, T * k, 0, 0, E)
     print(f"quantize+sort T={T} k={k} E={E} g0={g0} El={El} H={H} mode={mode} m_cap={m_cap}", flush=True)
     m.moe_quantize_sort_by_expert(dev_bf16(x) if T else dev((0, H), torch.bfloat16), T, H, mode, static or 0.0,
-                                  dev_i32(ids), k, E, g0, El, m_cap, perm, inv, gs, xs, ss, sc, ws)
+                                  dev_i32(ids), k, E, g0, El, m_cap, perm, inv, gs, xs, ss, sc, ws, row_amax=amax)
     assert m.moe_debug_check(ws) == 0
     assert_bits_equal(host(perm), o["perm"], "perm")
     assert_bits_equal(host(inv), o["inv_pos"], "inv_pos")
@@ -230,6 +237,8 @@ def test_quantize_sort_fused_bit_exact(T, k, E, g0, El, H, mode, extra, want_sca
         assert_bits_equal(host(ss), o["ss"], "ss")
     if sc is not None:
         assert_bits_equal(host(sc), xsc, "token scales")
+    if amax is not None and mode == m.MOE_SCALE_ROW_DYNAMIC:
+        assert_bits_equal(host(amax), xam, "token maxima")
 
 
 def test_empty_rows_tensor_dynamic():
