@@ -547,7 +547,7 @@ def main():
                     help="run a plain copy of this many MiB first (profiler byte-counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {a.gpus}); expert parallelism is modelled "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for {a.gpus}); expert parallelism is modelled "
               f"as one GPU's expert slice", file=sys.stderr)
         sys.exit(2)
     res, cfg = run_gpu(a.config, a.steps, a.warmup, a.calib_copy_mib)
