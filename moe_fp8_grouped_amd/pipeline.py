@@ -264,6 +264,25 @@ class BackwardPath:
         self.grad_input()
         self.grad_weight()
 
+    OUTPUTS = ("xq", "xscale", "perm", "inv_pos", "group_sizes", "xs", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax",
+               "dx", "dw")
+
+    def capture_graph(self, warmup=1):
+        """Record one backward step into a HIP graph (every buffer it writes is
+        fully rewritten by it, so replays equal eager steps)."""
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+
 
 class FFNBackwardPath:
     """The gated FFN's backward after a forward step of ``fwd`` (a

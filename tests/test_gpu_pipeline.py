@@ -400,6 +400,30 @@ def test_gated_ffn_backward_hip_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_backward_config5_hip_graph_replays_match_eager():
+    """The up-projection backward (reduced config-5 shape) as a HIP graph: every
+    replay, with scribbled outputs and eager steps between, leaves the eager
+    step's bits in every buffer the step writes."""
+    cfg = scaled_config(5, T=512, H=512, E=8, k=4, I=256)
+    data = generate(cfg)
+    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE)
+    print("config 5 backward graph replays", flush=True)
+    path.step()
+    torch.cuda.synchronize()
+    ref = {k: getattr(path, k).clone() for k in path.OUTPUTS}
+    path.capture_graph(warmup=1)
+    for rep in range(3):
+        for k in path.OUTPUTS:
+            getattr(path, k).view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        path.replay()
+        torch.cuda.synchronize()
+        for k in path.OUTPUTS:
+            assert torch.equal(getattr(path, k).view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+        path.step()
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("cid", [2, 4])
 def test_forward_step_hip_graph_replays_match_eager(cid):
     """The bench's timed step is a HIP graph of the forward step: every
