@@ -372,6 +372,46 @@ def test_gated_ffn_backward_stagewise(shape, fuse):
     check_bf16(host(bwd.dx), o["out"], o["abs_sum"], 0.0, "dx")
 
 
+def test_expert_slice_with_no_routed_rows_forward_and_backward():
+    """One GPU's expert slice that no token routes to (n = 0) with spare row
+    capacity: the sort metadata matches the oracle's, every expert row and
+    partial sum is zero, the zero rows requantize to code 0 with scale 1, and
+    every gradient of the backward is zero."""
+    cfg = scaled_config(4, T=256, H=512, E=16, k=2, I=256, group_offset=4, num_local_experts=4)
+    data = generate(cfg)
+    rng = np.random.default_rng(11)
+    others = np.setdiff1d(np.arange(cfg.E), np.arange(4, 8))
+    data["ids"] = np.stack([rng.permutation(others)[:cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    Mc = 256
+    fwd = ForwardPath(cfg, data, m_cap=Mc)
+    print(f"expert slice with no routed rows: m_cap={Mc} fused={fwd.fused_quantize}", flush=True)
+    fwd.step()
+    torch.cuda.synchronize()
+    assert m.moe_debug_check(fwd.ws_sort) == 0 and m.moe_debug_check(fwd.ws_gmm) == 0
+    srt = sort_by_expert(data["ids"], cfg.E, 4, 4, m_cap=Mc)
+    assert srt["n"] == 0
+    assert_bits_equal(host(fwd.perm), srt["perm"], "perm")
+    assert_bits_equal(host(fwd.inv_pos), srt["inv_pos"], "inv_pos")
+    assert_bits_equal(host(fwd.group_sizes), srt["group_sizes"], "group_sizes")
+    assert not host(fwd.ab).any() and not host(fwd.y).any() and not host(fwd.out).any()
+    hq, hs, _ = quantize_rows(host(fwd.a), SCALE_ROW_DYNAMIC, x_up_bits=host(fwd.b))
+    assert_bits_equal(host(fwd.hq), hq, "hq")
+    assert_bits_equal(host(fwd.hs), hs, "hs")
+    assert (hs == 1.0).all()
+    dout = dev_bf16(to_bf16_bits(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)))
+    bwd = FFNBackwardPath(fwd, data, dout)
+    bwd.step()
+    torch.cuda.synchronize()
+    for name in ("dy", "dw_router", "dh", "dwo", "dab", "dxs", "dw01", "dx"):
+        assert not host(getattr(bwd, name)).any(), name
+    q2, s2, _ = quantize_rows(host(bwd.dab), SCALE_ROW_DYNAMIC)
+    assert_bits_equal(host(bwd.dabq_r), q2, "[da|db] row q")
+    assert_bits_equal(host(bwd.dabs_r), s2, "[da|db] row scale")
+    q2t, s2t, _ = quantize_rows(host(bwd.dab), SCALE_TENSOR_DYNAMIC)
+    assert_bits_equal(host(bwd.dabq_t), q2t, "[da|db] tensor q")
+    assert_bits_equal(host(bwd.dabs_t), s2t, "[da|db] tensor scale")
+
+
 def test_gated_ffn_backward_hip_graph_replays_match_eager():
     """The backward step as a HIP graph: every replay, with scribbled outputs
     and eager steps between replays, leaves the eager step's bits in every
