@@ -761,6 +761,39 @@ __device__ __forceinline__ void store_rows(const OutPieces<C, OUT_BF16>& o, int 
   }
 }
 
+// Row block i of a converted float32 tile, written as whole 128-byte lines.
+// A lane's pieces of column blocks 2p and 2p+1 lie 64 bytes apart in its
+// row (row r = lane % 16), so storing them as they are fills each line of a
+// row with two stores.  Lanes r and 15 - r (one in each half of the 16 rows)
+// swap one piece over the DPP row mirror: lane r < 8 keeps block 2p of row r
+// and receives block 2p of row 15 - r; lane r >= 8 keeps block 2p + 1 of row
+// r and receives block 2p + 1 of row 15 - r.  The first store then covers
+// rows 0..7 and the second rows 8..15, each row's 128 bytes whole.
+// voff_a, voff_b = the byte offsets (from the tile's first row) of the
+// lane's piece in row block 0 for the two stores: rows min(r, 15 - r) and
+// max(r, 15 - r), at byte 64 (r / 8) + 16 (lane / 16) of the column range.
+template <class C, int POL = 0>
+__device__ __forceinline__ void store_rows_lines(const OutPieces<C, false>& o, int i, __amdgpu_buffer_rsrc_t r,
+                                                 uint32_t voff_a, uint32_t voff_b, uint32_t row_bytes, bool upper) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  static_assert(C::JN % 2 == 0, "pairs of column blocks");
+#pragma unroll
+  for (int p = 0; p < C::JN / 2; ++p) {
+    const uint4 p0 = o.v[i][2 * p], p1 = o.v[i][2 * p + 1];
+    const uint4 x = upper ? p0 : p1;              // the piece the mirrored lane stores
+    uint4 y;
+    y.x = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.x), 0x140, 0xF, 0xF, false));
+    y.y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.y), 0x140, 0xF, 0xF, false));
+    y.z = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.z), 0x140, 0xF, 0xF, false));
+    y.w = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x.w), 0x140, 0xF, 0xF, false));
+    const uint4 a = upper ? y : p0;               // rows 0..7
+    const uint4 b = upper ? p1 : y;               // rows 8..15
+    const uint32_t blk = 16 * i * row_bytes + p * 128;
+    __builtin_amdgcn_raw_buffer_store_b128(u4{a.x, a.y, a.z, a.w}, r, voff_a + blk, 0, POL);
+    __builtin_amdgcn_raw_buffer_store_b128(u4{b.x, b.y, b.z, b.w}, r, voff_b + blk, 0, POL);
+  }
+}
+
 template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH>
 __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
     const uint8_t* __restrict__ lhs, const float* __restrict__ ls, int ls_per_row, const uint8_t* __restrict__ rhs,
@@ -1017,9 +1050,19 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
       p_rsrc = tile_rsrc(static_cast<uint8_t*>(out) + (BATCH ? static_cast<int64_t>(Cd.g) * M * row_bytes : 0) +
                              Cd.row0 * row_bytes,
                          static_cast<uint32_t>(Cd.rows_here * row_bytes));
-      p_voff = static_cast<uint32_t>((rbase + (lane & 15)) * row_bytes + (Cd.col0 + cbase) * ESZ + 16 * (lane >> 4));
+      if constexpr (!OUT_BF16) {
+        const int r = lane & 15;
+        const bool upper = r >= 8;
+        const uint32_t colb = static_cast<uint32_t>((Cd.col0 + cbase) * ESZ + 64 * (upper ? 1 : 0) + 16 * (lane >> 4));
+        const uint32_t va = static_cast<uint32_t>((rbase + (upper ? 15 - r : r)) * row_bytes) + colb;
+        const uint32_t vb = static_cast<uint32_t>((rbase + (upper ? r : 15 - r)) * row_bytes) + colb;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16, SPOL>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+        for (int i = 0; i < MI; ++i) store_rows_lines<C, SPOL>(po, i, p_rsrc, va, vb, static_cast<uint32_t>(row_bytes), upper);
+      } else {
+        p_voff = static_cast<uint32_t>((rbase + (lane & 15)) * row_bytes + (Cd.col0 + cbase) * ESZ + 16 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < MI; ++i) store_rows<C, OUT_BF16, SPOL>(po, i, p_rsrc, p_voff, static_cast<uint32_t>(row_bytes));
+      }
       st_now = true;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
