@@ -500,7 +500,9 @@ def secondary_backward(steps, warmup):
         path.replay()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    by = {"quantize_x_and_sort": T * H * 3 + 4 + (M * 4 + 2 * M * 4 + E * 4 + T * H + M * H),
+    # fused: x read once, the sorted codes written; else the [T, H] codes are written and read back
+    qx = T * H * 2 + 4 if path.fused_quantize else T * H * 3 + 4 + T * H
+    by = {"quantize_x_and_sort": qx + (M * 4 + 2 * M * 4 + E * 4 + M * H),
           "quantize_dy_row_and_tensor": (M * I * 3 + M * 4) + (M * I * 2 + M * I * 3 + 4),
           "gmm_dx": M * I + E * I * H + M * H * 2 + M * 4 + E * 4,
           "tgmm_dw": M * H + M * I + E * H * I * 4}

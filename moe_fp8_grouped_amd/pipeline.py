@@ -201,8 +201,11 @@ class ForwardPath:
 class BackwardPath:
     """Config-5 backward: dX = gmm(dY, W^T), dW = tgmm(X_sorted, dY)."""
 
-    def __init__(self, cfg, data, static_act, static_weight, device="cuda", dw_dtype=MOE_F32):
+    def __init__(self, cfg, data, static_act, static_weight, device="cuda", dw_dtype=MOE_F32, fused_quantize=True):
         self.cfg, self.dev = cfg, device
+        # X quantized with its static scale inside the sort's gather (True), or
+        # to [T, H] codes by a pass of its own first
+        self.fused_quantize = bool(fused_quantize)
         T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
         self.T, self.H, self.E, self.k, self.I = T, H, E, k, I
         self.M = T * k
@@ -236,6 +239,11 @@ class BackwardPath:
         self.ws_tgmm = workspace(MOE_OP_TGMM, self.M, H, I, E, device=device)
 
     def quantize_and_sort(self):
+        if self.fused_quantize:
+            moe_quantize_sort_by_expert(self.x, self.T, self.H, MOE_SCALE_TENSOR_STATIC, self.static_act, self.ids,
+                                        self.k, self.E, self.g0, self.El, self.M, self.perm, self.inv_pos,
+                                        self.group_sizes, self.xs, None, self.xscale, self.ws_sort)
+            return
         moe_quantize_rows(self.x, None, MOE_ACT_NONE, self.T, self.H, MOE_SCALE_TENSOR_STATIC, self.static_act,
                           self.xq, self.xscale, None, None)
         moe_sort_by_expert(self.ids, self.T, self.k, self.E, self.g0, self.El, self.xq, self.xscale,
@@ -264,8 +272,11 @@ class BackwardPath:
         self.grad_input()
         self.grad_weight()
 
-    OUTPUTS = ("xq", "xscale", "perm", "inv_pos", "group_sizes", "xs", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax",
-               "dx", "dw")
+    @property
+    def OUTPUTS(self):
+        return ((() if self.fused_quantize else ("xq",)) +
+                ("xscale", "perm", "inv_pos", "group_sizes", "xs", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax",
+                 "dx", "dw"))
 
     def capture_graph(self, warmup=1):
         """Record one backward step into a HIP graph (every buffer it writes is

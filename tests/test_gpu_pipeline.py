@@ -239,17 +239,20 @@ def test_expert_slice_pipeline_config4_stagewise():
 
 
 @pytest.mark.timeout(600)
-def test_backward_pipeline_config5_stagewise():
+@pytest.mark.parametrize("fused", [True, False])
+def test_backward_pipeline_config5_stagewise(fused):
     cfg = CONFIGS[5]
     data = generate(cfg)
-    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE)
-    print("pipeline config 5 backward", flush=True)
+    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, fused_quantize=fused)
+    print(f"pipeline config 5 backward fused={fused}", flush=True)
     path.step()
     torch.cuda.synchronize()
     wq, ws_ = quantize_weights(data["weights"]["w_up"], 1, 1, static_scale=STATIC_WEIGHT_SCALE)
     assert_bits_equal(host(path.w.q), wq, "w q")
     xq, xsc, _ = quantize_rows(data["x"], SCALE_TENSOR_STATIC, static_scale=STATIC_ACT_SCALE)
-    assert_bits_equal(host(path.xq), xq, "xq")
+    if not fused:                      # the fused pass writes no [T, H] codes
+        assert_bits_equal(host(path.xq), xq, "xq")
+    assert_bits_equal(host(path.xscale), xsc, "xscale")
     srt = sort_by_expert(data["ids"], cfg.E, 0, cfg.E, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_STATIC)
     assert_bits_equal(host(path.xs), srt["xs"], "xs")
     dq_r, ds_r, _ = quantize_rows(data["dy"], SCALE_ROW_DYNAMIC)
