@@ -566,13 +566,13 @@ def main():
     if not a.no_secondary:
         torch.cuda.empty_cache()
         res["secondary"] = {"gated_ffn_fwd_cold": secondary_rotating_sets(a.steps, 2),
-                            "ep_slice_forward": secondary_ep_slice(min(a.steps, 10), 2),
-                            "backward": secondary_backward(min(a.steps, 10), 2),
+                            "ep_slice_forward": secondary_ep_slice(min(a.steps, 50), 5),
+                            "backward": secondary_backward(min(a.steps, 50), 5),
                             "tiny_up_proj": secondary_up_proj(1, False, a.steps, a.warmup),
                             "tiny_zipf_blockwise": secondary_up_proj(3, False, a.steps, a.warmup),
                             "tiny_zipf_blockwise_static": secondary_up_proj(3, True, a.steps, a.warmup),
-                            "skewed_large_blockwise": secondary_up_proj(6, False, min(a.steps, 10), 2),
-                            "skewed_large_blockwise_static": secondary_up_proj(6, True, min(a.steps, 10), 2)}
+                            "skewed_large_blockwise": secondary_up_proj(6, False, min(a.steps, 50), 5),
+                            "skewed_large_blockwise_static": secondary_up_proj(6, True, min(a.steps, 50), 5)}
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, a.cpu_tokens)
     print(json.dumps(res), flush=True)
