@@ -605,8 +605,9 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
 //    the next step's SLOTS (+1 blockwise scale) loads, plus one when that
 //    step starts a tile.
 //  * The epilogue writes the output from registers, since the stages in
-//    flight occupy the LDS: float32 as one 16-byte store per 16 x 16 block
-//    and lane; bfloat16 after two lane swaps per dword pair
+//    flight occupy the LDS: float32 as 16-byte stores per lane, after a DPP
+//    row-mirror swap that makes each store cover whole 128-byte lines of 8
+//    rows (store_rows_lines); bfloat16 after two lane swaps per dword pair
 //    (v_permlane32_swap, then v_permlane16_swap), which turn a lane's two
 //    blocks' four-column pieces into eight consecutive columns of its row --
 //    again one 16-byte store.
