@@ -133,12 +133,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
-  return v;
-}
-
 // Sticky device-error word: OR a bit into the first int32 of a workspace.
 __device__ __forceinline__ void raise_error(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);

@@ -273,11 +273,13 @@ __global__ __launch_bounds__(256) void gather_reduce_bwd_kernel(
     part = wave_sum(part);
     if (lane == 0) dw[f] = part;
   }
-  // rows [n, M_cap) of dy are zero (n from the local group sizes; negative ones count as 0)
-  int own = 0;
+  // rows [n, M_cap) of dy are zero (n from the local group sizes; negative ones count as 0; summed in
+  // 64 bits, so sizes adding up past 2^31 cannot wrap n below 0)
+  int64_t own = 0;
   for (int g = lane; g < El; g += 64) own += max(gs[g0 + g], 0);
-  int64_t n = wave_sum_int(own);
-  if (n > M_cap) n = M_cap;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) own += __shfl_xor(own, o, 64);
+  const int64_t n = own < M_cap ? own : M_cap;
   for (int64_t r = n + wid; r < M_cap; r += nw) {
     uint4* row = reinterpret_cast<uint4*>(dy + r * N);
     for (int64_t ch = lane; ch < nch; ch += 64) row[ch] = make_uint4(0, 0, 0, 0);

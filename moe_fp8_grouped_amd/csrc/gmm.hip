@@ -1457,6 +1457,8 @@ extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_s
       group_offset + num_local_experts > E)
     return MOE_ERR_SHAPE;
   if (M > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  // the tile table of any split of M rows into El groups stays below 2^31 entries
+  if ((moe_cdiv(M, 128) + num_local_experts + 1) * (N / 128) > INT32_MAX) return MOE_ERR_SHAPE;
   if (Kb <= 0 || Nb <= 0 || K % Kb || N % Nb) return MOE_ERR_SHAPE;
   if (Kb > 1 && (K / Kb) % 128) return MOE_ERR_UNSUPPORTED;
   if (lhs_scale_mode != MOE_SCALE_ROW_DYNAMIC && lhs_scale_mode != MOE_SCALE_TENSOR_DYNAMIC &&

@@ -80,6 +80,31 @@ __device__ void wave0_scan(const int* v, int* out, int n) {
   if (lane == 0) out[n] = carry;
 }
 
+// Exclusive scan of v[0..n) (every v >= 0) into out[0..n] by wave 0,
+// saturating at cap: out[i] = min(v[0] + ... + v[i-1], cap), out[n] =
+// min(total, cap).  The running sums are 64-bit (n <= 1024 values below 2^31
+// stay below 2^41), so sizes that add up past 2^31 cannot wrap; cap < 2^31.
+// Returns (in lane 0 of wave 0) whether the total exceeded cap.
+__device__ bool wave0_scan_sat(const int* v, int* out, int n, int64_t cap) {
+  if (threadIdx.x >= 64) return false;
+  const int lane = threadIdx.x;
+  int64_t carry = 0;
+  for (int b = 0; b < n; b += 64) {
+    const int i = b + lane;
+    const int64_t x = i < n ? v[i] : 0;
+    int64_t incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (i < n) out[i] = static_cast<int>(min(carry + incl - x, cap));
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) out[n] = static_cast<int>(min(carry, cap));
+  return carry > cap;
+}
+
 // Tiles of a group of m rows.  Plain: ceil(m / bm) m-tiles per n-tile.  With
 // wide tails (gmm): full m-tiles of bm rows, and a remainder of at most bm/2
 // rows is covered by tiles of bm/2 rows x two n-tiles (an odd last n-tile
@@ -91,10 +116,13 @@ __device__ __forceinline__ int group_tiles(int m, int bm, int nt, bool wide_tail
   return (nt / 2) * (2 * full + 1) + (nt & 1) * (full + 1);
 }
 
-// Fill the table: clamps negative sizes and rows past max_rows (flagging
-// the error word) so that every tile stays inside the buffers; a group of m
-// rows owns group_tiles(m, bm, tiles_per_mrow, wide_tail) tiles
-// (tiles_per_mrow = 0: one entry per group).
+// Fill the table: clamps negative sizes to 0 and the row offsets to
+// max_rows (flagging the error word) so that every tile stays inside the
+// buffers -- the offsets are a saturating 64-bit scan, so group sizes whose
+// sum passes 2^31 cannot wrap into a table that points outside the buffer;
+// a group of m rows owns group_tiles(m, bm, tiles_per_mrow, wide_tail) tiles
+// (tiles_per_mrow = 0: one entry per group).  The host bounds the tile count
+// of max_rows rows below 2^31.
 template <class GT>
 __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, int El, int64_t max_rows,
                              int tiles_per_mrow, int bm, int32_t* err, GT& gt, int* tmp,
@@ -108,20 +136,8 @@ __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, in
     tmp[g] = m;
   }
   __syncthreads();
-  wave0_scan(tmp, gt.rows_off, El);
-  __syncthreads();
-  for (int g = threadIdx.x; g < El; g += blockDim.x) {
-    int64_t lo = gt.rows_off[g], hi = gt.rows_off[g + 1];
-    if (hi > max_rows) {
-      if (blockIdx.x == 0) raise_error(err, MOE_DEVERR_ROWS);
-      hi = max_rows;
-      if (lo > hi) lo = hi;
-    }
-    tmp[g] = static_cast<int>(hi - lo);   // clamped rows
-  }
-  __syncthreads();
-  // recompute offsets from clamped sizes; then tiles
-  wave0_scan(tmp, gt.rows_off, El);
+  const bool over = wave0_scan_sat(tmp, gt.rows_off, El, max_rows);
+  if (over && threadIdx.x == 0 && blockIdx.x == 0) raise_error(err, MOE_DEVERR_ROWS);
   __syncthreads();
   for (int g = threadIdx.x; g < El; g += blockDim.x) {
     const int m = gt.rows_off[g + 1] - gt.rows_off[g];

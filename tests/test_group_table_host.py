@@ -1,0 +1,101 @@
+"""The grouped matmuls' local group table, replayed on the host.
+
+Every gmm / tgmm workgroup builds its table from the caller's group_sizes
+(device data, unchecked): negative sizes count as 0, the row offsets are a
+64-bit exclusive scan saturated at the row bound, and each group owns a
+number of tiles.  This replays that arithmetic with the device's integer
+widths (int32 table entries, 64-bit running sums) and checks that no row or
+tile of any table leaves the buffer, whatever the sizes -- including sizes
+whose sum passes 2^31, where a 32-bit running sum wraps."""
+
+import numpy as np
+import pytest
+
+import moe_fp8_grouped_amd as m
+
+I32 = np.iinfo(np.int32)
+
+
+def group_tiles(mr, bm, nt, wide_tail):
+    if nt <= 0:
+        return 1
+    full, rem = mr // bm, mr % bm
+    if not wide_tail or rem == 0 or rem > bm // 2:
+        return (full + (1 if rem else 0)) * nt
+    return (nt // 2) * (2 * full + 1) + (nt & 1) * (full + 1)
+
+
+def build_groups(sizes, max_rows, nt, bm, wide_tail):
+    """The table as the device builds it: (rows_off, tiles_off, rows flag, size flag)."""
+    v = np.asarray(sizes, np.int64)
+    neg = bool((v < 0).any())
+    v = np.maximum(v, 0)
+    incl = np.cumsum(v)                                   # 64-bit: at most 1024 * 2^31
+    rows_off = np.minimum(np.concatenate([[0], incl]), max_rows).astype(np.int32)
+    over = bool(incl[-1] > max_rows) if v.size else False
+    rows = np.diff(rows_off.astype(np.int64))
+    tiles = np.array([group_tiles(int(r), bm, nt, wide_tail) for r in rows], np.int64)
+    tiles_off = np.concatenate([[0], np.cumsum(tiles)])
+    assert tiles_off[-1] <= I32.max, "the host bound keeps the tile count in int32"
+    return rows_off, tiles_off.astype(np.int32), over, neg
+
+
+def wrapping_rows_off(sizes):
+    """A 32-bit running sum, for contrast: it wraps past 2^31."""
+    v = np.maximum(np.asarray(sizes, np.int64), 0)
+    s = np.concatenate([[0], np.cumsum(v)])
+    return ((s + 2 ** 31) % 2 ** 32 - 2 ** 31).astype(np.int64)
+
+
+CASES = [
+    [1 << 30] * 3,
+    [I32.max] * 1024,
+    [5, -7, 2 ** 31 - 1, 3],
+    [0] * 64,
+    [300, 0, 1, 129, 256, 384],
+    list(np.random.default_rng(0).integers(-10, 2 ** 31 - 1, 1024)),
+]
+
+
+@pytest.mark.parametrize("sizes", CASES)
+@pytest.mark.parametrize("max_rows,nt,bm,wide", [(1000, 2, 256, True), (8192, 32, 256, True), (40960, 1, 128, False),
+                                                 (2 ** 31 - 2, 16, 256, False)])
+def test_table_stays_inside_the_buffer(sizes, max_rows, nt, bm, wide):
+    if (max_rows // 128 + len(sizes) + 1) * nt > I32.max:
+        pytest.skip("rejected by the host's tile-count bound")
+    rows_off, tiles_off, over, neg = build_groups(sizes, max_rows, nt, bm, wide)
+    assert rows_off[0] == 0 and (np.diff(rows_off) >= 0).all() and rows_off[-1] <= max_rows
+    v = np.maximum(np.asarray(sizes, np.int64), 0)
+    assert rows_off[-1] == min(int(v.sum()), max_rows)
+    assert over == (int(v.sum()) > max_rows)
+    assert neg == any(x < 0 for x in sizes)
+    # every tile's rows lie inside [0, max_rows): a group's tiles cover its rows only
+    for g in range(len(sizes)):
+        r0, r1 = int(rows_off[g]), int(rows_off[g + 1])
+        assert 0 <= r0 <= r1 <= max_rows
+        assert tiles_off[g + 1] - tiles_off[g] == group_tiles(r1 - r0, bm, nt, wide)
+
+
+def test_a_32_bit_running_sum_would_leave_the_buffer():
+    """Why the scan is 64-bit and saturating: with [2^30] * 3 a 32-bit running
+    sum makes group 2 start at -2^31 and ends the table below zero."""
+    off = wrapping_rows_off([1 << 30] * 3)
+    assert off[2] < 0 and off[3] < 0
+    rows_off, _, over, _ = build_groups([1 << 30] * 3, 1000, 2, 256, True)
+    assert list(rows_off) == [0, 1000, 1000, 1000] and over
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import os
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libmoefp8.so not built")
+    return m.load_library()
+
+
+def test_gmm_rejects_tile_tables_past_int32(lib):
+    """The host bound that keeps the table's tile count in int32."""
+    one = 1
+    M, N, K = 2 ** 31 - 2, 128 * 1024, 128
+    st = lib.moe_gmm_fp8(one, one, 0, one, one, 1, N, 1, one, 8, 0, 8, M, K, N, 0, one, one, 256, None)
+    assert st == m.MOE_ERR_SHAPE
