@@ -111,3 +111,31 @@ def gmm_samples(lhs_q, lhs_scale, rhs_q, rhs_scale, group_sizes, g0, El, rows, c
                 acc = (s_col[:, b].astype(np.float64) * pb.astype(np.float64) + acc).astype(np.float32)
             out[sel] = lsr * acc
     return out
+
+
+def tgmm_samples(lhs_q, lhs_scale, rhs_q, rhs_scale, group_sizes, g0, El, gi, ki, ci):
+    """The modelled float32 tgmm output dW[g, k, c] at sampled (gi, ki, ci):
+    the group's rows are the contraction, chunked from the group's first row
+    (the kernels start every group on a chunk boundary and pad with zeros),
+    one accumulator, then ls[k] * (acc * rs[c])."""
+    gs = np.asarray(group_sizes, np.int64)[g0:g0 + El]
+    offs = np.concatenate([[0], np.cumsum(gs)])
+    ls = np.asarray(lhs_scale, np.float32).reshape(-1)
+    rs = np.asarray(rhs_scale, np.float32).reshape(-1)
+    gi, ki, ci = (np.asarray(v, np.int64) for v in (gi, ki, ci))
+    out = np.zeros(len(gi), np.float32)
+    for g in np.unique(gi):
+        sel = np.nonzero(gi == g)[0]
+        m = int(gs[g])
+        if m == 0:
+            continue
+        mp = -(-m // CHUNK) * CHUNK
+        X = np.zeros((len(sel), mp), np.uint8)
+        D = np.zeros((len(sel), mp), np.uint8)
+        X[:, :m] = lhs_q[offs[g]:offs[g] + m][:, ki[sel]].T
+        D[:, :m] = rhs_q[offs[g]:offs[g] + m][:, ci[sel]].T
+        acc = dot_f32(X, D)
+        lk = ls[ki[sel]] if ls.size > 1 else np.full(len(sel), ls[0], np.float32)
+        rc = rs[ci[sel]] if rs.size > 1 else np.full(len(sel), rs[0], np.float32)
+        out[sel] = lk * (acc * rc)
+    return out

@@ -14,6 +14,7 @@ from oracle.quantize import SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSO
 from oracle.sort import sort_by_expert
 from tests.parity import (assert_bits_equal, check_bf16, check_f32, dev_f32, dev_i32, dev_u8, gmm_allowance, host,
                           tgmm_allowance)
+from tests.mfma_model import gmm_samples, tgmm_samples
 from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate
 
 pytestmark = pytest.mark.gpu
@@ -50,12 +51,13 @@ def _check_gmm_full(lhs, ls, ls_mode, wq, ws_, gs, E, g0, El, tr, what, hw=False
     o = gmm(lhs_o, ls_o, wq, ws_, gs, g0, El)
     Mo, N = o["out"].shape
     B = (lambda idx: gmm_allowance(lhs_o, ls_o, wq, ws_, gs, g0, El, idx // N, idx % N)) if hw else None
+    mdl = None if hw else (lambda idx: gmm_samples(lhs_o, ls_o, wq, ws_, gs, g0, El, idx // N, idx % N))
     g32, err = gpu_gmm(lhs_o, ls_o, ls_mode, rhs, ws_, gs, E, g0, El, tr, m.MOE_F32)
     assert err == 0
-    st = check_f32(g32, o["out"], o["abs_sum"], what + " f32", hw_allowance=B)
+    st = check_f32(g32, o["out"], o["abs_sum"], what + " f32", hw_allowance=B, model=mdl)
     del g32
     g16, _ = gpu_gmm(lhs_o, ls_o, ls_mode, rhs, ws_, gs, E, g0, El, tr, m.MOE_BF16)
-    check_bf16(g16, o["out"], o["abs_sum"], what + " bf16", hw_allowance=B)
+    check_bf16(g16, o["out"], o["abs_sum"], what + " bf16", hw_allowance=B, model=mdl)
     n = int(np.asarray(gs)[g0:g0 + El].sum())
     assert not g16[n:].any()
     return st
@@ -173,7 +175,9 @@ def test_gmm_config5_input_gradient_full():
     o = gmm(dyq, dys, wT, ws_, gs, 0, cfg.E)
     g32, err = gpu_gmm(dyq, dys, m.MOE_SCALE_ROW_DYNAMIC, wq, ws_, gs, cfg.E, 0, cfg.E, 1, m.MOE_F32)
     assert err == 0
-    check_f32(g32, o["out"], o["abs_sum"], "config 5 dX f32")
+    N = cfg.H
+    check_f32(g32, o["out"], o["abs_sum"], "config 5 dX f32",
+              model=lambda idx: gmm_samples(dyq, dys, wT, ws_, gs, 0, cfg.E, idx // N, idx % N))
 
 
 @pytest.mark.parametrize("sizes", [[0, 5, 0, 130, 1, 0, 257, 0], [0, 0, 0, 0], [300], [1, 1, 1, 1, 1, 1, 1, 1]])
@@ -306,7 +310,10 @@ def test_tgmm_config5_full():
     g, err = gpu_tgmm(srt["xs"], xsc, dyq, dys, gs, cfg.E, 0, cfg.E)
     assert err == 0
     o = tgmm(srt["xs"], xsc, dyq, dys, gs, 0, cfg.E)
-    check_f32(g, o["out"], o["abs_sum"], "config 5 dW")
+    K, N = cfg.H, cfg.I
+    check_f32(g, o["out"], o["abs_sum"], "config 5 dW",
+              model=lambda idx: tgmm_samples(srt["xs"], xsc, dyq, dys, gs, 0, cfg.E, idx // (K * N), (idx // N) % K,
+                                             idx % N))
 
 
 @pytest.mark.parametrize("K,small_ws", [(384, False), (256, True)])
@@ -393,3 +400,38 @@ def test_tgmm_group_sizes_summing_past_2_31_stay_in_bounds():
     o = tgmm(X, xs, D, ds, gs1, 0, E)
     B = lambda idx: tgmm_allowance(X, xs, D, ds, gs1, 0, E, idx // (K * N), (idx // N) % K, idx % N)
     check_f32(g[:E], o["out"], o["abs_sum"], "tgmm sizes past 2^31", hw_allowance=B)
+
+
+# ------------------------------------------------- the matrix-core model
+@pytest.mark.parametrize("K", [128, 512, 2048])
+def test_matrix_core_model_matches_the_device(K):
+    """The model of the fp8 matrix core used by the workload checks
+    (tests/mfma_model.py) against the device itself: one group, unit scales,
+    float32 output, operands of random codes with exponents spread over the
+    whole format.  The device's dot products equal the model's up to the
+    order of the float32 additions of the chunk sums, and depart from the
+    exact sums by far more than that (so the agreement is not trivial)."""
+    from tests.mfma_model import dot_f32
+    from oracle.codec import e4m3_decode
+    rng = np.random.default_rng(K + 1)
+    M, N = 256, 256
+    lhs = rng.integers(0, 256, (M, K)).astype(np.uint8)
+    lhs[(lhs & 0x7F) == 0x7F] = 0x30
+    w = rng.integers(0, 256, (1, K, N)).astype(np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x30
+    g32, err = gpu_gmm(lhs, np.ones(1, np.float32), m.MOE_SCALE_TENSOR_STATIC,
+                       dev_u8(np.ascontiguousarray(w.transpose(0, 2, 1))).cpu().numpy(),
+                       np.ones((1, 1, 1, N), np.float32), np.array([M], np.int32), 1, 0, 1, 1, m.MOE_F32)
+    assert err == 0
+    rows = np.repeat(np.arange(M), N)
+    cols = np.tile(np.arange(N), M)
+    model = dot_f32(lhs[rows], w[0][:, cols].T).astype(np.float64)
+    p = e4m3_decode(lhs[rows]) * e4m3_decode(w[0][:, cols].T)
+    exact, A = p.sum(axis=1), np.abs(p).sum(axis=1)
+    g = g32.reshape(-1).astype(np.float64)
+    dev_vs_model = np.abs(g - model) / A
+    dev_vs_exact = np.abs(g - exact) / A
+    print(f"K={K}: device == model on {np.mean(g == model):.4f} of outputs; max |dev-model|/A "
+          f"{dev_vs_model.max():.3g}; max |dev-exact|/A {dev_vs_exact.max():.3g}", flush=True)
+    assert dev_vs_model.max() <= 2e-6
+    assert dev_vs_exact.max() > 20 * dev_vs_model.max()

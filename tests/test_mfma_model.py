@@ -134,3 +134,29 @@ def test_model_meets_the_strict_rule_on_workload_operands(cid, static):
     assert ratio.max() < 0.8 * REL_TOL, ratio.max()
     B = gmm_allowance(srt["xs"], ls, wq, ws_, srt["group_sizes"], 0, cfg.E, rows, cols)
     assert np.median(B / o["abs_sum"]) > 10 * REL_TOL
+
+
+def test_model_fallback_of_the_match_rules():
+    """The workload rule: an element outside 1e-5 * A of the exact value
+    passes only when it is within 1e-5 * A of the modelled matrix-core value
+    there; a value the model does not produce fails."""
+    from tests.parity import check_bf16, check_f32
+    rng = np.random.default_rng(5)
+    P, K = 3000, 64
+    ca, cb = _random_codes(rng, (P, K)), _random_codes(rng, (P, K))
+    p = e4m3_decode(ca) * e4m3_decode(cb)
+    exact, A = p.sum(axis=1), np.abs(p).sum(axis=1)
+    model = dot_f32(ca, cb)
+    assert (np.abs(model - exact) > REL_TOL * A).any()          # some need the fallback
+    mdl = lambda idx: model[idx]
+    st = check_f32(model, exact, A, "model itself", model=mdl)
+    assert 0 < st["model_frac"] < 1
+    with pytest.raises(AssertionError):
+        check_f32(model, exact, A, "no fallback")
+    far = np.nonzero(np.abs(model - exact) > REL_TOL * A)[0][0]
+    wrong = model.copy()
+    wrong[far] = np.float32(model[far] + 3 * REL_TOL * A[far] * np.sign(model[far] - exact[far]) + 3 * REL_TOL * A[far])
+    with pytest.raises(AssertionError):
+        check_f32(wrong, exact, A, "off the model", model=mdl)
+    from oracle.codec import bf16_rne_from_f32
+    check_bf16(bf16_rne_from_f32(model), exact, A, "model bf16", model=mdl)
