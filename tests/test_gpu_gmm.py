@@ -420,8 +420,7 @@ def test_matrix_core_model_matches_the_device(K):
     w = rng.integers(0, 256, (1, K, N)).astype(np.uint8)
     w[(w & 0x7F) == 0x7F] = 0x30
     g32, err = gpu_gmm(lhs, np.ones(1, np.float32), m.MOE_SCALE_TENSOR_STATIC,
-                       dev_u8(np.ascontiguousarray(w.transpose(0, 2, 1))).cpu().numpy(),
-                       np.ones((1, 1, 1, N), np.float32), np.array([M], np.int32), 1, 0, 1, 1, m.MOE_F32)
+                       np.ascontiguousarray(w.transpose(0, 2, 1)), np.ones((1, 1, 1, N), np.float32), np.array([M], np.int32), 1, 0, 1, 1, m.MOE_F32)
     assert err == 0
     rows = np.repeat(np.arange(M), N)
     cols = np.tile(np.arange(N), M)
