@@ -190,6 +190,37 @@ int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t 
                        int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs,
                        float* ss, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the device array that moe_sort_by_expert_noalloc uses in place of
+ * a workspace (one per GPU). */
+#define MOE_SORT_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+/*
+ * moe_sort_by_expert_noalloc -- moe_sort_by_expert that allocates nothing and
+ * takes no workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it.
+ * The sort's scratch (the window header and the per-tile histogram table)
+ * lives in a library-owned device array of MOE_SORT_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU, held from the first call on that GPU until the process
+ * ends.  Every call on a GPU shares that GPU's array: calls that overlap on
+ * one GPU (different streams, or several host threads) race and must be
+ * ordered by the caller.
+ *   device_error  optional [1] int32 device out (may be NULL, then dropped):
+ *            the MOE_DEVERR_* bits of this call's device-data errors are
+ *            OR'ed into it; the caller zeroes it.
+ * Every other argument, the results and the errors are those of
+ * moe_sort_by_expert.  Sizes whose workspace
+ * (moe_workspace_bytes(MOE_OP_SORT_BY_EXPERT, T*k, 0, 0, E)) exceeds
+ * MOE_SORT_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before any launch:
+ * T*k may be at most 4128768 with E = 64, 1043968 with E = 256 and 261632
+ * with E = 1024.
+ * No hipMalloc, hipFree or allocating call is made.
+ */
+int moe_sort_by_expert_noalloc(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                               int32_t group_offset, int32_t num_local_experts, const uint8_t* xq,
+                               const float* xscale, int xscale_mode, int64_t H, int64_t M_cap,
+                               int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs,
+                               float* ss, int32_t* device_error, void* stream);
+
 /*
  * moe_quantize_sort_by_expert -- moe_quantize_rows followed by
  * moe_sort_by_expert in one pass over the activations, for the single-GPU

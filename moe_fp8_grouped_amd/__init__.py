@@ -27,6 +27,7 @@ MOE_ACT_NONE, MOE_ACT_SILU_MUL = 0, 1
 (MOE_OP_QUANTIZE_ROWS, MOE_OP_SORT_BY_EXPERT, MOE_OP_GMM, MOE_OP_TGMM, MOE_OP_GATHER_REDUCE,
  MOE_OP_QUANTIZE_WEIGHTS) = range(6)
 MOE_DEVERR_EXPERT_ID, MOE_DEVERR_GROUP_SIZE, MOE_DEVERR_ROWS = 1, 2, 4
+MOE_SORT_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 # C signatures: name -> (restype, argtypes)
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -36,6 +37,8 @@ SIGNATURES = {
     "moe_quantize_weights": (_I, [_P, _I64, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _I, _F, _I, _P, _P, _P]),
     "moe_sort_by_expert": (_I, [_P, _I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                 _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_sort_by_expert_noalloc": (_I, [_P, _I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
+                                        _P, _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_sort_by_expert": (_I, [_P, _I64, _I64, _I, _F, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_gmm_fp8": (_I, [_P, _P, _I, _P, _P, ctypes.c_int32, ctypes.c_int32, _I, _P, ctypes.c_int32, ctypes.c_int32,
@@ -162,6 +165,13 @@ def moe_sort_by_expert(expert_ids, T, k, E, group_offset, num_local_experts, xq,
     return _call("moe_sort_by_expert", _ptr(expert_ids), T, k, E, group_offset, num_local_experts, _ptr(xq),
                  _ptr(xscale), xscale_mode, H, M_cap, _ptr(perm), _ptr(inv_pos), _ptr(group_sizes), _ptr(xs),
                  _ptr(ss), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_sort_by_expert_noalloc(expert_ids, T, k, E, group_offset, num_local_experts, xq, xscale, xscale_mode, H,
+                               M_cap, perm, inv_pos, group_sizes, xs, ss, device_error=None, stream=None):
+    return _call("moe_sort_by_expert_noalloc", _ptr(expert_ids), T, k, E, group_offset, num_local_experts, _ptr(xq),
+                 _ptr(xscale), xscale_mode, H, M_cap, _ptr(perm), _ptr(inv_pos), _ptr(group_sizes), _ptr(xs),
+                 _ptr(ss), _ptr(device_error), _stream(stream))
 
 
 def moe_quantize_sort_by_expert(x, T, H, scale_mode, static_scale, expert_ids, k, E, group_offset, num_local_experts,

@@ -21,6 +21,8 @@
 //            it to each of its local destinations; extra waves zero rows
 //            [n, M_cap).  Coalesced 16-byte loads and stores.
 // No float atomics and no order-dependent steps: the result is deterministic.
+#include <mutex>
+
 #include "quant_common.hpp"
 
 namespace moe {
@@ -43,7 +45,7 @@ __device__ __forceinline__ int key_of(int32_t id, int E, int32_t* err) {
 
 template <int TILE>
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
-                                                        int32_t* __restrict__ hdr, int32_t* __restrict__ tile_hist) {
+                                                        int32_t* __restrict__ err, int32_t* __restrict__ tile_hist) {
   extern __shared__ int hist[];
   for (int e = threadIdx.x; e <= E; e += 256) hist[e] = 0;
   __syncthreads();
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
 #pragma unroll
   for (int i = 0; i < TILE / 256; ++i) {
     const int64_t f = base + i * 256 + threadIdx.x;
-    if (f < M) atomicAdd(&hist[key_of(ids[f], E, hdr + kErr)], 1);
+    if (f < M) atomicAdd(&hist[key_of(ids[f], E, err)], 1);
   }
   __syncthreads();
   int32_t* out = tile_hist + static_cast<int64_t>(blockIdx.x) * (E + 1);
@@ -147,6 +149,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
 template <int TILE, bool FUSED_SCAN>
 __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E, int nbits,
                                                         int64_t M_cap, int32_t* __restrict__ hdr,
+                                                        int32_t* __restrict__ err,
                                                         const int32_t* __restrict__ tile_off, int ntiles, int g0,
                                                         int El, int32_t* __restrict__ group_sizes,
                                                         int32_t* __restrict__ perm, int32_t* __restrict__ inv_pos) {
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
     if (key < E && pos >= start && pos < start + n) {
       ip = pos - start;
       if (ip >= M_cap) {
-        raise_error(hdr + kErr, MOE_DEVERR_ROWS);
+        raise_error(err, MOE_DEVERR_ROWS);
         ip = -1;
       }
     }
@@ -443,15 +446,13 @@ size_t sort_ws_bytes(int64_t M, int E) {
 namespace moe {
 namespace {
 // The sort's metadata stages (histogram, scan, stable rank) into perm,
-// inv_pos, group_sizes and the workspace header.
+// inv_pos, group_sizes and the window header hdr; tile_hist holds
+// sort_ws_bytes(M, E) - kHdr bytes; device-data errors are OR'ed into err
+// (may be NULL).
 int sort_metadata(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, int32_t group_offset,
                   int32_t num_local_experts, int64_t M_cap, int32_t* perm, int32_t* inv_pos, int32_t* group_sizes,
-                  void* ws, size_t ws_bytes, hipStream_t st) {
+                  int32_t* hdr, int32_t* tile_hist, int32_t* err, hipStream_t st) {
   const int64_t M = T * k;
-  if (!group_sizes || !ws || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
-  if (ws_bytes < sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
-  int32_t* hdr = static_cast<int32_t*>(ws);
-  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kHdr);
   // small tiles (more workgroups) whenever their table fits the scan's LDS
   const bool small = moe_cdiv(M, kTileSmall) * (E + 1) <= kScanLds;
   const int tile = small ? kTileSmall : kTile;
@@ -462,9 +463,9 @@ int sort_metadata(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, in
   const size_t hist_lds = (E + 1) * sizeof(int);
   if (ntiles > 0) {
     if (small)
-      sort_hist_kernel<kTileSmall><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+      sort_hist_kernel<kTileSmall><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, err, tile_hist);
     else
-      sort_hist_kernel<kTile><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, hdr, tile_hist);
+      sort_hist_kernel<kTile><<<ntiles, 256, hist_lds, st>>>(expert_ids, M, E, err, tile_hist);
     MOE_CHECK_LAUNCH();
   }
   // hist -> rank with the scan fused into every rank block when the tile
@@ -473,11 +474,11 @@ int sort_metadata(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, in
   if (ntiles > 0 && scan_in_lds && rank_lds <= 64 * 1024) {
     if (small)
       sort_rank_kernel<kTileSmall, true><<<ntiles, 256, rank_lds, st>>>(
-          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+          expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
           perm, inv_pos);
     else
       sort_rank_kernel<kTile, true><<<ntiles, 256, rank_lds, st>>>(
-          expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
+          expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
           perm, inv_pos);
     MOE_CHECK_LAUNCH();
   } else {
@@ -488,14 +489,55 @@ int sort_metadata(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, in
     if (ntiles > 0) {
       if (small)
         sort_rank_kernel<kTileSmall, false><<<ntiles, 256, 5 * hist_lds, st>>>(
-            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-            perm, inv_pos);
+            expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts,
+            group_sizes, perm, inv_pos);
       else
         sort_rank_kernel<kTile, false><<<ntiles, 256, 5 * hist_lds, st>>>(
-            expert_ids, M, E, nbits, M_cap, hdr, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-            perm, inv_pos);
+            expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts,
+            group_sizes, perm, inv_pos);
       MOE_CHECK_LAUNCH();
     }
+  }
+  return MOE_OK;
+}
+
+// Argument checks of moe_sort_by_expert that do not involve the workspace.
+int sort_check(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, int32_t group_offset,
+               int32_t num_local_experts, const uint8_t* xq, const float* xscale, int xscale_mode, int64_t H,
+               int64_t M_cap, const int32_t* perm, const int32_t* inv_pos, const int32_t* group_sizes,
+               const uint8_t* xs, const float* ss) {
+  if (T < 0 || k <= 0 || k > 64 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
+  if (group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E) return MOE_ERR_SHAPE;
+  if (M_cap < 0 || T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (xscale_mode != MOE_SCALE_ROW_DYNAMIC && xscale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
+      xscale_mode != MOE_SCALE_TENSOR_STATIC)
+    return MOE_ERR_UNSUPPORTED;
+  if (xq && (H <= 0 || H % 16)) return MOE_ERR_SHAPE;
+  const int64_t M = T * k;
+  if (!group_sizes || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
+  if (xq && M_cap > 0 && !xs) return MOE_ERR_NULL;
+  const bool row_scale = xscale_mode == MOE_SCALE_ROW_DYNAMIC;
+  if (row_scale && xscale && M_cap > 0 && !ss) return MOE_ERR_NULL;
+  if (row_scale && ss && T > 0 && !xscale) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+// The whole sort on the given header, table and error word: metadata, then
+// the gather of the token rows (and per-token scales) when asked for.
+int sort_run(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, int32_t group_offset,
+             int32_t num_local_experts, const uint8_t* xq, const float* xscale, int xscale_mode, int64_t H,
+             int64_t M_cap, int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs, float* ss,
+             int32_t* hdr, int32_t* tile_hist, int32_t* err, hipStream_t st) {
+  const int rc = sort_metadata(expert_ids, T, k, E, group_offset, num_local_experts, M_cap, perm, inv_pos,
+                               group_sizes, hdr, tile_hist, err, st);
+  if (rc != MOE_OK) return rc;
+  if (xs || ss) {
+    int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
+    if (waves < 4) waves = 4;
+    if (waves > 65536) waves = 65536;
+    sort_scatter_kernel<<<static_cast<unsigned>(moe_cdiv(waves, 4)), 256, 0, st>>>(
+        xq, xscale, xscale_mode == MOE_SCALE_ROW_DYNAMIC ? 1 : 0, inv_pos, T, k, H, M_cap, hdr, xs, ss);
+    MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
 }
@@ -507,34 +549,16 @@ extern "C" int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t 
                                   const float* xscale, int xscale_mode, int64_t H, int64_t M_cap,
                                   int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs,
                                   float* ss, void* ws, size_t ws_bytes, void* stream) {
-  if (T < 0 || k <= 0 || k > 64 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
-  if (group_offset < 0 || num_local_experts < 0 || group_offset + num_local_experts > E) return MOE_ERR_SHAPE;
-  if (M_cap < 0 || T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
-  if (xscale_mode != MOE_SCALE_ROW_DYNAMIC && xscale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
-      xscale_mode != MOE_SCALE_TENSOR_STATIC)
-    return MOE_ERR_UNSUPPORTED;
-  if (xq && (H <= 0 || H % 16)) return MOE_ERR_SHAPE;
-  const int64_t M = T * k;
-  if (!group_sizes || !ws || (M > 0 && (!expert_ids || !perm || !inv_pos))) return MOE_ERR_NULL;
-  if (xq && M_cap > 0 && !xs) return MOE_ERR_NULL;
-  const bool row_scale = xscale_mode == MOE_SCALE_ROW_DYNAMIC;
-  if (row_scale && xscale && M_cap > 0 && !ss) return MOE_ERR_NULL;
-  if (row_scale && ss && T > 0 && !xscale) return MOE_ERR_NULL;
-  if (ws_bytes < moe::sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* hdr = static_cast<int32_t*>(ws);
-  const int rc = moe::sort_metadata(expert_ids, T, k, E, group_offset, num_local_experts, M_cap, perm, inv_pos,
-                                    group_sizes, ws, ws_bytes, st);
+  const int rc = moe::sort_check(expert_ids, T, k, E, group_offset, num_local_experts, xq, xscale, xscale_mode, H,
+                                 M_cap, perm, inv_pos, group_sizes, xs, ss);
   if (rc != MOE_OK) return rc;
-  if (xs || ss) {
-    int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
-    if (waves < 4) waves = 4;
-    if (waves > 65536) waves = 65536;
-    moe::sort_scatter_kernel<<<static_cast<unsigned>(moe_cdiv(waves, 4)), 256, 0, st>>>(
-        xq, xscale, row_scale ? 1 : 0, inv_pos, T, k, H, M_cap, hdr, xs, ss);
-    MOE_CHECK_LAUNCH();
-  }
-  return MOE_OK;
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < moe::sort_ws_bytes(T * k, E)) return MOE_ERR_WORKSPACE;
+  int32_t* hdr = static_cast<int32_t*>(ws);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + moe::kHdr);
+  return moe::sort_run(expert_ids, T, k, E, group_offset, num_local_experts, xq, xscale, xscale_mode, H, M_cap,
+                       perm, inv_pos, group_sizes, xs, ss, hdr, tile_hist, hdr + moe::kErr,
+                       static_cast<hipStream_t>(stream));
 }
 
 extern "C" int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_mode, float static_scale,
@@ -563,8 +587,9 @@ extern "C" int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, 
   if (ws_bytes < moe::sort_ws_bytes(M, E)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* hdr = static_cast<int32_t*>(ws);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + moe::kHdr);
   const int rc = moe::sort_metadata(expert_ids, T, k, E, group_offset, num_local_experts, M_cap, perm, inv_pos,
-                                    group_sizes, ws, ws_bytes, st);
+                                    group_sizes, hdr, tile_hist, hdr + moe::kErr, st);
   if (rc != MOE_OK) return rc;
   int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
   if (waves < 4) waves = 4;
@@ -591,4 +616,55 @@ extern "C" int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, 
 #undef MOE_QS
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------- no workspace
+// moe_sort_by_expert_noalloc keeps the window header and the histogram table
+// in this library-owned array instead of a caller workspace: one copy per GPU,
+// held until the process ends.  In host code the array's name is only a
+// stand-in for the device symbol, so it is never passed to a kernel; each
+// device's address comes from hipGetSymbolAddress, looked up once per device
+// (with that device current) on the entry point's first call there.
+static __device__ __align__(256) uint8_t scratch[MOE_SORT_NOALLOC_SCRATCH_BYTES];
+
+namespace moe {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_sort_by_expert_noalloc(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                                          int32_t group_offset, int32_t num_local_experts, const uint8_t* xq,
+                                          const float* xscale, int xscale_mode, int64_t H, int64_t M_cap,
+                                          int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs,
+                                          float* ss, int32_t* device_error, void* stream) {
+  int rc = moe::sort_check(expert_ids, T, k, E, group_offset, num_local_experts, xq, xscale, xscale_mode, H, M_cap,
+                           perm, inv_pos, group_sizes, xs, ss);
+  if (rc != MOE_OK) return rc;
+  if (moe::sort_ws_bytes(T * k, E) > MOE_SORT_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* p = nullptr;
+  rc = moe::scratch_on_current_device(&p);
+  if (rc != MOE_OK) return rc;
+  // every word of the header and the table that the kernels read is written
+  // by this call's own kernels first, so nothing is cleared between calls
+  int32_t* hdr = static_cast<int32_t*>(p);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(static_cast<char*>(p) + moe::kHdr);
+  return moe::sort_run(expert_ids, T, k, E, group_offset, num_local_experts, xq, xscale, xscale_mode, H, M_cap,
+                       perm, inv_pos, group_sizes, xs, ss, hdr, tile_hist, device_error,
+                       static_cast<hipStream_t>(stream));
 }

@@ -34,7 +34,7 @@ def lib():
 
 def test_header_declares_the_path_calls():
     names = _declared_functions()
-    for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
+    for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_sort_by_expert_noalloc", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
                "moe_gather_reduce_backward", "moe_silu_mul_backward", "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
                "moe_version"]:
         assert fn in names
@@ -122,6 +122,21 @@ def test_sort_validation(lib):
     assert call(gs=None) == m.MOE_ERR_NULL
     assert call(xq=one, H=32, xs=None) == m.MOE_ERR_NULL
     assert call(wsb=16) == m.MOE_ERR_WORKSPACE
+
+
+def test_sort_noalloc_validation(lib):
+    f = lambda *a: _c(lib, "moe_sort_by_expert_noalloc", *a)
+    one = 1
+    def call(T=4, k=2, E=8, g0=0, El=8, xq=None, xscale=None, mode=0, H=0, M_cap=8, gs=one):
+        return f(one, T, k, E, g0, El, xq, xscale, mode, H, M_cap, one, one, gs, None, None, None, None)
+    assert call(E=0) == m.MOE_ERR_SHAPE
+    assert call(g0=4, El=5) == m.MOE_ERR_SHAPE
+    assert call(mode=7) == m.MOE_ERR_UNSUPPORTED
+    assert call(gs=None) == m.MOE_ERR_NULL
+    # the largest sizes the library's scratch array holds, and one slot more (no launch either way here)
+    assert call(T=261633, k=1, E=1024, El=1024) == m.MOE_ERR_WORKSPACE
+    assert call(T=1043969, k=1, E=256, El=256) == m.MOE_ERR_WORKSPACE
+    assert m.workspace_bytes(m.MOE_OP_SORT_BY_EXPERT, 261632, 0, 0, 1024) <= m.MOE_SORT_NOALLOC_SCRATCH_BYTES
 
 
 def test_quantize_sort_validation(lib):
