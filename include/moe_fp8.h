@@ -285,7 +285,9 @@ int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_m
  *   out      [M, N], out_dtype MOE_BF16 (default) or MOE_F32.
  *   ws       workspace of moe_workspace_bytes(MOE_OP_GMM, M, K, N, E) (holds
  *            the error word).
- * K and N multiples of 128, M >= 0, 1 <= E <= 1024, num_local_experts <= 1024.
+ * K and N multiples of 16 (MOE_ERR_SHAPE otherwise); multiples of 128 take
+ * the tiled matrix-core kernels, other sizes a plainer edge kernel with the
+ * same results.  M >= 0, 1 <= E <= 1024, num_local_experts <= 1024.
  */
 int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const uint8_t* rhs,
                 const float* rhs_scale, int32_t Kb, int32_t Nb, int transpose_rhs,
@@ -306,7 +308,8 @@ int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, 
  *            scale does not factor out of the sum and is rejected).
  *   out      [E_loc, K, N], out_dtype MOE_F32 (default) or MOE_BF16.
  *   ws       workspace of moe_workspace_bytes(MOE_OP_TGMM, M, K, N, E).
- * K and N multiples of 128.
+ * K and N multiples of 16 (MOE_ERR_SHAPE otherwise); multiples of 128 take
+ * the tiled kernels, other sizes a plainer edge kernel with the same results.
  */
 int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t lhs_scale_len,
                  const uint8_t* rhs, const float* rhs_scale, int32_t rhs_scale_len,

@@ -239,6 +239,9 @@ int64_t tgmm_mpad(int64_t M, int E) { return moe_cdiv(M + 128 * static_cast<int6
 size_t tgmm_ws_bytes(int64_t M, int64_t K, int64_t N, int E) {
   return tile::kHdr + static_cast<size_t>((K + N) * tgmm_mpad(M, E));
 }
+hipError_t tgmm_edge_launch(const uint8_t* lhs, const float* ls, int ls_len, const uint8_t* rhs, const float* rs,
+                            int rs_len, const int32_t* gs, int g0, int El, int64_t M, int64_t K, int64_t N, bool bf16,
+                            void* out, int32_t* err, hipStream_t st);
 hipError_t gmm_batched_launch(const uint8_t* A, const float* ls, int ls_len, const uint8_t* B, const float* rs,
                               int rs_len, const int32_t* group_sizes, int g0, int El, int64_t max_rows, int64_t M,
                               int64_t K, int64_t N, bool bf16, void* out, int32_t* err, hipStream_t st);
@@ -249,7 +252,7 @@ extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t 
                             const int32_t* group_sizes, int32_t E, int32_t group_offset,
                             int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
                             void* out, void* ws, size_t ws_bytes, void* stream) {
-  if (M < 0 || K <= 0 || N <= 0 || K % 128 || N % 128) return MOE_ERR_SHAPE;
+  if (M < 0 || K <= 0 || N <= 0 || K % 16 || N % 16) return MOE_ERR_SHAPE;
   if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 ||
       num_local_experts > moe::tile::kMaxLocal || group_offset + num_local_experts > E)
     return MOE_ERR_SHAPE;
@@ -264,9 +267,13 @@ extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t 
   if (M > 0 && (!lhs || !rhs)) return MOE_ERR_NULL;
   if (!ws) return MOE_ERR_WORKSPACE;
   if (ws_bytes < moe::tile::kHdr) return MOE_ERR_WORKSPACE;
-  if (static_cast<int64_t>(El) * (K / 128) * (N / 128) > INT32_MAX) return MOE_ERR_SHAPE;
+  if (static_cast<int64_t>(El) * moe_cdiv(K, 64) * moe_cdiv(N, 64) > INT32_MAX) return MOE_ERR_SHAPE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* err = static_cast<int32_t*>(ws);
+  if (K % 128 || N % 128)        // multiples of 16 only: the edge kernel
+    return moe::tgmm_edge_launch(lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, group_sizes,
+                                 group_offset, El, M, K, N, out_dtype == MOE_BF16, out, err, st) == hipSuccess
+               ? MOE_OK : MOE_ERR_HIP;
   // Main path: both operands transposed into the workspace (each group's rows
   // become a contraction axis of their own), then the gmm pipeline per group.
   // The one-kernel path (transposing in LDS while multiplying) serves smaller

@@ -105,14 +105,17 @@ __device__ bool wave0_scan_sat(const int* v, int* out, int n, int64_t cap) {
   return carry > cap;
 }
 
-// Tiles of a group of m rows.  Plain: ceil(m / bm) m-tiles per n-tile.  With
-// wide tails (gmm): full m-tiles of bm rows, and a remainder of at most bm/2
-// rows is covered by tiles of bm/2 rows x two n-tiles (an odd last n-tile
-// keeps a plain tail tile).
-__device__ __forceinline__ int group_tiles(int m, int bm, int nt, bool wide_tail) {
+// Tiles of a group of m rows.  tail_mode 0 (plain): ceil(m / bm) m-tiles per
+// n-tile.  1 (wide tails, gmm): full m-tiles of bm rows, and a remainder of at
+// most bm/2 rows is covered by tiles of bm/2 rows x two n-tiles (an odd last
+// n-tile keeps a plain tail tile).  2 (all wide): every tile is bm/2 rows x
+// two n-tiles, ceil(m / (bm/2)) of them per n-tile pair (an odd last n-tile
+// keeps plain tiles).
+__device__ __forceinline__ int group_tiles(int m, int bm, int nt, int tail_mode) {
   if (nt <= 0) return 1;
+  if (tail_mode == 2) return ((m + bm / 2 - 1) / (bm / 2)) * (nt / 2) + (nt & 1) * ((m + bm - 1) / bm);
   const int full = m / bm, rem = m - full * bm;
-  if (!wide_tail || rem == 0 || rem > bm / 2) return (full + (rem ? 1 : 0)) * nt;
+  if (tail_mode == 0 || rem == 0 || rem > bm / 2) return (full + (rem ? 1 : 0)) * nt;
   return (nt / 2) * (2 * full + 1) + (nt & 1) * (full + 1);
 }
 
@@ -120,13 +123,13 @@ __device__ __forceinline__ int group_tiles(int m, int bm, int nt, bool wide_tail
 // max_rows (flagging the error word) so that every tile stays inside the
 // buffers -- the offsets are a saturating 64-bit scan, so group sizes whose
 // sum passes 2^31 cannot wrap into a table that points outside the buffer;
-// a group of m rows owns group_tiles(m, bm, tiles_per_mrow, wide_tail) tiles
+// a group of m rows owns group_tiles(m, bm, tiles_per_mrow, tail_mode) tiles
 // (tiles_per_mrow = 0: one entry per group).  The host bounds the tile count
 // of max_rows rows below 2^31.
 template <class GT>
 __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, int El, int64_t max_rows,
                              int tiles_per_mrow, int bm, int32_t* err, GT& gt, int* tmp,
-                             bool wide_tail = false) {
+                             int tail_mode = 0) {
   for (int g = threadIdx.x; g < El; g += blockDim.x) {
     int m = group_sizes[g0 + g];
     if (m < 0) {
@@ -141,7 +144,7 @@ __device__ void build_groups(const int32_t* __restrict__ group_sizes, int g0, in
   __syncthreads();
   for (int g = threadIdx.x; g < El; g += blockDim.x) {
     const int m = gt.rows_off[g + 1] - gt.rows_off[g];
-    tmp[g] = group_tiles(m, bm, tiles_per_mrow, wide_tail);
+    tmp[g] = group_tiles(m, bm, tiles_per_mrow, tail_mode);
   }
   __syncthreads();
   wave0_scan(tmp, gt.tiles_off, El);

@@ -164,8 +164,9 @@ def test_gmm_validation(lib):
     def call(M=256, K=256, N=256, Kb=1, Nb=256, tr=1, E=8, g0=0, El=8, mode=0, od=0, ws=one, wsb=256,
              lhs=one, out=one):
         return f(lhs, one, mode, one, one, Kb, Nb, tr, one, E, g0, El, M, K, N, od, out, ws, wsb, None)
-    assert call(K=200) == m.MOE_ERR_SHAPE
+    assert call(K=200) == m.MOE_ERR_SHAPE                    # not a multiple of 16
     assert call(N=100) == m.MOE_ERR_SHAPE
+    assert call(K=144, Kb=2) == m.MOE_ERR_UNSUPPORTED        # 72-row K blocks
     assert call(Kb=3) == m.MOE_ERR_SHAPE
     assert call(K=384, Kb=2) == m.MOE_ERR_UNSUPPORTED        # 192-row K blocks
     assert call(Nb=3) == m.MOE_ERR_SHAPE
@@ -184,6 +185,7 @@ def test_tgmm_and_gather_reduce_validation(lib):
     t = lambda *a: _c(lib, "moe_tgmm_fp8", *a)
     one = 1
     assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 200, 256, 1, one, one, 256, None) == m.MOE_ERR_SHAPE
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 256, 72, 1, one, one, 256, None) == m.MOE_ERR_SHAPE
     assert t(one, one, 3, one, one, 1, one, 8, 0, 8, 100, 256, 256, 1, one, one, 256, None) == m.MOE_ERR_UNSUPPORTED
     assert t(one, one, 1, one, one, 7, one, 8, 0, 8, 100, 256, 256, 1, one, one, 256, None) == m.MOE_ERR_UNSUPPORTED
     assert t(one, one, 1, one, one, 1, one, 8, 0, 0, 100, 256, 256, 1, one, one, 256, None) == m.MOE_OK  # no experts

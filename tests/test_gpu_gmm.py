@@ -434,3 +434,62 @@ def test_matrix_core_model_matches_the_device(K):
           f"{dev_vs_model.max():.3g}; max |dev-exact|/A {dev_vs_exact.max():.3g}", flush=True)
     assert dev_vs_model.max() <= 2e-6
     assert dev_vs_exact.max() > 20 * dev_vs_model.max()
+
+
+# ------------------------------------------------- K, N multiples of 16 only
+@pytest.mark.parametrize("K,N,tr,nb", [(144, 80, 1, "channel"), (144, 80, 0, "channel"), (16, 16, 1, "tensor"),
+                                       (272, 1552, 0, "coarse16"), (400, 208, 1, "channel")])
+def test_gmm_sizes_multiple_of_16(K, N, tr, nb):
+    """K and N that are multiples of 16 but not of 128 (the edge path):
+    ragged groups with empty ones, both weight layouts, per-channel, per-
+    tensor and 16-column-block scales, the rows after the last group zero."""
+    rng = np.random.default_rng(K * 7 + N + tr)
+    sizes = [0, 5, 0, 130, 1, 67, 0, 257]
+    E = len(sizes)
+    gs = np.array(sizes, np.int32)
+    M = int(gs.sum()) + 21
+    lhs = rng.integers(0, 0x70, (M, K)).astype(np.uint8)
+    w = rng.integers(0, 0x70, (E, K, N)).astype(np.uint8)
+    nbv = {"channel": N, "tensor": 1, "coarse16": N // 16}[nb]
+    rs = rng.uniform(0.001, 0.1, (E, 1, 1, nbv)).astype(np.float32)
+    ls = rng.uniform(0.01, 1, M).astype(np.float32)
+    _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, 0, E, tr, f"K={K} N={N} tr={tr} {nb}", hw=True)
+
+
+def test_gmm_sizes_multiple_of_16_quantized_operands_local_slice():
+    """Quantized gaussian operands at K=144, N=80 on a local slice of the
+    experts: the workload rule (1e-5 * A, else the modelled matrix core)."""
+    from workloads import to_bf16_bits
+    rng = np.random.default_rng(144)
+    E, g0, El, K, N = 12, 4, 5, 144, 80
+    gs = rng.integers(0, 90, E).astype(np.int32)
+    gs[g0 + 1] = 0
+    n = int(gs[g0:g0 + El].sum())
+    x = to_bf16_bits(rng.standard_normal((n + 7, K)).astype(np.float32))
+    w = to_bf16_bits((rng.standard_normal((El, K, N)) * 0.02).astype(np.float32))
+    xq, xs, _ = quantize_rows(x, SCALE_ROW_DYNAMIC)
+    wq, ws_ = quantize_weights(w, 1, N)
+    _check_gmm_full(xq, xs, SCALE_ROW_DYNAMIC, wq, ws_, gs, E, g0, El, 1, "K=144 N=80 quantized slice")
+    _check_gmm_full(xq, xs, SCALE_ROW_DYNAMIC, wq, ws_, gs, E, g0, El, 0, "K=144 N=80 quantized slice kn")
+
+
+@pytest.mark.parametrize("K,N,scales", [(144, 80, "k_and_n"), (16, 48, "tensor"), (144, 1040, "n")])
+def test_tgmm_sizes_multiple_of_16(K, N, scales):
+    rng = np.random.default_rng(K + N)
+    sizes = [0, 3, 200, 0, 1, 129]
+    E = len(sizes)
+    gs = np.array(sizes, np.int32)
+    M = int(gs.sum()) + 4
+    X = rng.integers(0, 0x7E, (M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)).astype(np.uint8) << 7)
+    D = rng.integers(0, 0x7E, (M, N)).astype(np.uint8) | (rng.integers(0, 2, (M, N)).astype(np.uint8) << 7)
+    xs = rng.uniform(0.01, 1, K).astype(np.float32) if scales == "k_and_n" else np.array([0.02], np.float32)
+    ds = rng.uniform(0.01, 1, N).astype(np.float32) if scales in ("k_and_n", "n") else np.array([0.003], np.float32)
+    o = tgmm(X, xs, D, ds, gs, 0, E)
+    g, err = gpu_tgmm(X, xs, D, ds, gs, E, 0, E)
+    assert err == 0
+    B = lambda idx: tgmm_allowance(X, xs, D, ds, gs, 0, E, idx // (K * N), (idx // N) % K, idx % N)
+    check_f32(g, o["out"], o["abs_sum"], f"tgmm K={K} N={N}", hw_allowance=B)
+    for e in np.nonzero(gs == 0)[0]:
+        assert not g[e].any()
+    g16, _ = gpu_tgmm(X, xs, D, ds, gs, E, 0, E, m.MOE_BF16)
+    check_bf16(g16, o["out"], o["abs_sum"], f"tgmm bf16 K={K} N={N}", hw_allowance=B)

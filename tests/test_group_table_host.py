@@ -16,11 +16,14 @@ import moe_fp8_grouped_amd as m
 I32 = np.iinfo(np.int32)
 
 
-def group_tiles(mr, bm, nt, wide_tail):
+def group_tiles(mr, bm, nt, mode):
+    """mode 0 plain tiles, 1 wide tails, 2 every tile wide (bm/2 rows x two n-tiles)."""
     if nt <= 0:
         return 1
+    if mode == 2:
+        return -(-mr // (bm // 2)) * (nt // 2) + (nt & 1) * -(-mr // bm)
     full, rem = mr // bm, mr % bm
-    if not wide_tail or rem == 0 or rem > bm // 2:
+    if mode == 0 or rem == 0 or rem > bm // 2:
         return (full + (1 if rem else 0)) * nt
     return (nt // 2) * (2 * full + 1) + (nt & 1) * (full + 1)
 
@@ -58,8 +61,8 @@ CASES = [
 
 
 @pytest.mark.parametrize("sizes", CASES)
-@pytest.mark.parametrize("max_rows,nt,bm,wide", [(1000, 2, 256, True), (8192, 32, 256, True), (40960, 1, 128, False),
-                                                 (2 ** 31 - 2, 16, 256, False)])
+@pytest.mark.parametrize("max_rows,nt,bm,wide", [(1000, 2, 256, 1), (8192, 32, 256, 1), (8192, 33, 256, 2),
+                                                 (40960, 1, 128, 0), (2 ** 31 - 2, 16, 256, 0)])
 def test_table_stays_inside_the_buffer(sizes, max_rows, nt, bm, wide):
     if (max_rows // 128 + len(sizes) + 1) * nt > I32.max:
         pytest.skip("rejected by the host's tile-count bound")
@@ -74,6 +77,25 @@ def test_table_stays_inside_the_buffer(sizes, max_rows, nt, bm, wide):
         r0, r1 = int(rows_off[g]), int(rows_off[g + 1])
         assert 0 <= r0 <= r1 <= max_rows
         assert tiles_off[g + 1] - tiles_off[g] == group_tiles(r1 - r0, bm, nt, wide)
+    if wide == 2 and len(sizes) <= 64:
+        # the all-wide decode: tile -> (n-tile, first row, rows) covers every (row, n-tile) of each group once
+        for g in range(len(sizes)):
+            m_g = int(rows_off[g + 1] - rows_off[g])
+            if m_g > 4096:
+                continue
+            cover = np.zeros((max(m_g, 1), nt), np.int64)
+            half, mtw, npair = bm // 2, -(-m_g // (bm // 2)), nt // 2
+            for local in range(int(tiles_off[g + 1] - tiles_off[g])):
+                if local < npair * mtw:
+                    pr = local // mtw
+                    roff, rows, nts = (local - pr * mtw) * half, half, (2 * pr, 2 * pr + 1)
+                else:
+                    roff, rows, nts = (local - npair * mtw) * bm, bm, (nt - 1,)
+                rows = min(rows, m_g - roff)
+                assert rows > 0 and roff + rows <= m_g
+                for j in nts:
+                    cover[roff:roff + rows, j] += 1
+            assert m_g == 0 or (cover == 1).all()
 
 
 def test_a_32_bit_running_sum_would_leave_the_buffer():
@@ -81,7 +103,7 @@ def test_a_32_bit_running_sum_would_leave_the_buffer():
     sum makes group 2 start at -2^31 and ends the table below zero."""
     off = wrapping_rows_off([1 << 30] * 3)
     assert off[2] < 0 and off[3] < 0
-    rows_off, _, over, _ = build_groups([1 << 30] * 3, 1000, 2, 256, True)
+    rows_off, _, over, _ = build_groups([1 << 30] * 3, 1000, 2, 256, 1)
     assert list(rows_off) == [0, 1000, 1000, 1000] and over
 
 
