@@ -109,6 +109,55 @@ def dense_bf16_reference(cfg, data):
     return bf16_rne_from_f64(out)
 
 
+def dense_bf16_backward_reference(cfg, data, dout_bits):
+    """The gated FFN's backward with unquantized bf16 operands (float64
+    products, bf16 between stages), for context next to the pages' gradient
+    columns ("Support quantization for tokamax gmm v2", table
+    "relative_norm_diff Across All Cases": grad_wi_0, grad_wi_1, grad_wo).
+    The forward is dense_bf16_reference's; for out = sum_j w_j y_j the
+    backward is dy_j = w_j * dout, dh = dy wo^T, dwo += h^T dy, the SiLU*mul
+    derivative (da = dh * b * s (1 + a (1 - s)), db = dh * a s with s the
+    logistic of a), dw0 += x^T da, dw1 += x^T db, dx += da w0^T + db w1^T.
+    Returns dx (bf16 bits [T, H]) and float64 dw0, dw1 [E_loc, H, I], dwo
+    [E_loc, I, H]."""
+    x = bf16_decode(data["x"]).astype(np.float64)
+    dout = bf16_decode(dout_bits).astype(np.float64)
+    ids = data["ids"]
+    T, k = ids.shape
+    W = {n: bf16_decode(w).astype(np.float64) for n, w in data["weights"].items()}
+    gl = lambda v: bf16_decode(bf16_rne_from_f64(v)).astype(np.float64)
+    El, H, I = cfg.E_loc, cfg.H, cfg.I
+    dw0, dw1, dwo = np.zeros((El, H, I)), np.zeros((El, H, I)), np.zeros((El, I, H))
+    dx = np.zeros((T, H))
+    for j in range(k):
+        e = ids[:, j]
+        loc = (e >= cfg.group_offset) & (e < cfg.group_offset + cfg.E_loc)
+        for g in np.unique(e[loc]):
+            rows = np.nonzero(e == g)[0]
+            gi = g - cfg.group_offset
+            xr = x[rows]
+            a = gl(xr @ W["wi_0"][gi])
+            b = gl(xr @ W["wi_1"][gi])
+            sg = 1.0 / (1.0 + np.exp(-a))
+            h = gl(a * sg * b)
+            dy = gl(data["topk_w"][rows, j].astype(np.float64)[:, None] * dout[rows])
+            dh = gl(dy @ W["wo"][gi].T)
+            dwo[gi] += h.T @ dy
+            da = gl(dh * b * sg * (1.0 + a * (1.0 - sg)))
+            db = gl(dh * a * sg)
+            dw0[gi] += xr.T @ da
+            dw1[gi] += xr.T @ db
+            dx[rows] += da @ W["wi_0"][gi].T + db @ W["wi_1"][gi].T
+    return bf16_rne_from_f64(dx), dw0, dw1, dwo
+
+
+def rel_norm_diff_f(g, ref):
+    """Frobenius-norm ratio of two float arrays (the pages' relative_norm_diff)."""
+    g = np.asarray(g, np.float64)
+    r = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(g - r) / np.linalg.norm(r))
+
+
 def rel_norm_diff(y_bits, ref_bits):
     y = bf16_decode(y_bits).astype(np.float64)
     r = bf16_decode(ref_bits).astype(np.float64)

@@ -10,7 +10,7 @@ import moe_fp8_grouped_amd as m
 from moe_fp8_grouped_amd.pipeline import BackwardPath, FFNBackwardPath, ForwardPath
 from oracle.gather_reduce import gather_reduce, gather_reduce_backward
 from oracle.gmm import gmm, tgmm
-from oracle.pipeline import dense_bf16_reference, rel_norm_diff
+from oracle.pipeline import dense_bf16_backward_reference, dense_bf16_reference, rel_norm_diff, rel_norm_diff_f
 from oracle.quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENSOR_STATIC, quantize_rows,
                              quantize_weights, silu_mul_backward)
 from oracle.sort import sort_by_expert
@@ -376,6 +376,17 @@ def test_gated_ffn_backward_stagewise(shape, fuse):
     # dx: unit-weight un-sort of dxs
     o = gather_reduce(dxs, True, inv, np.ones((T, k), np.float32))
     check_bf16(host(bwd.dx), o["out"], o["abs_sum"], "dx")
+    # fp8 gradients against an unquantized bf16 backward, next to the pages' TPU figures (context only)
+    rdx, rw0, rw1, rwo = dense_bf16_backward_reference(cfg, data, dout_bits)
+    dw01 = host(bwd.dw01)
+    rel = {"grad_wi_0": rel_norm_diff_f(dw01[:, :, :I], rw0), "grad_wi_1": rel_norm_diff_f(dw01[:, :, I:], rw1),
+           "grad_wo": rel_norm_diff_f(host(bwd.dwo), rwo), "dx": rel_norm_diff(host(bwd.dx), rdx)[0]}
+    page = accuracy_tables()[("rel", "megablox_fp8_dynamic_ep1")]
+    print(f"{shape} backward, fp8 vs bf16 dense relative_norm_diff: grad_wi_0 {rel['grad_wi_0']:.4f} "
+          f"grad_wi_1 {rel['grad_wi_1']:.4f} grad_wo {rel['grad_wo']:.4f} dx {rel['dx']:.4f} (pages, TPU v5p-8 "
+          f"whole layer, dynamic: grad_wi_0 {page[3]} grad_wi_1 {page[4]} grad_wo {page[5]} state_grad {page[1]})",
+          flush=True)
+    assert all(v < 0.3 for v in rel.values()), rel
 
 
 def test_expert_slice_with_no_routed_rows_forward_and_backward():
