@@ -156,6 +156,43 @@ int moe_quantize_weights(const void* w, int64_t E, int64_t K, int64_t N, int32_t
                          float* scale, void* stream);
 
 /*
+ * moe_quantize_rows_i8 -- absmax quantization of activations to symmetric
+ * int8 codes, the activation side of the int8 variant: "Keep qwix out of
+ * tpu-inference's fused MoE kernel and pre-quantize weights" ("Changes in
+ * this PR") allows int8 weights beside e4m3fn ones, and no matrix core
+ * multiplies int8 by fp8 codes, so int8 weights take int8 activations, with
+ * the per-token scales of "Quantize activations before EP all gather".
+ *
+ *   x        [R, C] bf16, rows contiguous, 16-byte aligned; C a multiple
+ *            of 16.
+ *   scale_mode MOE_SCALE_ROW_DYNAMIC (scale [R]), MOE_SCALE_TENSOR_DYNAMIC
+ *            (scale [1] from the whole tensor; row_amax [R] is required and
+ *            receives the rows' maxima), MOE_SCALE_TENSOR_STATIC (scale[0] =
+ *            static_scale, finite and > 0) or MOE_SCALE_TENSOR_FROM_ROW_AMAX
+ *            (scale [1] from the caller's row_amax [R]).
+ *   q        [R, C] int8 out, 8-byte aligned: q = clip(rint(f32(x / s)),
+ *            -127, 127), ties to even; s = f32(amax / 127), 1.0 for an
+ *            all-zero row or tensor.
+ *   row_amax [R] f32, optional in row mode (the rows' absmax out).
+ * Needs no workspace.  MOE_ERR_SHAPE for a bad size, alignment or static
+ * scale, MOE_ERR_NULL for a missing buffer, MOE_ERR_UNSUPPORTED for an
+ * unknown mode; R = 0 writes only the tensor scale.
+ */
+int moe_quantize_rows_i8(const void* x, int64_t R, int64_t C, int scale_mode, float static_scale, int8_t* q,
+                         float* scale, float* row_amax, void* stream);
+
+/*
+ * moe_quantize_weights_i8 -- moe_quantize_weights with int8 codes (the same
+ * passage allows int8 weights with the same [E, blocks, 1, N] scales):
+ * s = f32(amax / 127) per block (1.0 for an all-zero block),
+ * q = clip(rint(f32(w / s)), -127, 127) with ties to even.  Arguments,
+ * layouts and errors as in moe_quantize_weights; q is int8.
+ */
+int moe_quantize_weights_i8(const void* w, int64_t E, int64_t K, int64_t N, int32_t kb, int32_t nb,
+                            int scale_mode, float static_scale, int transpose_out, int8_t* q,
+                            float* scale, void* stream);
+
+/*
  * moe_sort_by_expert -- stable ragged sort of routed rows into per-expert
  * groups, and the gather of the quantized token rows into that order.
  * Defined by "Quantize activations before EP all gather" (review comments on
@@ -294,6 +331,26 @@ int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, 
                 const int32_t* group_sizes, int32_t E, int32_t group_offset,
                 int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
                 void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_gmm_i8 -- moe_gmm_fp8 with int8 operands (codes in [-127, 127] from
+ * moe_quantize_rows_i8 / moe_quantize_weights_i8), the int8 weights of "Keep
+ * qwix out of tpu-inference's fused MoE kernel and pre-quantize weights"
+ * ("Changes in this PR") with the 32-bit accumulator its description shows
+ * quantized operands need.  The products are summed exactly in int32 by the
+ * int8 matrix cores (exact for K up to 2^17); with one K block the sum is
+ * converted to float32 once, with several each block's exact sum is scaled
+ * and added in float32:
+ *   out[r, c] = ls[r] * sum_b rs[g, b, 0, c*Nb/N] * P_b[r, c],
+ *   P_b = sum_{k in block b} lhs[r, k] * W_g[k, c] (an integer).
+ * Arguments, layouts, workspace, size rules and errors as in moe_gmm_fp8;
+ * K <= 2^17 (MOE_ERR_SHAPE beyond).
+ */
+int moe_gmm_i8(const int8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const int8_t* rhs,
+               const float* rhs_scale, int32_t Kb, int32_t Nb, int transpose_rhs,
+               const int32_t* group_sizes, int32_t E, int32_t group_offset,
+               int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
+               void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_tgmm_fp8 -- transposed grouped matmul for weight gradients, the tgmm2

@@ -35,6 +35,9 @@ SIGNATURES = {
     "moe_quantize_rows": (_I, [_P, _P, _I, _I64, _I64, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_rows_strided": (_I, [_P, _P, _I64, _I, _I64, _I64, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "moe_quantize_weights": (_I, [_P, _I64, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _I, _F, _I, _P, _P, _P]),
+    "moe_quantize_rows_i8": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _P, _P]),
+    "moe_quantize_weights_i8": (_I, [_P, _I64, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _I, _F, _I, _P, _P,
+                                     _P]),
     "moe_sort_by_expert": (_I, [_P, _I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                 _I, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_sort_by_expert_noalloc": (_I, [_P, _I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
@@ -43,6 +46,8 @@ SIGNATURES = {
                                          ctypes.c_int32, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_gmm_fp8": (_I, [_P, _P, _I, _P, _P, ctypes.c_int32, ctypes.c_int32, _I, _P, ctypes.c_int32, ctypes.c_int32,
                          ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
+    "moe_gmm_i8": (_I, [_P, _P, _I, _P, _P, ctypes.c_int32, ctypes.c_int32, _I, _P, ctypes.c_int32, ctypes.c_int32,
+                        ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_tgmm_fp8": (_I, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                           ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_gather_reduce": (_I, [_P, _I, _P, _P, _I64, ctypes.c_int32, _I64, _I, _P, _P]),
@@ -160,6 +165,16 @@ def moe_quantize_weights(w, E, K, N, kb, nb, scale_mode, static_scale, transpose
                  transpose_out, _ptr(q), _ptr(scale), _stream(stream))
 
 
+def moe_quantize_rows_i8(x, R, C, scale_mode, static_scale, q, scale, row_amax=None, stream=None):
+    return _call("moe_quantize_rows_i8", _ptr(x), R, C, scale_mode, float(static_scale), _ptr(q), _ptr(scale),
+                 _ptr(row_amax), _stream(stream))
+
+
+def moe_quantize_weights_i8(w, E, K, N, kb, nb, scale_mode, static_scale, transpose_out, q, scale, stream=None):
+    return _call("moe_quantize_weights_i8", _ptr(w), E, K, N, kb, nb, scale_mode, float(static_scale),
+                 transpose_out, _ptr(q), _ptr(scale), _stream(stream))
+
+
 def moe_sort_by_expert(expert_ids, T, k, E, group_offset, num_local_experts, xq, xscale, xscale_mode, H, M_cap,
                        perm, inv_pos, group_sizes, xs, ss, ws, stream=None):
     return _call("moe_sort_by_expert", _ptr(expert_ids), T, k, E, group_offset, num_local_experts, _ptr(xq),
@@ -185,6 +200,13 @@ def moe_quantize_sort_by_expert(x, T, H, scale_mode, static_scale, expert_ids, k
 def moe_gmm_fp8(lhs, lhs_scale, lhs_scale_mode, rhs, rhs_scale, Kb, Nb, transpose_rhs, group_sizes, E,
                 group_offset, num_local_experts, M, K, N, out_dtype, out, ws, stream=None):
     return _call("moe_gmm_fp8", _ptr(lhs), _ptr(lhs_scale), lhs_scale_mode, _ptr(rhs), _ptr(rhs_scale), Kb, Nb,
+                 transpose_rhs, _ptr(group_sizes), E, group_offset, num_local_experts, M, K, N, out_dtype,
+                 _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_gmm_i8(lhs, lhs_scale, lhs_scale_mode, rhs, rhs_scale, Kb, Nb, transpose_rhs, group_sizes, E,
+               group_offset, num_local_experts, M, K, N, out_dtype, out, ws, stream=None):
+    return _call("moe_gmm_i8", _ptr(lhs), _ptr(lhs_scale), lhs_scale_mode, _ptr(rhs), _ptr(rhs_scale), Kb, Nb,
                  transpose_rhs, _ptr(group_sizes), E, group_offset, num_local_experts, M, K, N, out_dtype,
                  _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
 

@@ -58,6 +58,15 @@ __device__ __forceinline__ uint32_t quantize_one(float x, float s) {
   return e4m3_encode(v);
 }
 
+// x / s rounded to the nearest integer (ties to even) and saturated to the
+// symmetric int8 range [-127, 127]; the quotient is the IEEE float32 divide.
+// Returns the code's byte.
+__device__ __forceinline__ uint32_t quantize_one_i8(float x, float s) {
+  float v = __builtin_rintf(x / s);
+  v = fminf(fmaxf(v, -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int>(v)) & 0xffu;
+}
+
 // ---------------------------------------------------------------- pinned exp
 // float32 exp by Cody & Waite's two-constant argument reduction and the
 // degree-7 Taylor polynomial of exp(r) in Horner form, every multiply and add

@@ -318,7 +318,9 @@ constexpr int loads_per_step() { return C::SLOTS + (KBLOCKS ? 1 : 0); }   // per
 // contiguous, row stride K, group g's contraction at columns
 // 128 * tiles_off[g] .. of both (its rows, zero-padded to a multiple of 128);
 // rows = the group table's row bound (max_rows).  Empty groups get zeros.
-template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH = false>
+// I8: int8 operands (v_mfma_i32_16x16x64_i8 pairs, int32 accumulation; with
+// blockwise scales each step's exact int32 product is folded in float32).
+template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH = false, bool I8 = false>
 __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
                                                        int ls_per_row, const uint8_t* __restrict__ rhs,
                                                        const float* __restrict__ rs, int Kb, int Nb,
@@ -515,11 +517,17 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
           if (KBLOCKS) {
-            const v4f p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
+            v4f p;
+            if constexpr (I8)
+              p = __builtin_convertvector(mfma_i8x2(b[j], a, v4i32{0, 0, 0, 0}), v4f);   // exact: |p| < 2^24
+            else
+              p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
             acc[i][j][0] = fmaf(s_col[j].x, p[0], acc[i][j][0]);
             acc[i][j][1] = fmaf(s_col[j].y, p[1], acc[i][j][1]);
             acc[i][j][2] = fmaf(s_col[j].z, p[2], acc[i][j][2]);
             acc[i][j][3] = fmaf(s_col[j].w, p[3], acc[i][j][3]);
+          } else if constexpr (I8) {      // the int32 sums live in the accumulator's registers
+            acc[i][j] = __builtin_bit_cast(v4f, mfma_i8x2(b[j], a, __builtin_bit_cast(v4i32, acc[i][j])));
           } else {
             acc[i][j] = mfma_f8(b[j], a, acc[i][j]);
           }
@@ -527,6 +535,12 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       }
     }
 
+    if constexpr (I8 && !KBLOCKS) {   // the int32 sums to float32 (rounded to nearest beyond 2^24)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < JN; ++j) acc[i][j] = __builtin_convertvector(__builtin_bit_cast(v4i32, acc[i][j]), v4f);
+    }
     // ---- epilogue: out = ls[row] * (rs[col] *) acc
     // The product is formed transposed per 16 x 16 block (D = B^T A^T), so
     // lane l holds output row rbase + 16i + l%16 and the four consecutive
@@ -1387,7 +1401,7 @@ __global__ __launch_bounds__(g256::THREADS) void gmm256_kernel(const uint8_t* __
 }
 
 // Launch one configuration: persistent grid of (workgroups per CU) x CUs.
-template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16>
+template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool I8>
 hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs, int Kb,
                       int Nb, const int32_t* gs, int g0, int El, int64_t M, int64_t K, int64_t N, void* out,
                       int32_t* err, hipStream_t st) {
@@ -1397,7 +1411,7 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
   int64_t grid = static_cast<int64_t>(per_cu) * tile::num_cus();
   if (ub < grid) grid = ub;
   if (grid < 8) grid = 8;
-  if constexpr (TRANS && !KBLOCKS && OUT_BF16 && MOE_GMM256 != 0) {
+  if constexpr (TRANS && !KBLOCKS && OUT_BF16 && !I8 && MOE_GMM256 != 0) {
     // measured: faster from 1536 output columns on; with fewer n-tiles the
     // 256 x 128 tiles balance better over the CUs
     if (N % g256::BN == 0 && N >= 1536) {
@@ -1406,7 +1420,7 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
       return hipGetLastError();
     }
   }
-  if constexpr (MOE_GMM_STREAM != 0) {
+  if constexpr (MOE_GMM_STREAM != 0 && !I8) {
     if (El <= kStreamMaxLocal) {
       gmm_stream_kernel<C, TRANS, KBLOCKS, OUT_BF16, false>
           <<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N,
@@ -1414,17 +1428,19 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
       return hipGetLastError();
     }
   }
-  gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
+  gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16, false, I8><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
       lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err, 0, MOE_GMM_WIDE_ALL);
   return hipGetLastError();
 }
 
-template <class C, bool TRANS, bool KBLOCKS>
+template <class C, bool TRANS, bool KBLOCKS, bool I8>
 hipError_t launch_dtype(bool bf16, const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs,
                         const float* rs, int Kb, int Nb, const int32_t* gs, int g0, int El, int64_t M, int64_t K,
                         int64_t N, void* out, int32_t* err, hipStream_t st) {
-  return bf16 ? launch_cfg<C, TRANS, KBLOCKS, true>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err, st)
-              : launch_cfg<C, TRANS, KBLOCKS, false>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err, st);
+  return bf16 ? launch_cfg<C, TRANS, KBLOCKS, true, I8>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out,
+                                                        err, st)
+              : launch_cfg<C, TRANS, KBLOCKS, false, I8>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out,
+                                                         err, st);
 }
 
 }  // namespace
@@ -1433,7 +1449,7 @@ size_t gmm_ws_bytes() { return tile::kHdr; }
 
 hipError_t gmm_edge_launch(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs,
                            int Kb, int Nb, bool trans, const int32_t* gs, int g0, int El, int64_t M, int64_t K,
-                           int64_t N, bool bf16, void* out, int32_t* err, hipStream_t st);
+                           int64_t N, bool bf16, bool i8, void* out, int32_t* err, hipStream_t st);
 
 // The weight-gradient product on the gmm pipeline: for each local group g,
 // out[g] (M x N, f32 or bf16) = ls[m] * rs[n] * sum_r A[m, c_g + r] B[n, c_g + r]
@@ -1471,13 +1487,17 @@ hipError_t gmm_batched_launch(const uint8_t* A, const float* ls, int ls_len, con
 
 }  // namespace moe
 
-extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const uint8_t* rhs,
-                           const float* rhs_scale, int32_t Kb, int32_t Nb, int transpose_rhs,
-                           const int32_t* group_sizes, int32_t E, int32_t group_offset,
-                           int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
-                           void* out, void* ws, size_t ws_bytes, void* stream) {
+namespace moe {
+namespace {
+// Validation and dispatch shared by the e4m3fn and the int8 entry points.
+template <bool I8>
+int gmm_entry(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const uint8_t* rhs,
+              const float* rhs_scale, int32_t Kb, int32_t Nb, int transpose_rhs, const int32_t* group_sizes,
+              int32_t E, int32_t group_offset, int32_t num_local_experts, int64_t M, int64_t K, int64_t N,
+              int out_dtype, void* out, void* ws, size_t ws_bytes, void* stream) {
   using moe::tile::kMaxLocal;
   if (M < 0 || K <= 0 || N <= 0 || K % 16 || N % 16) return MOE_ERR_SHAPE;
+  if (I8 && K > (int64_t{1} << 17)) return MOE_ERR_SHAPE;   // 127^2 * 2^17 < 2^31: the int32 sums stay exact
   if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 || num_local_experts > kMaxLocal ||
       group_offset + num_local_experts > E)
     return MOE_ERR_SHAPE;
@@ -1505,13 +1525,35 @@ extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_s
   hipError_t e;
   if (K % 128 || N % 128)        // multiples of 16 only: the edge kernel
     return moe::gmm_edge_launch(lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, transpose_rhs != 0, group_sizes,
-                                group_offset, El, M, K, N, bf16, out, err, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+                                group_offset, El, M, K, N, bf16, I8, out, err, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   using C = moe::Cfg<MOE_GMM_CFG>;
 #define MOE_GMM_ARGS bf16, lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, group_sizes, group_offset, El, M, K, N, out, err, st
   if (transpose_rhs)
-    e = Kb > 1 ? moe::launch_dtype<C, true, true>(MOE_GMM_ARGS) : moe::launch_dtype<C, true, false>(MOE_GMM_ARGS);
+    e = Kb > 1 ? moe::launch_dtype<C, true, true, I8>(MOE_GMM_ARGS) : moe::launch_dtype<C, true, false, I8>(MOE_GMM_ARGS);
   else
-    e = Kb > 1 ? moe::launch_dtype<C, false, true>(MOE_GMM_ARGS) : moe::launch_dtype<C, false, false>(MOE_GMM_ARGS);
+    e = Kb > 1 ? moe::launch_dtype<C, false, true, I8>(MOE_GMM_ARGS)
+               : moe::launch_dtype<C, false, false, I8>(MOE_GMM_ARGS);
 #undef MOE_GMM_ARGS
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_gmm_fp8(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const uint8_t* rhs,
+                           const float* rhs_scale, int32_t Kb, int32_t Nb, int transpose_rhs,
+                           const int32_t* group_sizes, int32_t E, int32_t group_offset,
+                           int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
+                           void* out, void* ws, size_t ws_bytes, void* stream) {
+  return moe::gmm_entry<false>(lhs, lhs_scale, lhs_scale_mode, rhs, rhs_scale, Kb, Nb, transpose_rhs, group_sizes, E,
+                               group_offset, num_local_experts, M, K, N, out_dtype, out, ws, ws_bytes, stream);
+}
+
+extern "C" int moe_gmm_i8(const int8_t* lhs, const float* lhs_scale, int lhs_scale_mode, const int8_t* rhs,
+                          const float* rhs_scale, int32_t Kb, int32_t Nb, int transpose_rhs,
+                          const int32_t* group_sizes, int32_t E, int32_t group_offset,
+                          int32_t num_local_experts, int64_t M, int64_t K, int64_t N, int out_dtype,
+                          void* out, void* ws, size_t ws_bytes, void* stream) {
+  return moe::gmm_entry<true>(reinterpret_cast<const uint8_t*>(lhs), lhs_scale, lhs_scale_mode,
+                              reinterpret_cast<const uint8_t*>(rhs), rhs_scale, Kb, Nb, transpose_rhs, group_sizes, E,
+                              group_offset, num_local_experts, M, K, N, out_dtype, out, ws, ws_bytes, stream);
 }

@@ -38,7 +38,7 @@ __device__ __forceinline__ void scatter16(uint8_t* base, int r0, int col, const 
 // sum_{k in b} X[r, k] W_g[k, c], f32 accumulate; rows [n, M) zero.  Blockwise
 // K scales need K / Kb a multiple of 128 (the host rejects the rest), so every
 // 128-byte step lies in one scale block.
-template <bool TRANS, bool OUT_BF16>
+template <bool TRANS, bool OUT_BF16, bool I8>
 __global__ __launch_bounds__(256) void gmm_edge_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
                                                        int ls_per_row, const uint8_t* __restrict__ rhs,
                                                        const float* __restrict__ rs, int Kb, int Nb,
@@ -117,7 +117,11 @@ __global__ __launch_bounds__(256) void gmm_edge_kernel(const uint8_t* __restrict
           for (int q = 0; q < 4; ++q) s[q] = c + q < N ? rs_g[kb * Nb + (c + q) / ncb] : 0.f;
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            const v4f p = mfma_f8(b[j], a[i], v4f{0.f, 0.f, 0.f, 0.f});
+            v4f p;
+            if constexpr (I8)
+              p = __builtin_convertvector(mfma_i8x2(b[j], a[i], v4i32{0, 0, 0, 0}), v4f);
+            else
+              p = mfma_f8(b[j], a[i], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(s[q], p[q], acc[i][j][q]);
           }
@@ -126,7 +130,20 @@ __global__ __launch_bounds__(256) void gmm_edge_kernel(const uint8_t* __restrict
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f8(b[j], a[i], acc[i][j]);
+          for (int j = 0; j < 2; ++j) {
+            if constexpr (I8)
+              acc[i][j] = __builtin_bit_cast(v4f, mfma_i8x2(b[j], a[i], __builtin_bit_cast(v4i32, acc[i][j])));
+            else
+              acc[i][j] = mfma_f8(b[j], a[i], acc[i][j]);
+          }
+      }
+    }
+    if constexpr (I8) {
+      if (Kb == 1) {                              // the int32 sums to float32
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_convertvector(__builtin_bit_cast(v4i32, acc[i][j]), v4f);
       }
     }
     // epilogue: lane l holds row rbase + 16 i + l%16 and columns cbase + 16 j + 4 (l/16) .. +3
@@ -247,19 +264,21 @@ __global__ __launch_bounds__(256) void tgmm_edge_kernel(const uint8_t* __restric
 
 hipError_t gmm_edge_launch(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs,
                            int Kb, int Nb, bool trans, const int32_t* gs, int g0, int El, int64_t M, int64_t K,
-                           int64_t N, bool bf16, void* out, int32_t* err, hipStream_t st) {
+                           int64_t N, bool bf16, bool i8, void* out, int32_t* err, hipStream_t st) {
   const int64_t ub = (moe_cdiv(M, ET) + El) * moe_cdiv(N, ET);
   int64_t grid = 4LL * tile::num_cus();
   if (ub < grid) grid = ub;
   if (grid < 1) grid = 1;
   const unsigned gx = static_cast<unsigned>(grid);
-#define MOE_EDGE(TR, BF) \
-  gmm_edge_kernel<TR, BF><<<gx, 256, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err)
+#define MOE_EDGE(TR, BF, I) \
+  gmm_edge_kernel<TR, BF, I><<<gx, 256, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err)
+#define MOE_EDGE_I(TR, BF) do { if (i8) MOE_EDGE(TR, BF, true); else MOE_EDGE(TR, BF, false); } while (0)
   if (trans) {
-    if (bf16) MOE_EDGE(true, true); else MOE_EDGE(true, false);
+    if (bf16) MOE_EDGE_I(true, true); else MOE_EDGE_I(true, false);
   } else {
-    if (bf16) MOE_EDGE(false, true); else MOE_EDGE(false, false);
+    if (bf16) MOE_EDGE_I(false, true); else MOE_EDGE_I(false, false);
   }
+#undef MOE_EDGE_I
 #undef MOE_EDGE
   return hipGetLastError();
 }

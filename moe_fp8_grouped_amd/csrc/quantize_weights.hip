@@ -1,8 +1,10 @@
-// moe_quantize_weights: offline blockwise absmax quantization of expert
-// weights to e4m3fn with [E, kb, 1, nb] scales ("Keep qwix out of
-// tpu-inference's fused MoE kernel and pre-quantize weights", "Changes in
-// this PR").  Setup-time work, run once per weight; the output can be laid
-// out [E, K, N] or, for the matmul's preferred operand layout, [E, N, K].
+// moe_quantize_weights / moe_quantize_weights_i8: offline blockwise absmax
+// quantization of expert weights to e4m3fn (or int8) with [E, kb, 1, nb]
+// scales ("Keep qwix out of tpu-inference's fused MoE kernel and pre-quantize
+// weights", "Changes in this PR": either code type is allowed).  Setup-time
+// work, run once per weight; the output can be laid out [E, K, N] or, for the
+// matmul's preferred operand layout, [E, N, K].  The scale is amax / 448
+// (e4m3fn) or amax / 127 (int8, symmetric codes).
 #include "common.hpp"
 
 namespace moe {
@@ -11,7 +13,7 @@ namespace {
 // Per-output-channel case (block = bk rows x 1 column): one thread per
 // (e, b, column), columns contiguous across threads so loads coalesce.
 __global__ __launch_bounds__(256) void colmax_scale_kernel(const uint16_t* __restrict__ w, int64_t E,
-                                                           int64_t K, int64_t N, int kb, int nb,
+                                                           int64_t K, int64_t N, int kb, int nb, float qmax,
                                                            float* __restrict__ scale) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t total = E * kb * N;
@@ -23,12 +25,12 @@ __global__ __launch_bounds__(256) void colmax_scale_kernel(const uint16_t* __res
   const uint16_t* p = w + (e * K + b * bk) * N + n;
   float m = 0.0f;
   for (int64_t k = 0; k < bk; ++k) m = fmaxf(m, fabsf(bf16_to_f32(p[k * N])));
-  scale[(e * kb + b) * nb + n] = m == 0.0f ? 1.0f : m / 448.0f;
+  scale[(e * kb + b) * nb + n] = m == 0.0f ? 1.0f : m / qmax;
 }
 
 // General blocks (bn > 1 columns): one workgroup per (e, b, c) block.
 __global__ __launch_bounds__(256) void blockmax_scale_kernel(const uint16_t* __restrict__ w, int64_t K,
-                                                             int64_t N, int kb, int nb,
+                                                             int64_t N, int kb, int nb, float qmax,
                                                              float* __restrict__ scale) {
   __shared__ float red[4];
   const int64_t blk = blockIdx.x;
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(256) void blockmax_scale_kernel(const uint16_t* __r
   __syncthreads();
   if (threadIdx.x == 0) {
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    scale[blk] = m == 0.0f ? 1.0f : m / 448.0f;
+    scale[blk] = m == 0.0f ? 1.0f : m / qmax;
   }
 }
 
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(256) void fill_kernel(float* __restrict__ p, int64_
 // Quantize a 64 x 64 tile (rows k, columns n) of one expert, writing either
 // the same layout or the transposed one (through LDS, so both the read and
 // the write are coalesced).  Grid: (N/64, K/64, E), 256 threads.
-template <bool TRANSPOSE>
+template <bool TRANSPOSE, bool I8>
 __global__ __launch_bounds__(256) void quantize_tile_kernel(const uint16_t* __restrict__ w, int64_t K,
                                                             int64_t N, int kb, int nb,
                                                             const float* __restrict__ scale,
@@ -71,7 +73,8 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(const uint16_t* __re
     uint32_t code = 0;
     if (k < K && n < N) {
       const float s = sc[(k / bk) * nb + n / bn];
-      code = quantize_one(bf16_to_f32(w[(e * K + k) * N + n]), s);
+      const float x = bf16_to_f32(w[(e * K + k) * N + n]);
+      code = I8 ? quantize_one_i8(x, s) : quantize_one(x, s);
     }
     if (TRANSPOSE)
       tile[r][c] = static_cast<uint8_t>(code);
@@ -91,9 +94,11 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(const uint16_t* __re
 }  // namespace
 }  // namespace moe
 
-extern "C" int moe_quantize_weights(const void* w, int64_t E, int64_t K, int64_t N, int32_t kb,
-                                    int32_t nb, int scale_mode, float static_scale, int transpose_out,
-                                    uint8_t* q, float* scale, void* stream) {
+namespace moe {
+namespace {
+int quantize_weights_entry(bool i8, const void* w, int64_t E, int64_t K, int64_t N, int32_t kb, int32_t nb,
+                           int scale_mode, float static_scale, int transpose_out, uint8_t* q, float* scale,
+                           void* stream) {
   if (E < 0 || K <= 0 || N <= 0 || K % 16 || N % 16) return MOE_ERR_SHAPE;
   if (kb <= 0 || nb <= 0 || K % kb || N % nb) return MOE_ERR_SHAPE;
   if (scale_mode != MOE_SCALE_ROW_DYNAMIC && scale_mode != MOE_SCALE_TENSOR_STATIC) return MOE_ERR_UNSUPPORTED;
@@ -105,21 +110,40 @@ extern "C" int moe_quantize_weights(const void* w, int64_t E, int64_t K, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint16_t* wb = static_cast<const uint16_t*>(w);
   const int64_t nscale = E * kb * nb;
+  const float qmax = i8 ? 127.0f : 448.0f;
   if (scale_mode == MOE_SCALE_TENSOR_STATIC) {
-    moe::fill_kernel<<<static_cast<unsigned>(moe_cdiv(nscale, 256)), 256, 0, st>>>(scale, nscale, static_scale);
+    fill_kernel<<<static_cast<unsigned>(moe_cdiv(nscale, 256)), 256, 0, st>>>(scale, nscale, static_scale);
   } else if (nb == N) {
-    moe::colmax_scale_kernel<<<static_cast<unsigned>(moe_cdiv(E * kb * N, 256)), 256, 0, st>>>(wb, E, K, N, kb,
-                                                                                            nb, scale);
+    colmax_scale_kernel<<<static_cast<unsigned>(moe_cdiv(E * kb * N, 256)), 256, 0, st>>>(wb, E, K, N, kb, nb, qmax,
+                                                                                       scale);
   } else {
-    moe::blockmax_scale_kernel<<<static_cast<unsigned>(nscale), 256, 0, st>>>(wb, K, N, kb, nb, scale);
+    blockmax_scale_kernel<<<static_cast<unsigned>(nscale), 256, 0, st>>>(wb, K, N, kb, nb, qmax, scale);
   }
   MOE_CHECK_LAUNCH();
   const dim3 grid(static_cast<unsigned>(moe_cdiv(N, 64)), static_cast<unsigned>(moe_cdiv(K, 64)),
                   static_cast<unsigned>(E));
   if (transpose_out)
-    moe::quantize_tile_kernel<true><<<grid, 256, 0, st>>>(wb, K, N, kb, nb, scale, q);
+    i8 ? quantize_tile_kernel<true, true><<<grid, 256, 0, st>>>(wb, K, N, kb, nb, scale, q)
+       : quantize_tile_kernel<true, false><<<grid, 256, 0, st>>>(wb, K, N, kb, nb, scale, q);
   else
-    moe::quantize_tile_kernel<false><<<grid, 256, 0, st>>>(wb, K, N, kb, nb, scale, q);
+    i8 ? quantize_tile_kernel<false, true><<<grid, 256, 0, st>>>(wb, K, N, kb, nb, scale, q)
+       : quantize_tile_kernel<false, false><<<grid, 256, 0, st>>>(wb, K, N, kb, nb, scale, q);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_quantize_weights(const void* w, int64_t E, int64_t K, int64_t N, int32_t kb,
+                                    int32_t nb, int scale_mode, float static_scale, int transpose_out,
+                                    uint8_t* q, float* scale, void* stream) {
+  return moe::quantize_weights_entry(false, w, E, K, N, kb, nb, scale_mode, static_scale, transpose_out, q, scale,
+                                     stream);
+}
+
+extern "C" int moe_quantize_weights_i8(const void* w, int64_t E, int64_t K, int64_t N, int32_t kb,
+                                       int32_t nb, int scale_mode, float static_scale, int transpose_out,
+                                       int8_t* q, float* scale, void* stream) {
+  return moe::quantize_weights_entry(true, w, E, K, N, kb, nb, scale_mode, static_scale, transpose_out,
+                                     reinterpret_cast<uint8_t*>(q), scale, stream);
 }

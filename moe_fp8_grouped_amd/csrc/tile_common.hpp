@@ -25,6 +25,19 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// The int8 counterpart of mfma_f8 on the same 32-byte fragments: two
+// v_mfma_i32_16x16x64_i8, the first on bytes 0..15 of every lane's share of
+// the contraction, the second on bytes 16..31.  Both operands split their
+// fragments the same way, so the pair sums every product exactly once, in
+// int32 (exact for |codes| <= 127 below 2^17 terms).
+__device__ __forceinline__ v4i32 mfma_i8x2(const v8i& a, const v8i& b, v4i32 c) {
+  c = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i32{a[0], a[1], a[2], a[3]}, v4i32{b[0], b[1], b[2], b[3]}, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i32{a[4], a[5], a[6], a[7]}, v4i32{b[4], b[5], b[6], b[7]}, c, 0, 0,
+                                               0);
+}
+
 // Fragment of a K-contiguous staged tile: 32 bytes at row `row`, byte 32*grp.
 __device__ __forceinline__ v8i frag_rows(const uint8_t* lds, int row, int grp) {
   const uint4* p = reinterpret_cast<const uint4*>(lds + row * LDS_STRIDE + 32 * grp);

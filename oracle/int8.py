@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 What the pages fix:
 
-* Weights are pre-quantized outside the kernel "to float8_e4m3fn (or int8)"
+* Weights are pre-quantized outside the kernel, to e4m3fn or to int8 codes,
   with [E, blocks, 1, N] scales, blockwise or channelwise ("Keep qwix out of
   tpu-inference's fused MoE kernel and pre-quantize weights", "Changes in
   this PR").
@@ -99,13 +99,13 @@ def quantize_weights_int8(w_bits, kb, nb, static_scale=None):
     if K % kb or N % nb:
         raise ValueError("quantize_weights_int8: blocks must tile the matrix")
     bk, bn = K // kb, N // nb
+    wb = w.reshape(E, kb, bk, nb, bn)                 # [expert, K block, row in block, N block, column in block]
     if static_scale is None:
-        amax = np.abs(w).reshape(E, kb, bk, nb, bn).max(axis=(2, 4))
-        s = _scale_from_amax(amax)
+        s = _scale_from_amax(np.abs(wb).max(axis=(2, 4)))
     else:
         s = np.full((E, kb, nb), static_scale, dtype=np.float32)
-    s_full = np.repeat(np.repeat(s, bk, axis=1), bn, axis=2)
-    return _quantize_with_scale(w, s_full), s.reshape(E, kb, 1, nb).astype(np.float32)
+    q = _quantize_with_scale(wb, s[:, :, None, :, None]).reshape(E, K, N)
+    return q, s.reshape(E, kb, 1, nb).astype(np.float32)
 
 
 def gmm_int8(lhs_q, lhs_scale, rhs_q, rhs_scale, group_sizes, group_offset, num_local_experts,

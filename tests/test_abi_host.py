@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_path_calls():
     names = _declared_functions()
     for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_sort_by_expert_noalloc", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
-               "moe_gather_reduce_backward", "moe_silu_mul_backward", "moe_quantize_weights", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
+               "moe_gather_reduce_backward", "moe_silu_mul_backward", "moe_quantize_weights", "moe_quantize_rows_i8",
+               "moe_quantize_weights_i8", "moe_gmm_i8", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
                "moe_version"]:
         assert fn in names
 
@@ -236,3 +237,34 @@ def test_weight_quantizer_validation(lib):
     assert q(one, 2, 256, 256, 1, 256, 0, 0.0, 2, one, one, None) == m.MOE_ERR_UNSUPPORTED
     assert q(None, 2, 256, 256, 1, 256, 0, 0.0, 0, one, one, None) == m.MOE_ERR_NULL
     assert q(None, 0, 256, 256, 1, 256, 0, 0.0, 0, None, None, None) == m.MOE_OK
+
+
+def test_int8_quantizer_validation(lib):
+    f = lambda *a: _c(lib, "moe_quantize_rows_i8", *a)
+    p = 4096                       # non-null, 16-byte aligned dummy pointer: never dereferenced on these paths
+    assert f(p, 4, 24, 0, 0.0, p, p, None, None) == m.MOE_ERR_SHAPE                    # C % 16
+    assert f(p, -1, 32, 0, 0.0, p, p, None, None) == m.MOE_ERR_SHAPE
+    assert f(p, 4, 32, 7, 0.0, p, p, None, None) == m.MOE_ERR_UNSUPPORTED
+    assert f(p, 4, 32, m.MOE_SCALE_TENSOR_STATIC, 0.0, p, p, None, None) == m.MOE_ERR_SHAPE   # bad static scale
+    assert f(p, 4, 32, 0, 0.0, p, None, None, None) == m.MOE_ERR_NULL
+    assert f(None, 4, 32, 0, 0.0, p, p, None, None) == m.MOE_ERR_NULL
+    for mode in (m.MOE_SCALE_TENSOR_DYNAMIC, m.MOE_SCALE_TENSOR_FROM_ROW_AMAX):
+        assert f(p, 4, 32, mode, 0.0, p, p, None, None) == m.MOE_ERR_NULL         # the row maxima are needed
+    assert f(p + 8, 4, 32, 0, 0.0, p, p, None, None) == m.MOE_ERR_SHAPE            # x not 16-byte aligned
+    w = lambda *a: _c(lib, "moe_quantize_weights_i8", *a)
+    assert w(p, 2, 256, 250, 1, 250, 0, 0.0, 0, p, p, None) == m.MOE_ERR_SHAPE
+    assert w(p, 2, 256, 256, 1, 256, 0, 0.0, 2, p, p, None) == m.MOE_ERR_UNSUPPORTED
+    assert w(None, 0, 256, 256, 1, 256, 0, 0.0, 0, None, None, None) == m.MOE_OK
+
+
+def test_int8_gmm_validation(lib):
+    f = lambda *a: _c(lib, "moe_gmm_i8", *a)
+    one = 1
+    def call(M=256, K=256, N=256, Kb=1, Nb=256, tr=1, E=8, El=8, ws=one, wsb=256, lhs=one, out=one):
+        return f(lhs, one, 0, one, one, Kb, Nb, tr, one, E, 0, El, M, K, N, 0, out, ws, wsb, None)
+    assert call(K=200) == m.MOE_ERR_SHAPE
+    assert call(K=(1 << 17) + 128, Kb=1) == m.MOE_ERR_SHAPE       # the int32 sums could overflow
+    assert call(K=144, Kb=2) == m.MOE_ERR_UNSUPPORTED
+    assert call(lhs=None) == m.MOE_ERR_NULL
+    assert call(wsb=8) == m.MOE_ERR_WORKSPACE
+    assert call(M=0, out=None) == m.MOE_OK
