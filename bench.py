@@ -17,6 +17,10 @@ Prints one JSON line:
 
   value      whole-step throughput: algorithmic GMM flops of a step / step
              time, the step replayed as a HIP graph (K timed replays after W)
+  settle     directly before each timed region (and its W warm-up steps),
+             untimed steps for --settle-s seconds (0.3 by default): after any
+             host-side pause the first ~50 steps run slower while the clocks
+             ramp up; the record keeps the ms per step of the first K steps
   roofline   the dominant kernel, the fused input projections' moe_gmm_fp8
              launch: its algorithmic bytes (and flops) per launch / its
              average duration by HIP events around each launch on its own
@@ -29,7 +33,8 @@ Prints one JSON line:
   secondary  the other workloads: the gated FFN forward (config 2, one and
              three rotating buffer sets), the MoE backward (config 5, one and
              three sets), the gated FFN's backward, the tiny and skewed
-             up-projections (configs 1, 3 and the large skewed variant)
+             up-projections (configs 1, 3 and the large skewed variant), and
+             the line of record's two grouped matmuls in the int8 variant
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, timed
              stage by stage on the host's cores (plus configs 1 and 3 whole,
              single-threaded and on every core)
@@ -88,6 +93,63 @@ def _stats(durs_ms):
     d = np.asarray(durs_ms, np.float64) * 1e3
     return {"avg_us": round(float(d.mean()), 2), "median_us": round(float(np.median(d)), 2),
             "min_us": round(float(d.min()), 2)}
+
+
+SETTLE_S = 0.3     # --settle-s
+
+
+def eager_step(calls):
+    def run():
+        for _, fn in calls:
+            fn()
+    return run
+
+
+def settle(step, steps):
+    """Untimed runs of ``step`` (a callable doing one whole step) for
+    SETTLE_S seconds, directly before a timed region.  After any pause --
+    the host-side gaps of data generation, graph capture or event
+    read-back, even ~1 ms -- the device runs the next ~50 expert-slice steps
+    (~40 ms) up to 15-40 % slower while its clocks ramp up again, and a
+    default window of warm-up plus timed steps would fall inside that ramp.
+    Returns the settle record: seconds, steps run, and the ms per step of
+    its first ``steps`` runs (the unsettled figure)."""
+    if SETTLE_S <= 0:
+        return {"s": 0.0, "steps": 0}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    first = (time.perf_counter() - t0) * 1e3 / steps
+    n = steps
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return {"s": SETTLE_S, "steps": n, "ms_per_step_first_steps": round(first, 4)}
+
+
+def rotation(paths):
+    state = {"i": 0}
+
+    def run():
+        paths[state["i"] % len(paths)].replay()
+        state["i"] += 1
+    return run
+
+
+def time_back_to_back(calls, steps):
+    """ms per step of ``steps`` eager steps launched back to back (no events
+    between launches), bracketed by device synchronisations."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def time_calls(calls, steps, warmup):
@@ -207,16 +269,66 @@ def measure_forward(path, steps, warmup):
     """Per-launch HIP-event durations over ``steps`` eager steps, then the
     step as a HIP graph: ``steps`` timed replays after ``warmup``."""
     acc = step_accounting(path)
-    durs, ms_eager = time_calls(step_calls(path), steps, warmup)
+    calls = step_calls(path)
+    st = settle(eager_step(calls), steps)
+    durs, ms_eager = time_calls(calls, steps, warmup)
     kern = {nm: kern_entry(d, acc[nm]["bytes"], acc[nm]["flops"]) for nm, d in durs.items()}
+    settle(eager_step(calls), steps)
+    ms_b2b = time_back_to_back(calls, steps)
     path.capture_graph(warmup=1)
+    settle(path.replay, steps)
     ms = time_replays([path], steps, warmup)
     flops = sum(a["flops"] for a in acc.values())
     cfg = path.cfg
     return {"workload": workload_name(cfg), "routed_local_rows": path.n_local, "m_cap": path.m_cap,
             "ms_per_step": round(ms, 4), "ms_per_step_eager": round(ms_eager, 4),
+            "ms_per_step_eager_back_to_back": round(ms_b2b, 4), "settle": st,
             "gmm_flops_per_step": int(flops), "gmm_TFLOP_s_whole_step": round(flops / (ms * 1e-3) / 1e12, 1),
             "kernels": kern}, durs, acc
+
+
+def int8_gmm_timing(path, acc, steps, warmup):
+    """The two grouped matmuls of the expert-slice step in the int8 variant
+    (moe_gmm_i8, int8 codes, int32 accumulation), on the step's own group
+    sizes and row capacity, with random codes and scales (the int8 matrix
+    cores' speed does not depend on the values).  Same algorithmic bytes and
+    operations as the fp8 launches (one byte per code); int8 dense peak 5.0
+    POP/s, the fp8 one."""
+    import moe_fp8_grouped_amd as m
+    cfg = path.cfg
+    g = torch.Generator(device="cuda").manual_seed(11)
+    El, H, I, m_cap = cfg.E_loc, cfg.H, cfg.I, path.m_cap
+    lhs = torch.randint(-127, 128, (m_cap, H), dtype=torch.int8, device="cuda", generator=g)
+    h = torch.randint(-127, 128, (m_cap, I), dtype=torch.int8, device="cuda", generator=g)
+    ls = torch.rand(m_cap, device="cuda", generator=g) + 0.5
+    w01 = torch.randint(-127, 128, (El, 2 * I, H), dtype=torch.int8, device="cuda", generator=g)
+    wo = torch.randint(-127, 128, (El, H, I), dtype=torch.int8, device="cuda", generator=g)
+    s01 = torch.rand((El, H // 128, 1, 2 * I // 128), device="cuda", generator=g) * 1e-3
+    so = torch.rand((El, I // 128, 1, H // 128), device="cuda", generator=g) * 1e-3
+    y01 = torch.empty((m_cap, 2 * I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((m_cap, H), dtype=torch.bfloat16, device="cuda")
+    ws = m.workspace(m.MOE_OP_GMM, m_cap, H, max(H, 2 * I), cfg.E)
+
+    def gmm(a, w, s, out, K, N):
+        m.moe_gmm_i8(a, ls, m.MOE_SCALE_ROW_DYNAMIC, w, s, s.shape[1], s.shape[3], 1, path.group_sizes, cfg.E,
+                     cfg.group_offset, El, m_cap, K, N, m.MOE_BF16, out, ws)
+
+    calls = [("gmm_wi_01", lambda: gmm(lhs, w01, s01, y01, H, 2 * I)), ("gmm_wo", lambda: gmm(h, wo, so, y, I, H))]
+    settle(eager_step(calls), steps)
+    durs, _ = time_calls(calls, steps, warmup)
+    if m.moe_debug_check(ws) != 0:
+        raise RuntimeError("moe_gmm_i8 flagged a device error")
+    res = {"workload": workload_name(cfg) + ", int8 operands (moe_gmm_i8) on the step's group sizes",
+           "kernels": {}}
+    for nm, d in durs.items():
+        e = kern_entry(d, acc[nm]["bytes"])
+        tops = acc[nm]["flops"] / (e["avg_us"] * 1e-6) / 1e12
+        e.update({"alg_ops": int(acc[nm]["flops"]), "TOP_s": round(tops, 1),
+                  "frac_int8_peak": round(tops / PEAK_FP8_TFLOPS, 4)})
+        res["kernels"]["i8_" + nm] = e
+    del lhs, h, w01, wo, y01, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def workload_name(cfg, static=False):
@@ -275,6 +387,7 @@ def rotating_forward(cid, steps, warmup, nsets=3):
         p.capture_graph(warmup=1)
         paths.append(p)
     nrep = max(steps, nsets) // nsets * nsets
+    settle(rotation(paths), nrep)
     ms = time_replays(paths, nrep, warmup)
     flops = sum(a["flops"] for a in step_accounting(paths[0]).values())
     res = {"workload": workload_name(paths[0].cfg) + f", {nsets} independent weight and buffer sets in rotation",
@@ -305,8 +418,10 @@ def secondary_backward(steps, warmup, nsets=3):
     M = T * k
     calls = [("quantize_x_and_sort", path.quantize_and_sort), ("quantize_dy_row_and_tensor", path.quantize_dy),
              ("gmm_dx", path.grad_input), ("tgmm_dw", path.grad_weight)]
+    settle(eager_step(calls), steps)
     durs, ms_eager = time_calls(calls, steps, warmup)
     path.capture_graph(warmup=1)
+    settle(path.replay, steps)
     ms = time_replays([path], steps, warmup)
     qx = T * H * 2 + 4 if path.fused_quantize else T * H * 3 + 4 + T * H
     by = {"quantize_x_and_sort": qx + (M * 4 + 2 * M * 4 + E * 4 + M * H),
@@ -323,6 +438,7 @@ def secondary_backward(steps, warmup, nsets=3):
     for p in paths[1:]:
         p.capture_graph(warmup=1)
     nrep = max(steps, nsets) // nsets * nsets
+    settle(rotation(paths), nrep)
     msr = time_replays(paths, nrep, warmup)
     res["rotating_sets"] = {"sets": nsets, "steps": nrep, "ms_per_step": round(msr, 4),
                             "gmm_TFLOP_s_whole_step": round(flops / (msr * 1e-3) / 1e12, 1)}
@@ -347,8 +463,11 @@ def secondary_ffn_backward(steps, warmup):
     del weights
     names = ("combine_backward", "quantize_dy", "grad_h", "grad_wo", "silu_backward", "quantize_dab",
              "grad_x_sorted", "grad_w01", "grad_x")
-    durs, ms_eager = time_calls([(nm, getattr(b, nm)) for nm in names], min(steps, 10), warmup)
+    calls = [(nm, getattr(b, nm)) for nm in names]
+    settle(eager_step(calls), min(steps, 10))
+    durs, ms_eager = time_calls(calls, min(steps, 10), warmup)
     b.capture_graph(warmup=1)
+    settle(b.replay, steps)
     ms = time_replays([b], steps, warmup)
     fl = {"grad_h": 2 * n * H * I, "grad_wo": 2 * n * I * H, "grad_x_sorted": 2 * n * 2 * I * H,
           "grad_w01": 2 * n * H * 2 * I}
@@ -476,6 +595,7 @@ def cpu_baseline(cfg4_data, n_local_experts=8, reps_small=5):
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -484,9 +604,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the other workloads measured beside the line of record")
+    ap.add_argument("--settle-s", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before each timed region (clock ramp; 0 to skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (profiler byte-counter calibration)")
     a = ap.parse_args()
+    SETTLE_S = a.settle_s
     if a.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for {a.gpus}); expert parallelism is modelled "
               f"as one GPU's expert slice", file=sys.stderr)
@@ -509,12 +632,18 @@ def main():
     head, durs, acc = measure_forward(path, a.steps, a.warmup)
     dominant = "gmm_wi_01" if cfg.pipeline == "ffn" else "gmm_w_up"
     roof = roofline(durs[dominant], acc[dominant])
+    int8 = None
+    if not a.no_secondary and cfg.pipeline == "ffn" and cfg.weight_block_k and cfg.weight_block_n > 1:
+        print("bench: int8 grouped matmuls", file=sys.stderr, flush=True)
+        int8 = int8_gmm_timing(path, acc, a.steps, a.warmup)
     del path
     torch.cuda.empty_cache()
     value = head["gmm_TFLOP_s_whole_step"]
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": head["ms_per_step"], "ms_per_step_eager": head["ms_per_step_eager"],
+        "ms_per_step_eager_back_to_back": head["ms_per_step_eager_back_to_back"],
+        "settle": head["settle"],
         "launch": "HIP graph replay of the whole step (per-launch times from eager steps with HIP events)",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8 (e4m3fn operands, f32 accumulate)", "data": "synthetic (seeded; random-init weights)",
@@ -540,6 +669,8 @@ def main():
                         ("skewed_large_blockwise_static", lambda: secondary_forward(6, a.steps, a.warmup, True))):
             print(f"bench: secondary {key}", file=sys.stderr, flush=True)
             sec[key] = fn()
+        if int8 is not None:
+            sec["int8_gmm_expert_slice"] = int8
         res["secondary"] = sec
     if keep is not None:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
