@@ -53,6 +53,18 @@
 // and the waves split it into the same 64 x 64 wave tiles, so such a tail costs
 // half a plain tile per n-tile (the wide tile's wave grid is 2 x 4).
 //
+// Absorbing tiles (all-wide mode, [E, N, K] weights, at most 512 local
+// groups): a group of m rows gets ceil(m / 144) row blocks instead of
+// ceil(m / 128); block b starts at row 128 b + min(16 b, x), x = m - 128 *
+// blocks, so the first blocks carry up to 16 rows past their 128.  Those rows
+// are staged in a 2 KiB region after the stage's scale slot (each wave's
+// lanes 0..15 fill two of the 16 rows: every wave issues one more load per
+// step, so the wait counts stay uniform) and each wave multiplies them with
+// its own weight fragments, two more 16 x 16 blocks per step.  A group of
+// 257..288 rows then takes two row blocks instead of three: with routing
+// that fills experts to about 256 rows, the leftover rows of the fuller
+// experts no longer cost a third pass over their weights.
+//
 // Scheduling: persistent workgroups (as many per CU as the LDS allows).
 // Each derives the local group table (row and tile offsets) from
 // group_sizes in LDS -- empty groups
@@ -61,6 +73,8 @@
 // XCDs), and walks its part with m-tiles fastest inside a group so that
 // consecutive tiles reuse the expert's weight tile from that XCD's L2.
 // Rows [n, M) are zeroed after the tiles.
+#include <type_traits>
+
 #include "tile_common.hpp"
 
 #ifndef MOE_GMM_CFG
@@ -86,6 +100,11 @@
 // projection 222 -> 205 us, fused input projections 351 -> 347 us.
 #ifndef MOE_GMM_WIDE_ALL
 #define MOE_GMM_WIDE_ALL 1
+#endif
+// Absorbing tiles in the all-wide mode (see the header comment; [E, N, K]
+// weights, at most 512 local groups).
+#ifndef MOE_GMM_ABSORB
+#define MOE_GMM_ABSORB 1
 #endif
 #ifndef MOE_GMM_STREAM_BATCH
 #define MOE_GMM_STREAM_BATCH 1
@@ -163,8 +182,9 @@ __device__ __forceinline__ const uint8_t* slot_src0(bool wide, const uint8_t* __
                                                     const LaneOff offK, const LaneOff offN) {
   const int R = slot_row<NW, S>(wide, wave);
   if (slot_is_a<NW, S>(wide)) {
+    // the lane's row, clamped into the buffer (a no-op unless the tile reaches past row M - 1); always
+    // clamped rather than branching on `tail`, so the per-tile source set-up stays free of branches
     const uint32_t off = offK.pick(stage_bit(R));
-    if (!tail) return lhs + (row0 + R) * K + off;
     const int sub = lane >> 3;
     const int64_t r = min(row0 + R + sub, M - 1);
     return lhs + r * K + (off - static_cast<uint32_t>(sub * K));
@@ -254,6 +274,30 @@ __device__ __forceinline__ FragOff frag_off(int base, int lane) {
   return o;
 }
 
+// Fragment 0 (rows 0 .. 15) of a K-contiguous staged region at `region`, as
+// frag_i reads it, completed before returning.  One asm block, for the same
+// reason as lds_read_4x16f: the region is filled by direct loads whose
+// completion the caller has already waited for, and a plain read of it made
+// the compiler wait for every direct load still in flight (vmcnt(0) inside
+// the K loop, which drains the later stages' loads).
+__device__ __forceinline__ v8i frag0_waited(const uint8_t* region, const FragOff& o) {
+  typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)region));
+  const uint32_t a0 = base + static_cast<uint32_t>(o.lo[0]), a1 = base + static_cast<uint32_t>(o.hi[0]);
+  v4i32 lo, hi;
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo), "=&v"(hi)
+      : "v"(a0), "v"(a1)
+      : "memory");
+  v8i r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
 // Fragment i (rows base + 16 i ..) of a K-contiguous staged operand.
 __device__ __forceinline__ v8i frag_i(const uint8_t* stage, const FragOff& o, int i) {
   const int b = (i >> 1) & 1;
@@ -320,7 +364,8 @@ constexpr int loads_per_step() { return C::SLOTS + (KBLOCKS ? 1 : 0); }   // per
 // rows = the group table's row bound (max_rows).  Empty groups get zeros.
 // I8: int8 operands (v_mfma_i32_16x16x64_i8 pairs, int32 accumulation; with
 // blockwise scales each step's exact int32 product is folded in float32).
-template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH = false, bool I8 = false>
+// ABS: absorbing tiles in the all-wide mode (see the header comment).
+template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool BATCH = false, bool I8 = false, bool ABS = false>
 __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restrict__ lhs, const float* __restrict__ ls,
                                                        int ls_per_row, const uint8_t* __restrict__ rhs,
                                                        const float* __restrict__ rs, int Kb, int Nb,
@@ -329,9 +374,14 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
                                                        int32_t* __restrict__ err, int64_t max_rows = 0,
                                                        int wide_all = 0) {
   constexpr int BM = C::BM, BN = C::BN, NST = C::NST, WM = C::WM, WN = C::WN, MI = C::MI, JN = C::JN;
-  constexpr int STAGE = C::STAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
-  __shared__ GroupTable gt;
+  constexpr int XROWS = 16;                                   // ABS: rows a block may carry past BM/2
+  constexpr int X_OFF = C::SC_OFF + 1024;                     // ABS: their staging region in a stage
+  constexpr int STAGE = C::STAGE + (ABS ? XROWS * G_BK : 0);
+  constexpr int LDS_BYTES = ABS && NST * STAGE > C::LDS ? NST * STAGE : C::LDS;
+  static_assert(!ABS || (TRANS && !BATCH && BM == 256 && BN == 128), "absorbing tiles: forward, [E, N, K] weights");
+  static_assert(!ABS || (BM / 2 + XROWS) * (2 * BN + 8) * 2 <= LDS_BYTES, "absorbing tile's output staging");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+  __shared__ GroupTableN<ABS ? kAbsMaxLocal : kMaxLocal> gt;
   __shared__ float ls_tile[BM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: keeps staging addresses scalar
@@ -343,7 +393,28 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
   if constexpr (BATCH)   // tiles_off = the groups' padded row offsets in 128-row blocks
     build_groups(group_sizes, g0, El, max_rows, 1, G_BK, err, gt, reinterpret_cast<int*>(smem), false);
   else
-    build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), wide_all ? 2 : 1);
+    build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem),
+                 wide_all ? (ABS ? 3 : 2) : 1);
+  // ABS: absorbing row blocks only where they take fewer rounds of tiles over the workgroups of an
+  // XCD than the plain all-wide layout; otherwise they only make a few tiles heavier.  Every
+  // workgroup takes the same decision from the same group sizes.
+  int use_abs = 0;
+  if constexpr (ABS && !BATCH) {
+    int* plain = reinterpret_cast<int*>(smem);                // per-group plain tile counts, then their scan
+    int* plain_off = plain + kAbsMaxLocal + 1;
+    for (int g = threadIdx.x; g < El; g += blockDim.x)
+      plain[g] = group_tiles(gt.rows_off[g + 1] - gt.rows_off[g], BM, NT, 2);
+    __syncthreads();
+    wave0_scan(plain, plain_off, El);
+    __syncthreads();
+    const int per_xcd = max(static_cast<int>(gridDim.x) / 8, 1);
+    const int r_abs = ((gt.tiles_off[El] + 7) / 8 + per_xcd - 1) / per_xcd;
+    const int r_plain = ((plain_off[El] + 7) / 8 + per_xcd - 1) / per_xcd;
+    use_abs = __builtin_amdgcn_readfirstlane(r_abs < r_plain ? 1 : 0);
+    if (!use_abs)
+      for (int g = threadIdx.x; g <= El; g += blockDim.x) gt.tiles_off[g] = plain_off[g];
+    __syncthreads();
+  }
   const int total = BATCH ? El * MTb * NT : gt.tiles_off[El];
   const int n_rows = gt.rows_off[El];
   const int KT = static_cast<int>(K / G_BK);
@@ -364,16 +435,20 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
     const int full = m_g / BM, rem = m_g - full * BM;
     int nt, roff;                 // the tile's n-tile and its first row inside the group
+    int wrows = BM / 2;           // rows of a wide tile (ABS: up to BM/2 + XROWS)
     bool wide = false;
     if (BATCH) {
       nt = local / MTb;
       roff = (local - nt * MTb) * BM;
     } else if (wide_all) {        // every tile BM/2 rows x two n-tiles, m-tiles fastest within a pair
-      const int half = BM / 2, mtw = (m_g + half - 1) / half, npair = NT / 2;
+      const int half = BM / 2, npair = NT / 2;
+      const int mtw = use_abs ? (m_g + half + XROWS - 1) / (half + XROWS) : (m_g + half - 1) / half;
+      const int xr = use_abs ? max(m_g - half * mtw, 0) : 0;  // rows past half * blocks, spread over the first blocks
       if (local < npair * mtw) {
-        const int pr = local / mtw;
+        const int pr = local / mtw, mb = local - pr * mtw;
         nt = 2 * pr;
-        roff = (local - pr * mtw) * half;
+        roff = mb * half + (ABS ? min(XROWS * mb, xr) : 0);
+        if (ABS) wrows = (mb + 1 < mtw ? (mb + 1) * half + min(XROWS * (mb + 1), xr) : min(m_g, roff + half + XROWS)) - roff;
         wide = true;
       } else {
         nt = NT - 1;
@@ -402,7 +477,9 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       }
     }
     const int64_t row0 = BATCH ? static_cast<int64_t>(roff) : gt.rows_off[g] + static_cast<int64_t>(roff);
-    const int rows_here = BATCH ? BM : min(wide ? BM / 2 : BM, m_g - roff);
+    const int rows_here = BATCH ? BM : min(wide ? wrows : BM, m_g - roff);
+    // ABS: this tile carries rows past BM/2 (uniform: keeps its branches scalar)
+    const bool ab = ABS && __builtin_amdgcn_readfirstlane(wide && rows_here > BM / 2 ? 1 : 0) != 0;
     const int64_t col0 = static_cast<int64_t>(nt) * BN;
     // BATCH: the group's contraction columns, its K steps and its output matrix
     const int64_t cofs = BATCH ? static_cast<int64_t>(gt.tiles_off[g]) * G_BK : 0;
@@ -419,193 +496,286 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     const int rbase = (wave / gn) * WM, cbase = (wave % gn) * WN;
     const FragOff fa = frag_off(rbase, lane);
     const FragOff fb = frag_off(cbase, lane);
+    const FragOff fx = frag_off(0, lane);                  // ABS: the extra rows' staging region
     const float* rs_g = BATCH ? rs : rs + static_cast<int64_t>(g) * Kb * Nb;
     // blockwise scales ride the stages: lane l of wave w stages the scale of
     // tile column 64(w mod 4) + l (clamped to the tile; surplus lanes and the
     // upper four of eight waves repeat columns, writing the same values)
     const int w4 = wave & 3;
     const float* rs_lane = rs_g + static_cast<uint32_t>(col0 + min(w4 * 64 + lane, bn_t - 1)) / ncol_blk;
-
-    v4f acc[MI][JN];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // the previous tile's epilogue is done with the LDS (a bare barrier: its
-    // output stores need not have completed)
-    step_barrier();
-    // prologue: stages 0 .. NST-2 in flight
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s) {
-      if (s < KTt) {
-        const int64_t kb = static_cast<int64_t>(s) * G_BK;
-#define MOE_SLOT(S, stg, kbv) \
-  issue_slot<TRANS, NW, S>(wide, stg, lhs_t, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
-        MOE_SLOT(0, smem + s * STAGE, kb); MOE_SLOT(1, smem + s * STAGE, kb); MOE_SLOT(2, smem + s * STAGE, kb);
-        MOE_SLOT(3, smem + s * STAGE, kb); MOE_SLOT(4, smem + s * STAGE, kb); MOE_SLOT(5, smem + s * STAGE, kb);
-        if constexpr (C::SLOTS == 12) {
-          MOE_SLOT(6, smem + s * STAGE, kb); MOE_SLOT(7, smem + s * STAGE, kb); MOE_SLOT(8, smem + s * STAGE, kb);
-          MOE_SLOT(9, smem + s * STAGE, kb); MOE_SLOT(10, smem + s * STAGE, kb); MOE_SLOT(11, smem + s * STAGE, kb);
-        }
-        if (KBLOCKS)
-          __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(s / steps_per_block) * Nb,
-                                           (lds_void*)(smem + s * STAGE + C::SC_OFF + w4 * 256), 4, 0, 0);
-        if (s == 0) {   // the tile's lhs row scales ride its first stage (rows past the tile repeat its last)
-          const int r = min(w4 * 64 + lane, rows_here - 1);
-          __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? row0 + r : 0), (lds_void*)(ls_tile + w4 * 64), 4, 0, 0);
-        }
-      }
+    // ABS: lanes 0..15 of wave w stage extra rows 2w and 2w + 1 (rows BM/2 + 2w.. of the tile, clamped
+    // into the buffer; rows past the tile's are never stored), chunk c of a row at slot c ^ swz(row)
+    const uint8_t* xsrc = nullptr;
+    if constexpr (ABS) {
+      const int xrow = 2 * wave + ((lane >> 3) & 1);
+      xsrc = lhs + min(row0 + BM / 2 + xrow, M - 1) * K + 16 * ((lane & 7) ^ swz(xrow));
     }
+#define MOE_XLOAD(stg, kbv)                                                                                 \
+  do {                                                                                                      \
+    if (lane < 16) __builtin_amdgcn_global_load_lds(xsrc + (kbv), (lds_void*)((stg) + X_OFF + 2 * wave * G_BK), 16, \
+                                                    0, 0);                                                  \
+  } while (0)
 
-    for (int kt = 0; kt < KTt; ++kt) {
-      // this wave's loads of step kt have landed once at most the loads of the
-      // NST-2 later stages are outstanding (loads complete in order)
-      if (kt + NST - 1 <= KTt)
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * loads_per_step<C, KBLOCKS>()));
-      else
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      step_barrier();                         // everyone's have, and step kt-1's readers are done
-      const int ks = kt + NST - 1;            // the step whose loads are issued now
-      const bool more = ks < KTt;
-      const int64_t kb_next = static_cast<int64_t>(ks) * G_BK;
-      uint8_t* nxt = smem + (ks % NST) * STAGE;
-      const uint8_t* As = smem + (kt % NST) * STAGE;
-      const uint8_t* Bs = As + bm_t * G_BK;
-      float4 s_col[JN];    // scales of this lane's output columns 16j + 4(l/16) .. +3
-      if (KBLOCKS) {
-        const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + 4 * (lane >> 4);
-        static_assert(JN == 4, "four column groups per scale read");
-        lds_read_4x16f(sc, s_col);
-      }
-      v8i b[JN];
-#pragma unroll
-      for (int j = 0; j < JN; ++j) {
-        const int n0 = cbase + j * 16;
-        if (TRANS)
-          b[j] = frag_i(Bs, fb, j);
-        else
-          b[j] = frag_tr_swz(Bs + (n0 >> 7) * (128 * G_BK), n0 & 127, lane);
-      }
-      // MI rounds: an A fragment, this round's share of the loads of step ks,
-      // then the round's MFMAs -- so memory back-pressure on the loads never
-      // holds up a long run of MFMA issue
-      // (the step's SLOTS loads spread over the MI rounds, 1.5 per round)
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const v8i a = frag_i(As, fa, i);
-        if (more) {
-          if constexpr (C::SLOTS == 12) {
-            if (i == 0) { MOE_SLOT(0, nxt, kb_next); }
-            if (i == 1) { MOE_SLOT(1, nxt, kb_next); MOE_SLOT(2, nxt, kb_next); }
-            if (i == 2) { MOE_SLOT(3, nxt, kb_next); }
-            if (i == 3) { MOE_SLOT(4, nxt, kb_next); MOE_SLOT(5, nxt, kb_next); }
-            if (i == 4) { MOE_SLOT(6, nxt, kb_next); }
-            if (i == 5) { MOE_SLOT(7, nxt, kb_next); MOE_SLOT(8, nxt, kb_next); }
-            if (i == 6) { MOE_SLOT(9, nxt, kb_next); }
-            if (i == 7) { MOE_SLOT(10, nxt, kb_next); MOE_SLOT(11, nxt, kb_next); }
-          } else {
-            if (i == 0) { MOE_SLOT(0, nxt, kb_next); MOE_SLOT(1, nxt, kb_next); }
-            if (i == 1) { MOE_SLOT(2, nxt, kb_next); }
-            if (i == 2) { MOE_SLOT(3, nxt, kb_next); MOE_SLOT(4, nxt, kb_next); }
-            if (i == 3) { MOE_SLOT(5, nxt, kb_next); }
-          }
-          if (KBLOCKS && i == 0)
-            __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(ks / steps_per_block) * Nb,
-                                             (lds_void*)(nxt + C::SC_OFF + w4 * 256), 4, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < JN; ++j) {
-          if (KBLOCKS) {
-            v4f p;
-            if constexpr (I8)
-              p = __builtin_convertvector(mfma_i8x2(b[j], a, v4i32{0, 0, 0, 0}), v4f);   // exact: |p| < 2^24
-            else
-              p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
-            acc[i][j][0] = fmaf(s_col[j].x, p[0], acc[i][j][0]);
-            acc[i][j][1] = fmaf(s_col[j].y, p[1], acc[i][j][1]);
-            acc[i][j][2] = fmaf(s_col[j].z, p[2], acc[i][j][2]);
-            acc[i][j][3] = fmaf(s_col[j].w, p[3], acc[i][j][3]);
-          } else if constexpr (I8) {      // the int32 sums live in the accumulator's registers
-            acc[i][j] = __builtin_bit_cast(v4f, mfma_i8x2(b[j], a, __builtin_bit_cast(v4i32, acc[i][j])));
-          } else {
-            acc[i][j] = mfma_f8(b[j], a, acc[i][j]);
-          }
-        }
-      }
-    }
-
-    if constexpr (I8 && !KBLOCKS) {   // the int32 sums to float32 (rounded to nearest beyond 2^24)
+    // the tile body, compiled once for tiles that carry extra rows and once for
+    // the rest, so the ordinary tiles' K loop has no branches on the tile kind
+    auto tile_body = [=](auto ab_c) {
+      constexpr bool AB = decltype(ab_c)::value;
+      v4f acc[MI][JN];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < JN; ++j) acc[i][j] = __builtin_convertvector(__builtin_bit_cast(v4i32, acc[i][j]), v4f);
-    }
-    // ---- epilogue: out = ls[row] * (rs[col] *) acc
-    // The product is formed transposed per 16 x 16 block (D = B^T A^T), so
-    // lane l holds output row rbase + 16i + l%16 and the four consecutive
-    // columns cbase + 16j + 4(l/16) .. +3.
-    float4 s_out[JN];
+        for (int j = 0; j < JN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      v4f acc_x[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};   // ABS: the two extra blocks
+
+      // the previous tile's epilogue is done with the LDS (a bare barrier: its
+      // output stores need not have completed)
+      step_barrier();
+      // prologue: stages 0 .. NST-2 in flight
 #pragma unroll
-    for (int j = 0; j < JN; ++j) {
-      const int64_t c = col0 + cbase + j * 16 + 4 * (lane >> 4);
-      if (KBLOCKS)
-        s_out[j] = make_float4(1.f, 1.f, 1.f, 1.f);
-      else if (ncol_blk == 1)
-        s_out[j] = *reinterpret_cast<const float4*>(rs_g + c);
-      else
-        s_out[j] = make_float4(rs_g[static_cast<uint32_t>(c) / ncol_blk], rs_g[static_cast<uint32_t>(c + 1) / ncol_blk],
-                               rs_g[static_cast<uint32_t>(c + 2) / ncol_blk], rs_g[static_cast<uint32_t>(c + 3) / ncol_blk]);
-    }
-    // BATCH: a group without rows writes exact zeros (its row scales were never loaded)
-    const bool empty = BATCH && KTt == 0;
-    if (empty) {
-#pragma unroll
-      for (int j = 0; j < JN; ++j) s_out[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (OUT_BF16) {
-      const int ch_log = wide ? 5 : 4;          // log2 of the 16-byte chunks per output row
-      const int OS = bn_t + 8;
-      __syncthreads();                          // all waves are done with the operand stages
-      // [bm_t rows][bn_t cols] bf16 with rows padded to OS elements (OS/2 = 4 mod
-      // 64 dwords): each half-wave's 8-byte writes (16 rows x two 8-byte
-      // column steps) land on distinct bank pairs
-      uint16_t* st = reinterpret_cast<uint16_t*>(smem);
-      uint16_t* st_lane = st + (rbase + (lane & 15)) * OS + cbase + 4 * (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const float lsr = empty ? 0.f : ls_tile[rbase + i * 16 + (lane & 15)];
+      for (int s = 0; s < NST - 1; ++s) {
+        if (s < KTt) {
+          const int64_t kb = static_cast<int64_t>(s) * G_BK;
+  #define MOE_SLOT(S, stg, kbv) \
+    issue_slot<TRANS, NW, S>(wide, stg, lhs_t, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
+          MOE_SLOT(0, smem + s * STAGE, kb); MOE_SLOT(1, smem + s * STAGE, kb); MOE_SLOT(2, smem + s * STAGE, kb);
+          MOE_SLOT(3, smem + s * STAGE, kb); MOE_SLOT(4, smem + s * STAGE, kb); MOE_SLOT(5, smem + s * STAGE, kb);
+          if constexpr (C::SLOTS == 12) {
+            MOE_SLOT(6, smem + s * STAGE, kb); MOE_SLOT(7, smem + s * STAGE, kb); MOE_SLOT(8, smem + s * STAGE, kb);
+            MOE_SLOT(9, smem + s * STAGE, kb); MOE_SLOT(10, smem + s * STAGE, kb); MOE_SLOT(11, smem + s * STAGE, kb);
+          }
+          if (KBLOCKS)
+            __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(s / steps_per_block) * Nb,
+                                             (lds_void*)(smem + s * STAGE + C::SC_OFF + w4 * 256), 4, 0, 0);
+          if constexpr (AB) MOE_XLOAD(smem + s * STAGE, kb);
+          if (s == 0) {   // the tile's lhs row scales ride its first stage (rows past the tile repeat its last)
+            const int r = min(w4 * 64 + lane, rows_here - 1);
+            __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? row0 + r : 0), (lds_void*)(ls_tile + w4 * 64), 4, 0, 0);
+          }
+        }
+      }
+
+      for (int kt = 0; kt < KTt; ++kt) {
+        // this wave's loads of step kt have landed once at most the loads of the
+        // NST-2 later stages are outstanding (loads complete in order)
+        if (kt + NST - 1 <= KTt) {
+          if constexpr (AB)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * (loads_per_step<C, KBLOCKS>() + 1)));
+          else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((NST - 2) * loads_per_step<C, KBLOCKS>()));
+        } else {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        step_barrier();                         // everyone's have, and step kt-1's readers are done
+        const int ks = kt + NST - 1;            // the step whose loads are issued now
+        const bool more = ks < KTt;
+        const int64_t kb_next = static_cast<int64_t>(ks) * G_BK;
+        uint8_t* nxt = smem + (ks % NST) * STAGE;
+        const uint8_t* As = smem + (kt % NST) * STAGE;
+        const uint8_t* Bs = As + bm_t * G_BK;
+        float4 s_col[JN];    // scales of this lane's output columns 16j + 4(l/16) .. +3
+        if (KBLOCKS) {
+          const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + 4 * (lane >> 4);
+          static_assert(JN == 4, "four column groups per scale read");
+          lds_read_4x16f(sc, s_col);
+        }
+        v8i b[JN];
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
-          const uint32_t lo = pack_bf16x2(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y));
-          const uint32_t hi = pack_bf16x2(lsr * (acc[i][j][2] * s_out[j].z), lsr * (acc[i][j][3] * s_out[j].w));
-          *reinterpret_cast<uint2*>(st_lane + i * 16 * OS + j * 16) = make_uint2(lo, hi);
+          const int n0 = cbase + j * 16;
+          if (TRANS)
+            b[j] = frag_i(Bs, fb, j);
+          else
+            b[j] = frag_tr_swz(Bs + (n0 >> 7) * (128 * G_BK), n0 & 127, lane);
+        }
+        // MI rounds: an A fragment, this round's share of the loads of step ks,
+        // then the round's MFMAs -- so memory back-pressure on the loads never
+        // holds up a long run of MFMA issue
+        // (the step's SLOTS loads spread over the MI rounds, 1.5 per round)
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const v8i a = frag_i(As, fa, i);
+          if (more) {
+            if constexpr (C::SLOTS == 12) {
+              if (i == 0) { MOE_SLOT(0, nxt, kb_next); }
+              if (i == 1) { MOE_SLOT(1, nxt, kb_next); MOE_SLOT(2, nxt, kb_next); }
+              if (i == 2) { MOE_SLOT(3, nxt, kb_next); }
+              if (i == 3) { MOE_SLOT(4, nxt, kb_next); MOE_SLOT(5, nxt, kb_next); }
+              if (i == 4) { MOE_SLOT(6, nxt, kb_next); }
+              if (i == 5) { MOE_SLOT(7, nxt, kb_next); MOE_SLOT(8, nxt, kb_next); }
+              if (i == 6) { MOE_SLOT(9, nxt, kb_next); }
+              if (i == 7) { MOE_SLOT(10, nxt, kb_next); MOE_SLOT(11, nxt, kb_next); }
+            } else {
+              if (i == 0) { MOE_SLOT(0, nxt, kb_next); MOE_SLOT(1, nxt, kb_next); }
+              if (i == 1) { MOE_SLOT(2, nxt, kb_next); if constexpr (AB) MOE_XLOAD(nxt, kb_next); }
+              if (i == 2) { MOE_SLOT(3, nxt, kb_next); MOE_SLOT(4, nxt, kb_next); }
+              if (i == 3) { MOE_SLOT(5, nxt, kb_next); }
+            }
+            if (KBLOCKS && i == 0)
+              __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(ks / steps_per_block) * Nb,
+                                               (lds_void*)(nxt + C::SC_OFF + w4 * 256), 4, 0, 0);
+          }
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            if (KBLOCKS) {
+              v4f p;
+              if constexpr (I8)
+                p = __builtin_convertvector(mfma_i8x2(b[j], a, v4i32{0, 0, 0, 0}), v4f);   // exact: |p| < 2^24
+              else
+                p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
+              acc[i][j][0] = fmaf(s_col[j].x, p[0], acc[i][j][0]);
+              acc[i][j][1] = fmaf(s_col[j].y, p[1], acc[i][j][1]);
+              acc[i][j][2] = fmaf(s_col[j].z, p[2], acc[i][j][2]);
+              acc[i][j][3] = fmaf(s_col[j].w, p[3], acc[i][j][3]);
+            } else if constexpr (I8) {      // the int32 sums live in the accumulator's registers
+              acc[i][j] = __builtin_bit_cast(v4f, mfma_i8x2(b[j], a, __builtin_bit_cast(v4i32, acc[i][j])));
+            } else {
+              acc[i][j] = mfma_f8(b[j], a, acc[i][j]);
+            }
+          }
+        }
+        if constexpr (AB) {
+          {   // the extra rows: this wave's blocks at tile rows BM/2 .. +15, columns cbase + 32 (wave / 4) ..
+            const v8i ax = frag0_waited(As + X_OFF, fx);
+            auto xblock = [&](v4f& c, const v8i& bj, const float4& sj) {
+              if (KBLOCKS) {
+                v4f p;
+                if constexpr (I8)
+                  p = __builtin_convertvector(mfma_i8x2(bj, ax, v4i32{0, 0, 0, 0}), v4f);
+                else
+                  p = mfma_f8(bj, ax, v4f{0.f, 0.f, 0.f, 0.f});
+                c[0] = fmaf(sj.x, p[0], c[0]);
+                c[1] = fmaf(sj.y, p[1], c[1]);
+                c[2] = fmaf(sj.z, p[2], c[2]);
+                c[3] = fmaf(sj.w, p[3], c[3]);
+              } else if constexpr (I8) {
+                c = __builtin_bit_cast(v4f, mfma_i8x2(bj, ax, __builtin_bit_cast(v4i32, c)));
+              } else {
+                c = mfma_f8(bj, ax, c);
+              }
+            };
+            if (wave < 4) {
+              xblock(acc_x[0], b[0], s_col[0]);
+              xblock(acc_x[1], b[1], s_col[1]);
+            } else {
+              xblock(acc_x[0], b[2], s_col[2]);
+              xblock(acc_x[1], b[3], s_col[3]);
+            }
+          }
         }
       }
-      __syncthreads();
-      uint16_t* o = static_cast<uint16_t*>(out_t);
+  #undef MOE_XLOAD
+
+      if constexpr (I8 && !KBLOCKS) {   // the int32 sums to float32 (rounded to nearest beyond 2^24)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < JN; ++j) acc[i][j] = __builtin_convertvector(__builtin_bit_cast(v4i32, acc[i][j]), v4f);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc_x[q] = __builtin_convertvector(__builtin_bit_cast(v4i32, acc_x[q]), v4f);
+      }
+      // ---- epilogue: out = ls[row] * (rs[col] *) acc
+      // The product is formed transposed per 16 x 16 block (D = B^T A^T), so
+      // lane l holds output row rbase + 16i + l%16 and the four consecutive
+      // columns cbase + 16j + 4(l/16) .. +3.
+      float4 s_out[JN];
+#pragma unroll
+      for (int j = 0; j < JN; ++j) {
+        const int64_t c = col0 + cbase + j * 16 + 4 * (lane >> 4);
+        if (KBLOCKS)
+          s_out[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+        else if (ncol_blk == 1)
+          s_out[j] = *reinterpret_cast<const float4*>(rs_g + c);
+        else
+          s_out[j] = make_float4(rs_g[static_cast<uint32_t>(c) / ncol_blk], rs_g[static_cast<uint32_t>(c + 1) / ncol_blk],
+                                 rs_g[static_cast<uint32_t>(c + 2) / ncol_blk], rs_g[static_cast<uint32_t>(c + 3) / ncol_blk]);
+      }
+      // BATCH: a group without rows writes exact zeros (its row scales were never loaded)
+      const bool empty = BATCH && KTt == 0;
+      if (empty) {
+#pragma unroll
+        for (int j = 0; j < JN; ++j) s_out[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (OUT_BF16) {
+        const int ch_log = wide ? 5 : 4;          // log2 of the 16-byte chunks per output row
+        const int OS = bn_t + 8;
+        __syncthreads();                          // all waves are done with the operand stages
+        // [bm_t rows][bn_t cols] bf16 with rows padded to OS elements (OS/2 = 4 mod
+        // 64 dwords): each half-wave's 8-byte writes (16 rows x two 8-byte
+        // column steps) land on distinct bank pairs
+        uint16_t* st = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* st_lane = st + (rbase + (lane & 15)) * OS + cbase + 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const float lsr = empty ? 0.f : ls_tile[rbase + i * 16 + (lane & 15)];
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            const uint32_t lo = pack_bf16x2(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y));
+            const uint32_t hi = pack_bf16x2(lsr * (acc[i][j][2] * s_out[j].z), lsr * (acc[i][j][3] * s_out[j].w));
+            *reinterpret_cast<uint2*>(st_lane + i * 16 * OS + j * 16) = make_uint2(lo, hi);
+          }
+        }
+        if constexpr (AB) {         // the extra rows BM/2 .. +15 (a wide tile: OS = 2 BN + 8)
+          const float lsr = ls_tile[BM / 2 + (lane & 15)];
+          const int jx = wave < 4 ? 0 : 2;
+          uint16_t* xl = st + (BM / 2 + (lane & 15)) * OS + cbase + 4 * (lane >> 4);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float4 so = jx == 0 ? s_out[q] : s_out[2 + q];
+            const uint32_t lo = pack_bf16x2(lsr * (acc_x[q][0] * so.x), lsr * (acc_x[q][1] * so.y));
+            const uint32_t hi = pack_bf16x2(lsr * (acc_x[q][2] * so.z), lsr * (acc_x[q][3] * so.w));
+            *reinterpret_cast<uint2*>(xl + (jx + q) * 16) = make_uint2(lo, hi);
+          }
+        }
+        __syncthreads();
+        uint16_t* o = static_cast<uint16_t*>(out_t);
+        // chunks: a plain tile BM x BN/8, a wide one BM/2 x 2BN/8 (ABS: plus XROWS rows)
+        constexpr int OUT_IT = (BM * (BN / 8) + (ABS ? XROWS * (2 * BN / 8) : 0) + G_THREADS - 1) / G_THREADS;
 #pragma unroll 4
-      for (int it = 0; it < BM * (BN / 8) / G_THREADS; ++it) {     // same chunk count for both shapes
-        const int id = it * G_THREADS + tid;
-        const int r = id >> ch_log, c = id & ((1 << ch_log) - 1);
-        if (r < rows_here) {
-          const uint4 v = *reinterpret_cast<const uint4*>(st + r * OS + c * 8);
-          *reinterpret_cast<uint4*>(o + (row0 + r) * N + col0 + c * 8) = v;
+        for (int it = 0; it < OUT_IT; ++it) {
+          const int id = it * G_THREADS + tid;
+          const int r = id >> ch_log, c = id & ((1 << ch_log) - 1);
+          if (r < rows_here) {
+            const uint4 v = *reinterpret_cast<const uint4*>(st + r * OS + c * 8);
+            *reinterpret_cast<uint4*>(o + (row0 + r) * N + col0 + c * 8) = v;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int r = rbase + i * 16 + (lane & 15);
+          if (r >= rows_here) continue;
+          const float lsr = empty ? 0.f : ls_tile[r];
+          float* o = static_cast<float*>(out_t) + (row0 + r) * N + col0 + cbase + 4 * (lane >> 4);
+#pragma unroll
+          for (int j = 0; j < JN; ++j)
+            *reinterpret_cast<float4*>(o + j * 16) =
+                make_float4(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y),
+                            lsr * (acc[i][j][2] * s_out[j].z), lsr * (acc[i][j][3] * s_out[j].w));
+        }
+        if constexpr (AB) {
+          const int r = BM / 2 + (lane & 15);
+          if (r < rows_here) {
+            const float lsr = ls_tile[r];
+            const int jx = wave < 4 ? 0 : 2;
+            float* o = static_cast<float*>(out_t) + (row0 + r) * N + col0 + cbase + 4 * (lane >> 4);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const float4 so = jx == 0 ? s_out[q] : s_out[2 + q];
+              *reinterpret_cast<float4*>(o + (jx + q) * 16) =
+                  make_float4(lsr * (acc_x[q][0] * so.x), lsr * (acc_x[q][1] * so.y), lsr * (acc_x[q][2] * so.z),
+                              lsr * (acc_x[q][3] * so.w));
+            }
+          }
         }
       }
+    };
+    if constexpr (ABS) {
+      if (ab)
+        tile_body(std::integral_constant<bool, true>{});
+      else
+        tile_body(std::integral_constant<bool, false>{});
     } else {
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r = rbase + i * 16 + (lane & 15);
-        if (r >= rows_here) continue;
-        const float lsr = empty ? 0.f : ls_tile[r];
-        float* o = static_cast<float*>(out_t) + (row0 + r) * N + col0 + cbase + 4 * (lane >> 4);
-#pragma unroll
-        for (int j = 0; j < JN; ++j)
-          *reinterpret_cast<float4*>(o + j * 16) =
-              make_float4(lsr * (acc[i][j][0] * s_out[j].x), lsr * (acc[i][j][1] * s_out[j].y),
-                          lsr * (acc[i][j][2] * s_out[j].z), lsr * (acc[i][j][3] * s_out[j].w));
-      }
+      tile_body(std::integral_constant<bool, false>{});
     }
   }
 #undef MOE_SLOT
@@ -1425,6 +1595,13 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
       gmm_stream_kernel<C, TRANS, KBLOCKS, OUT_BF16, false>
           <<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N,
                                                               out, err, 0);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (TRANS && MOE_GMM_WIDE_ALL != 0 && MOE_GMM_ABSORB != 0) {
+    if (El <= kAbsMaxLocal) {
+      gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16, false, I8, true><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
+          lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err, 0, 1);
       return hipGetLastError();
     }
   }

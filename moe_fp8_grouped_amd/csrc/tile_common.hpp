@@ -20,6 +20,7 @@ constexpr int LDS_STRIDE = BK + 16;         // bytes per staged row
 constexpr int TILE_BYTES = 128 * LDS_STRIDE;
 constexpr int kHdr = 256;                   // workspace header (error word)
 constexpr int kMaxLocal = 1024;
+constexpr int kAbsMaxLocal = 512;           // group table of the kernels with absorbing tiles (LDS budget)
 
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -124,9 +125,13 @@ __device__ bool wave0_scan_sat(const int* v, int* out, int n, int64_t cap) {
 // n-tile keeps a plain tail tile).  2 (all wide): every tile is bm/2 rows x
 // two n-tiles, ceil(m / (bm/2)) of them per n-tile pair (an odd last n-tile
 // keeps plain tiles).
+// 3 (all wide, absorbing): as 2, but ceil(m / (bm/2 + 16)) row blocks per
+// n-tile pair, each of at most bm/2 + 16 rows (the first blocks take the rows
+// past bm/2 per block, up to 16 each).
 __device__ __forceinline__ int group_tiles(int m, int bm, int nt, int tail_mode) {
   if (nt <= 0) return 1;
   if (tail_mode == 2) return ((m + bm / 2 - 1) / (bm / 2)) * (nt / 2) + (nt & 1) * ((m + bm - 1) / bm);
+  if (tail_mode == 3) return ((m + bm / 2 + 15) / (bm / 2 + 16)) * (nt / 2) + (nt & 1) * ((m + bm - 1) / bm);
   const int full = m / bm, rem = m - full * bm;
   if (tail_mode == 0 || rem == 0 || rem > bm / 2) return (full + (rem ? 1 : 0)) * nt;
   return (nt / 2) * (2 * full + 1) + (nt & 1) * (full + 1);

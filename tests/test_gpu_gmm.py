@@ -226,6 +226,29 @@ def test_gmm_256_tiles_ragged(sizes, N, nb, static):
     _check_gmm_full(lhs, ls, mode, w, rs, gs, E, 0, E, 1, f"256 tiles {sizes} N={N} {nb}", hw=True)
 
 
+@pytest.mark.parametrize("N,nb,Kb", [(512, "block", 2), (384, "channel", 1), (256, "block", 3)])
+def test_gmm_absorbing_row_blocks(N, nb, Kb):
+    """Group sizes at the boundaries of the absorbing row blocks (a group of
+    m rows takes ceil(m / 144) blocks of 128 rows plus up to 16 each, so
+    wide tiles of 129..144 rows): every element of the float32 and bf16
+    outputs against the oracle, with an even and an odd count of 128-column
+    blocks (the odd one's last column takes plain tiles), blockwise and
+    per-channel scales, and rows past the groups."""
+    sizes = [0, 1, 16, 17, 128, 129, 140, 144, 145, 256, 257, 272, 285, 288, 289, 300, 431, 432, 433]
+    rng = np.random.default_rng(N + Kb)
+    E = len(sizes)
+    gs = np.array(sizes, np.int32)
+    n = int(gs.sum())
+    M = n + 37
+    K = 128 * Kb if Kb > 1 else 512
+    lhs = rng.integers(0, 0x70, (M, K)).astype(np.uint8)
+    w = rng.integers(0, 0x70, (E, K, N)).astype(np.uint8)
+    nbv = N // 128 if nb == "block" else N
+    rs = rng.uniform(0.001, 0.1, (E, Kb, 1, nbv)).astype(np.float32)
+    ls = rng.uniform(0.01, 1, M).astype(np.float32)
+    _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, 0, E, 1, f"absorbing N={N} {nb} Kb={Kb}", hw=True)
+
+
 def test_gmm_256_tiles_local_slice():
     rng = np.random.default_rng(21)
     E, g0, El = 10, 3, 4

@@ -140,6 +140,8 @@ def _codes(rng, shape):
     ([64, 0, 200, 7], 144, 80, 1, 1),                 # sizes that take the 64 x 64 edge kernel
     ([64, 0, 200, 7], 144, 80, 1, 0),
     ([3, 90, 0, 41], 16, 48, 1, 1),
+    ([0, 285, 16, 140, 433, 257], 512, 512, 4, 1),    # row blocks of up to 144 rows (absorbing tiles)
+    ([0, 285, 16, 140, 433, 257], 512, 384, 1, 1),
 ])
 def test_gmm_i8_integer_sums_exact(sizes, K, N, Kb, tr):
     """Unit scales, float32 output: every element must equal the exact

@@ -16,12 +16,19 @@ import moe_fp8_grouped_amd as m
 I32 = np.iinfo(np.int32)
 
 
+XROWS = 16     # rows an absorbing row block may carry past bm/2
+
+
 def group_tiles(mr, bm, nt, mode):
-    """mode 0 plain tiles, 1 wide tails, 2 every tile wide (bm/2 rows x two n-tiles)."""
+    """mode 0 plain tiles, 1 wide tails, 2 every tile wide (bm/2 rows x two
+    n-tiles), 3 every tile wide with absorbing row blocks (up to bm/2 + 16
+    rows each)."""
     if nt <= 0:
         return 1
     if mode == 2:
         return -(-mr // (bm // 2)) * (nt // 2) + (nt & 1) * -(-mr // bm)
+    if mode == 3:
+        return -(-mr // (bm // 2 + XROWS)) * (nt // 2) + (nt & 1) * -(-mr // bm)
     full, rem = mr // bm, mr % bm
     if mode == 0 or rem == 0 or rem > bm // 2:
         return (full + (1 if rem else 0)) * nt
@@ -62,6 +69,7 @@ CASES = [
 
 @pytest.mark.parametrize("sizes", CASES)
 @pytest.mark.parametrize("max_rows,nt,bm,wide", [(1000, 2, 256, 1), (8192, 32, 256, 1), (8192, 33, 256, 2),
+                                                 (8192, 33, 256, 3), (1000, 4, 256, 3),
                                                  (40960, 1, 128, 0), (2 ** 31 - 2, 16, 256, 0)])
 def test_table_stays_inside_the_buffer(sizes, max_rows, nt, bm, wide):
     if (max_rows // 128 + len(sizes) + 1) * nt > I32.max:
@@ -77,25 +85,58 @@ def test_table_stays_inside_the_buffer(sizes, max_rows, nt, bm, wide):
         r0, r1 = int(rows_off[g]), int(rows_off[g + 1])
         assert 0 <= r0 <= r1 <= max_rows
         assert tiles_off[g + 1] - tiles_off[g] == group_tiles(r1 - r0, bm, nt, wide)
-    if wide == 2 and len(sizes) <= 64:
+    if wide >= 2 and len(sizes) <= 64:
         # the all-wide decode: tile -> (n-tile, first row, rows) covers every (row, n-tile) of each group once
         for g in range(len(sizes)):
             m_g = int(rows_off[g + 1] - rows_off[g])
             if m_g > 4096:
                 continue
-            cover = np.zeros((max(m_g, 1), nt), np.int64)
-            half, mtw, npair = bm // 2, -(-m_g // (bm // 2)), nt // 2
-            for local in range(int(tiles_off[g + 1] - tiles_off[g])):
-                if local < npair * mtw:
-                    pr = local // mtw
-                    roff, rows, nts = (local - pr * mtw) * half, half, (2 * pr, 2 * pr + 1)
-                else:
-                    roff, rows, nts = (local - npair * mtw) * bm, bm, (nt - 1,)
-                rows = min(rows, m_g - roff)
-                assert rows > 0 and roff + rows <= m_g
-                for j in nts:
-                    cover[roff:roff + rows, j] += 1
-            assert m_g == 0 or (cover == 1).all()
+            check_wide_cover(m_g, nt, bm, wide, int(tiles_off[g + 1] - tiles_off[g]))
+
+
+def wide_decode(local, m_g, nt, bm, mode):
+    """(first row, rows, n-tiles) of tile `local` of a group, as the kernel decodes it."""
+    half, npair = bm // 2, nt // 2
+    mtw = -(-m_g // (half + XROWS)) if mode == 3 else -(-m_g // half)
+    xr = max(m_g - half * mtw, 0) if mode == 3 else 0
+    if local < npair * mtw:
+        pr, mb = local // mtw, local % mtw
+        roff = mb * half + min(XROWS * mb, xr)
+        if mode == 3:
+            nxt = (mb + 1) * half + min(XROWS * (mb + 1), xr) if mb + 1 < mtw else m_g
+            rows = nxt - roff
+        else:
+            rows = min(half, m_g - roff)
+        return roff, rows, (2 * pr, 2 * pr + 1)
+    roff = (local - npair * mtw) * bm
+    return roff, min(bm, m_g - roff), (nt - 1,)
+
+
+def check_wide_cover(m_g, nt, bm, mode, ntiles):
+    cover = np.zeros((max(m_g, 1), nt), np.int64)
+    for local in range(ntiles):
+        roff, rows, nts = wide_decode(local, m_g, nt, bm, mode)
+        assert rows > 0 and roff + rows <= m_g
+        limit = bm // 2 + (XROWS if mode == 3 else 0) if len(nts) == 2 else bm
+        assert rows <= limit, (m_g, local, rows)
+        for j in nts:
+            cover[roff:roff + rows, j] += 1
+    assert m_g == 0 or (cover == 1).all()
+
+
+@pytest.mark.parametrize("nt", [2, 3, 32, 56])
+def test_absorbing_blocks_cover_every_row_once(nt):
+    """Every group size up to 1200 rows: the absorbing decode covers each
+    (row, n-tile) once, no wide tile exceeds 144 rows, and it never needs more
+    tiles than the plain all-wide decode (fewer when up to 16 rows per block
+    spill past a multiple of 128)."""
+    for m_g in range(0, 1201):
+        t3, t2 = group_tiles(m_g, 256, nt, 3), group_tiles(m_g, 256, nt, 2)
+        assert t3 <= t2
+        check_wide_cover(m_g, nt, 256, 3, t3)
+    # the expert-slice case: 257..288 rows take two row blocks, not three
+    assert group_tiles(285, 256, 32, 3) == 2 * 16 and group_tiles(285, 256, 32, 2) == 3 * 16
+    assert group_tiles(289, 256, 32, 3) == 3 * 16
 
 
 def test_a_32_bit_running_sum_would_leave_the_buffer():
@@ -121,3 +162,31 @@ def test_gmm_rejects_tile_tables_past_int32(lib):
     M, N, K = 2 ** 31 - 2, 128 * 1024, 128
     st = lib.moe_gmm_fp8(one, one, 0, one, one, 1, N, 1, one, 8, 0, 8, M, K, N, 0, one, one, 256, None)
     assert st == m.MOE_ERR_SHAPE
+
+
+def absorb_decision(sizes, nt, workgroups=256, bm=256):
+    """The kernel's per-launch choice: absorbing row blocks only when they
+    take fewer rounds of tiles over an XCD's workgroups than plain wide tiles."""
+    per_xcd = max(workgroups // 8, 1)
+    rounds = lambda total: (-(-total // 8) + per_xcd - 1) // per_xcd
+    t3 = sum(group_tiles(int(m), bm, nt, 3) for m in sizes)
+    t2 = sum(group_tiles(int(m), bm, nt, 2) for m in sizes)
+    return rounds(t3) < rounds(t2), t2, t3
+
+
+def test_absorbing_decision_on_the_workload_routings():
+    """The expert slice's routing (experts filled to ~250 rows, 11 of 32 past
+    256) takes absorbing blocks on both of its launches (1200 -> 1024 and
+    2100 -> 1792 tiles: one round and two rounds fewer); the skewed Zipf
+    routing of the large up-projection keeps plain tiles (560 vs 544 tiles,
+    three rounds either way)."""
+    from workloads import CONFIGS, generate
+    c4, c6 = CONFIGS[4], CONFIGS[6]
+    ids4 = generate(c4, with_weights=False)["ids"]
+    loc = np.bincount(ids4.ravel(), minlength=c4.E)[c4.group_offset:c4.group_offset + c4.E_loc]
+    for n_cols, want in ((2 * c4.I, (1200, 1024)), (c4.H, (2100, 1792))):
+        ok, t2, t3 = absorb_decision(loc, n_cols // 128)
+        assert ok and (t2, t3) == want
+    sizes6 = np.bincount(generate(c6, with_weights=False)["ids"].ravel(), minlength=c6.E)
+    ok, t2, t3 = absorb_decision(sizes6, c6.I // 128)
+    assert not ok and (t2, t3) == (560, 544)
