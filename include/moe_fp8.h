@@ -320,8 +320,20 @@ int moe_quantize_sort_by_expert(const void* x, int64_t T, int64_t H, int scale_m
  *   group_sizes [E] int32 device; E, group_offset, num_local_experts as in
  *            moe_sort_by_expert.
  *   out      [M, N], out_dtype MOE_BF16 (default) or MOE_F32.
- *   ws       workspace of moe_workspace_bytes(MOE_OP_GMM, M, K, N, E) (holds
- *            the error word).
+ *   ws       workspace of moe_workspace_bytes(MOE_OP_GMM, M, K, N, E): the
+ *            error word, one counter per tile of a split last round, and one
+ *            float32 slot of 144 x 256 per workgroup (about 36 MiB on a
+ *            256-CU GPU).  Zeroed once before its first use; the counters
+ *            return to zero at the end of every call.  With it, when an XCD's
+ *            share of tiles leaves a last round that fills few of its
+ *            workgroups, each of those tiles is split along K over several
+ *            workgroups and their float32 sums are added in a fixed order
+ *            (int8 with one K block: int32 sums, added exactly).  Any smaller
+ *            workspace of at least 256 bytes also works, without the split:
+ *            the fp8 results may then differ in the last bits (another
+ *            association of the same float32 sums); the same workspace size
+ *            gives the same bits on every call.  Calls that share a workspace
+ *            must not overlap (same stream, or ordered by events).
  * K and N multiples of 16 (MOE_ERR_SHAPE otherwise); multiples of 128 take
  * the tiled matrix-core kernels, other sizes a plainer edge kernel with the
  * same results.  M >= 0, 1 <= E <= 1024, num_local_experts <= 1024.

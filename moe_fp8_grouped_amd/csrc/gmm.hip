@@ -65,6 +65,18 @@
 // that fills experts to about 256 rows, the leftover rows of the fuller
 // experts no longer cost a third pass over their weights.
 //
+// Split last round: when an XCD's share of tiles leaves a last round that
+// occupies few of its workgroups, each of those tiles is split along K into
+// up to workgroups / tiles parts (at least four K steps each).  A part writes
+// its raw float32 sums to its workgroup's slot in the workspace with
+// device-coherent stores, waits for them to complete and counts itself in
+// with an integer atomic; the part that finishes last reads the slots back
+// with device-coherent loads, adds them up in part order and writes the
+// output -- no waiting, the same sums in the same order on every run, and no
+// device-scope fence (on this chip one writes back and invalidates a whole
+// L2, which cost more than the split saves).  The counters return to zero
+// after each use.
+//
 // Scheduling: persistent workgroups (as many per CU as the LDS allows).
 // Each derives the local group table (row and tile offsets) from
 // group_sizes in LDS -- empty groups
@@ -341,6 +353,63 @@ __device__ __forceinline__ void step_barrier() { asm volatile("s_waitcnt lgkmcnt
 // (BM/2 x 2BN) over (BM/2WM) x (2BN/WN); both use WM x WN wave tiles (NW = 4:
 // 128 x 64, NW = 8: 64 x 64).  A stage holds the A rows, the B rows and 1 KiB
 // for the step's blockwise weight scales (one float per tile column).
+// The last part of a split tile: the parts' raw sums, read back from their
+// slots with device-coherent loads, added up in part order, then scaled like
+// the ordinary epilogue (out = ls[row] * (rs[col] *) sum).  Kept out of line so
+// that its registers (every part's loads of a thread's share go out together:
+// one memory round trip per part) do not count against the tile loop's.
+// Slot of part p: xcd + 8 * (ul + p * lft) (workgroup ul + p * lft of the XCD).
+// INT_SUMS (int8 codes, one scale per column): the slots hold int32 sums,
+// added as integers and converted to float32 once, as without the split.
+template <int THREADS, int EPT, bool KBLOCKS, bool OUT_BF16, bool INT_SUMS>
+__device__ __attribute__((noinline)) void split_fixup(const float* __restrict__ part, int xcd, int ul, int lft,
+                                                      int parts, int rows, int cols, const float* ls_tile,
+                                                      const float* __restrict__ rs_g, uint32_t ncol_blk,
+                                                      int64_t row0, int64_t col0, int64_t N, void* out_t) {
+  const int tid = threadIdx.x;
+  const int q4 = cols / 4, nel = rows * q4;
+  v4f tot[EPT];
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) tot[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int pp = 0; pp < parts; ++pp) {
+    const __amdgpu_buffer_rsrc_t sp = slot_rsrc(const_cast<float*>(part) +
+                                                static_cast<int64_t>(xcd + 8 * (ul + pp * lft)) * kSplitSlot);
+    v4f v[EPT];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = min(tid + u * THREADS, nel - 1);
+      v[u] = slot_load(sp, 4 * ((e / q4) * cols + 4 * (e % q4)));
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u)
+      tot[u] = INT_SUMS ? __builtin_bit_cast(v4f, __builtin_bit_cast(v4i32, tot[u]) + __builtin_bit_cast(v4i32, v[u]))
+                        : tot[u] + v[u];
+  }
+  if (INT_SUMS) {
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) tot[u] = __builtin_convertvector(__builtin_bit_cast(v4i32, tot[u]), v4f);
+  }
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = tid + u * THREADS;
+    if (e >= nel) break;
+    const int r = e / q4, c = 4 * (e % q4);
+    const int64_t gc = col0 + c;
+    float4 sc = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (!KBLOCKS)
+      sc = make_float4(rs_g[static_cast<uint32_t>(gc) / ncol_blk], rs_g[static_cast<uint32_t>(gc + 1) / ncol_blk],
+                       rs_g[static_cast<uint32_t>(gc + 2) / ncol_blk], rs_g[static_cast<uint32_t>(gc + 3) / ncol_blk]);
+    const float lsr = ls_tile[r];
+    const float o0 = lsr * (tot[u][0] * sc.x), o1 = lsr * (tot[u][1] * sc.y), o2 = lsr * (tot[u][2] * sc.z),
+                o3 = lsr * (tot[u][3] * sc.w);
+    if (OUT_BF16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out_t) + (row0 + r) * N + gc) =
+          make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(out_t) + (row0 + r) * N + gc) = make_float4(o0, o1, o2, o3);
+  }
+}
+
 template <int BM_, int BN_, int NST_, int NW_ = 4>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, NST = NST_, NW = NW_, THREADS = 64 * NW;
@@ -372,7 +441,8 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
                                                        const int32_t* __restrict__ group_sizes, int g0, int El,
                                                        int64_t M, int64_t K, int64_t N, void* __restrict__ out,
                                                        int32_t* __restrict__ err, int64_t max_rows = 0,
-                                                       int wide_all = 0) {
+                                                       int wide_all = 0, float* __restrict__ part = nullptr,
+                                                       int32_t* __restrict__ cnt = nullptr, int nslots = 0) {
   constexpr int BM = C::BM, BN = C::BN, NST = C::NST, WM = C::WM, WN = C::WN, MI = C::MI, JN = C::JN;
   constexpr int XROWS = 16;                                   // ABS: rows a block may carry past BM/2
   constexpr int X_OFF = C::SC_OFF + 1024;                     // ABS: their staging region in a stage
@@ -383,6 +453,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   __shared__ GroupTableN<ABS ? kAbsMaxLocal : kMaxLocal> gt;
   __shared__ float ls_tile[BM];
+  __shared__ int split_last;                                  // ABS: this part finished its split tile last
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: keeps staging addresses scalar
   constexpr int NW = C::NW, G_THREADS = C::THREADS;
@@ -424,8 +495,36 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
   xcd_share(total, first, last, step);
   const LaneOff offK = stage_lane_off(lane, K);
   const LaneOff offN = stage_lane_off(lane, N);
+  // ABS: the last, partial round of this XCD's tiles may be split along K: its `lft` tiles go to
+  // `split_s` workgroups each (part p of tile l: workgroup l + p * lft on the XCD)
+  const int xj = static_cast<int>(blockIdx.x) / 8;            // this workgroup's index on its XCD
+  int n_full, split_s = 1, lft = 0, lbase = 0;
+  {
+    const int x = static_cast<int>(blockIdx.x) % 8;
+    const int lo = static_cast<int>((static_cast<int64_t>(total) * x) / 8);
+    const int hi = static_cast<int>((static_cast<int64_t>(total) * (x + 1)) / 8);
+    const int rounds = (hi - lo) / step;
+    lft = hi - lo - rounds * step;
+    lbase = lo + rounds * step;
+    if constexpr (ABS) {
+      if (part != nullptr && lft > 0 && static_cast<int>(gridDim.x) <= nslots && lft <= kSplitPerXcd)
+        split_s = max(min(step / lft, KT / kSplitMinSteps), 1);
+    }
+    n_full = split_s >= 2 ? rounds : (first < last ? (last - first + step - 1) / step : 0);
+  }
+  const int ul = lft > 0 ? xj % lft : 0, up = lft > 0 ? xj / lft : 0;   // this workgroup's leftover tile, part
+  const int n_items = n_full + (split_s >= 2 && xj < lft * split_s ? 1 : 0);
 
-  for (int t = first; t < last; t += step) {
+  // the tile loop, compiled once with a split part and once without, so the
+  // workgroups of an XCD without a split round run a loop that holds none of
+  // the split's state
+  auto tile_loop = [&](auto split_c) {
+  constexpr bool SPLIT = decltype(split_c)::value;
+  for (int item = 0; item < n_items; ++item) {
+    const bool psplit = SPLIT && item == n_full;               // a part of a split tile
+    const int t = psplit ? lbase + ul : first + item * step;
+    const int kbeg = psplit ? (up * KT) / split_s : 0;
+    const int kend = psplit ? ((up + 1) * KT) / split_s : KT;
     // ---- decode tile t of the group table (tiles of a group: n-tile major,
     // m-tiles fastest; a short remainder of at most BM/2 rows is covered by
     // wide tiles of two n-tiles each, placed after the two n-tiles' full
@@ -483,7 +582,8 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     const int64_t col0 = static_cast<int64_t>(nt) * BN;
     // BATCH: the group's contraction columns, its K steps and its output matrix
     const int64_t cofs = BATCH ? static_cast<int64_t>(gt.tiles_off[g]) * G_BK : 0;
-    const int KTt = BATCH ? (m_g + G_BK - 1) / G_BK : KT;
+    const int KTt = BATCH ? (m_g + G_BK - 1) / G_BK : kend - kbeg;
+    const int kofs = BATCH ? 0 : kbeg;                          // the tile's first K step (split parts)
     const uint8_t* lhs_t = lhs + cofs;
     const uint8_t* wg = BATCH ? rhs + cofs : rhs + static_cast<int64_t>(g) * K * N;
     void* out_t = BATCH ? static_cast<void*>(static_cast<uint8_t*>(out) +
@@ -534,7 +634,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
 #pragma unroll
       for (int s = 0; s < NST - 1; ++s) {
         if (s < KTt) {
-          const int64_t kb = static_cast<int64_t>(s) * G_BK;
+          const int64_t kb = static_cast<int64_t>(kofs + s) * G_BK;
   #define MOE_SLOT(S, stg, kbv) \
     issue_slot<TRANS, NW, S>(wide, stg, lhs_t, wg, K, N, row0, col0, M, tail, kbv, wave, lane, offK, offN)
           MOE_SLOT(0, smem + s * STAGE, kb); MOE_SLOT(1, smem + s * STAGE, kb); MOE_SLOT(2, smem + s * STAGE, kb);
@@ -544,7 +644,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
             MOE_SLOT(9, smem + s * STAGE, kb); MOE_SLOT(10, smem + s * STAGE, kb); MOE_SLOT(11, smem + s * STAGE, kb);
           }
           if (KBLOCKS)
-            __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(s / steps_per_block) * Nb,
+            __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>((kofs + s) / steps_per_block) * Nb,
                                              (lds_void*)(smem + s * STAGE + C::SC_OFF + w4 * 256), 4, 0, 0);
           if constexpr (AB) MOE_XLOAD(smem + s * STAGE, kb);
           if (s == 0) {   // the tile's lhs row scales ride its first stage (rows past the tile repeat its last)
@@ -568,7 +668,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
         step_barrier();                         // everyone's have, and step kt-1's readers are done
         const int ks = kt + NST - 1;            // the step whose loads are issued now
         const bool more = ks < KTt;
-        const int64_t kb_next = static_cast<int64_t>(ks) * G_BK;
+        const int64_t kb_next = static_cast<int64_t>(kofs + ks) * G_BK;
         uint8_t* nxt = smem + (ks % NST) * STAGE;
         const uint8_t* As = smem + (kt % NST) * STAGE;
         const uint8_t* Bs = As + bm_t * G_BK;
@@ -611,7 +711,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
               if (i == 3) { MOE_SLOT(5, nxt, kb_next); }
             }
             if (KBLOCKS && i == 0)
-              __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>(ks / steps_per_block) * Nb,
+              __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>((kofs + ks) / steps_per_block) * Nb,
                                                (lds_void*)(nxt + C::SC_OFF + w4 * 256), 4, 0, 0);
           }
 #pragma unroll
@@ -665,6 +765,41 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
       }
   #undef MOE_XLOAD
 
+      if constexpr (SPLIT) {
+        if (psplit) {   // a part of a split tile: its raw sums (int8 per column: int32) to this workgroup's slot
+                        // ([row][bn_t columns])
+          const __amdgpu_buffer_rsrc_t slot = slot_rsrc(part + static_cast<int64_t>(blockIdx.x) * kSplitSlot);
+#pragma unroll
+          for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < JN; ++j)
+              slot_store(slot, 4 * ((rbase + 16 * i + (lane & 15)) * bn_t + cbase + 16 * j + 4 * (lane >> 4)), acc[i][j]);
+          if constexpr (AB) {
+            const int jx = wave < 4 ? 0 : 2;
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              slot_store(slot, 4 * ((BM / 2 + (lane & 15)) * bn_t + cbase + 16 * (jx + q) + 4 * (lane >> 4)), acc_x[q]);
+          }
+          __builtin_amdgcn_s_waitcnt(0);                           // this wave's sums have reached the coherent level
+          __syncthreads();                                         // ... and every wave's
+          int32_t* ctr = cnt + (static_cast<int>(blockIdx.x) % 8) * kSplitPerXcd + ul;
+          if (tid == 0) {
+            const int before = atomicAdd(ctr, 1);
+            split_last = before == split_s - 1;
+            if (split_last)                                        // every part has counted in: reset for the next call
+              __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          __syncthreads();
+          if (split_last) {   // the parts' sums in part order, then the epilogue
+            constexpr int EPT = ((BM / 2 + XROWS) * 2 * BN / 4 + G_THREADS - 1) / G_THREADS;
+            static_assert(EPT * G_THREADS * 4 >= BM * BN, "plain tiles fit the same count");
+            split_fixup<G_THREADS, EPT, KBLOCKS, OUT_BF16, I8 && !KBLOCKS>(
+                part, static_cast<int>(blockIdx.x) % 8, ul, lft, split_s, rows_here, bn_t, ls_tile, rs_g, ncol_blk,
+                row0, col0, N, out_t);
+          }
+          return;
+        }
+      }
       if constexpr (I8 && !KBLOCKS) {   // the int32 sums to float32 (rounded to nearest beyond 2^24)
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -777,6 +912,15 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
     } else {
       tile_body(std::integral_constant<bool, false>{});
     }
+  }
+  };
+  if constexpr (ABS) {
+    if (split_s >= 2)
+      tile_loop(std::integral_constant<bool, true>{});
+    else
+      tile_loop(std::integral_constant<bool, false>{});
+  } else {
+    tile_loop(std::integral_constant<bool, false>{});
   }
 #undef MOE_SLOT
   // rows [n, M) are zero
@@ -1574,7 +1718,7 @@ __global__ __launch_bounds__(g256::THREADS) void gmm256_kernel(const uint8_t* __
 template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool I8>
 hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs, int Kb,
                       int Nb, const int32_t* gs, int g0, int El, int64_t M, int64_t K, int64_t N, void* out,
-                      int32_t* err, hipStream_t st) {
+                      int32_t* err, float* part, int32_t* cnt, int nslots, hipStream_t st) {
   constexpr int lds = C::LDS + static_cast<int>(sizeof(GroupTable)) + C::BM * 4;
   constexpr int per_cu = (160 * 1024) / lds > 0 ? (160 * 1024) / lds : 1;
   const int64_t ub = (moe_cdiv(M, C::BM) + El) * (N / C::BN);    // tile-count bound
@@ -1601,7 +1745,7 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
   if constexpr (TRANS && MOE_GMM_WIDE_ALL != 0 && MOE_GMM_ABSORB != 0) {
     if (El <= kAbsMaxLocal) {
       gmm_kernel<C, TRANS, KBLOCKS, OUT_BF16, false, I8, true><<<static_cast<unsigned>(grid), C::THREADS, 0, st>>>(
-          lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err, 0, 1);
+          lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out, err, 0, 1, part, cnt, nslots);
       return hipGetLastError();
     }
   }
@@ -1613,16 +1757,21 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
 template <class C, bool TRANS, bool KBLOCKS, bool I8>
 hipError_t launch_dtype(bool bf16, const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs,
                         const float* rs, int Kb, int Nb, const int32_t* gs, int g0, int El, int64_t M, int64_t K,
-                        int64_t N, void* out, int32_t* err, hipStream_t st) {
+                        int64_t N, void* out, int32_t* err, float* part, int32_t* cnt, int nslots, hipStream_t st) {
   return bf16 ? launch_cfg<C, TRANS, KBLOCKS, true, I8>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out,
-                                                        err, st)
+                                                        err, part, cnt, nslots, st)
               : launch_cfg<C, TRANS, KBLOCKS, false, I8>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs, g0, El, M, K, N, out,
-                                                         err, st);
+                                                         err, part, cnt, nslots, st);
 }
 
 }  // namespace
 
-size_t gmm_ws_bytes() { return tile::kHdr; }
+// The header (error word), and for the split last round the counters and one
+// float32 slot per workgroup of the persistent grid (one workgroup per CU).
+size_t gmm_ws_bytes() {
+  return static_cast<size_t>(tile::kSplitSlotOff) +
+         static_cast<size_t>(tile::num_cus()) * tile::kSplitSlot * sizeof(float);
+}
 
 hipError_t gmm_edge_launch(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs,
                            int Kb, int Nb, bool trans, const int32_t* gs, int g0, int El, int64_t M, int64_t K,
@@ -1693,9 +1842,18 @@ int gmm_entry(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, co
   if (!out || !group_sizes) return MOE_ERR_NULL;
   if (num_local_experts > 0 && (!lhs || !lhs_scale || !rhs || !rhs_scale)) return MOE_ERR_NULL;
   if (!ws) return MOE_ERR_WORKSPACE;
-  if (ws_bytes < moe::gmm_ws_bytes()) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < static_cast<size_t>(moe::tile::kHdr)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* err = static_cast<int32_t*>(ws);
+  // the split last round needs the counters and the slots: a workspace of the full size
+  float* part = nullptr;
+  int32_t* cnt = nullptr;
+  int nslots = 0;
+  if (ws_bytes >= moe::gmm_ws_bytes()) {
+    cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + moe::tile::kSplitCntOff);
+    part = reinterpret_cast<float*>(static_cast<char*>(ws) + moe::tile::kSplitSlotOff);
+    nslots = static_cast<int>((ws_bytes - moe::tile::kSplitSlotOff) / (moe::tile::kSplitSlot * sizeof(float)));
+  }
   const int El = num_local_experts;
   const int per_row = lhs_scale_mode == MOE_SCALE_ROW_DYNAMIC ? 1 : 0;
   const bool bf16 = out_dtype == MOE_BF16;
@@ -1704,7 +1862,8 @@ int gmm_entry(const uint8_t* lhs, const float* lhs_scale, int lhs_scale_mode, co
     return moe::gmm_edge_launch(lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, transpose_rhs != 0, group_sizes,
                                 group_offset, El, M, K, N, bf16, I8, out, err, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   using C = moe::Cfg<MOE_GMM_CFG>;
-#define MOE_GMM_ARGS bf16, lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, group_sizes, group_offset, El, M, K, N, out, err, st
+#define MOE_GMM_ARGS bf16, lhs, lhs_scale, per_row, rhs, rhs_scale, Kb, Nb, group_sizes, group_offset, El, M, K, N, out, err, \
+                     part, cnt, nslots, st
   if (transpose_rhs)
     e = Kb > 1 ? moe::launch_dtype<C, true, true, I8>(MOE_GMM_ARGS) : moe::launch_dtype<C, true, false, I8>(MOE_GMM_ARGS);
   else

@@ -21,6 +21,39 @@ constexpr int TILE_BYTES = 128 * LDS_STRIDE;
 constexpr int kHdr = 256;                   // workspace header (error word)
 constexpr int kMaxLocal = 1024;
 constexpr int kAbsMaxLocal = 512;           // group table of the kernels with absorbing tiles (LDS budget)
+// Split last round of the grouped matmul: workspace layout after the header --
+// one counter per leftover tile (kSplitPerXcd per XCD), then one float32 slot
+// of kSplitSlot elements (a 144 x 256 tile) per workgroup
+constexpr int kSplitPerXcd = 128;
+constexpr int kSplitMinSteps = 4;           // K steps per part at least
+constexpr int kSplitSlot = 144 * 256;
+constexpr int64_t kSplitCntOff = 256;       // bytes
+constexpr int64_t kSplitSlotOff = 8192;     // bytes
+
+// The split parts' sums travel between workgroups that may sit on different
+// XCDs, each behind its own L2.  They are written and read with the
+// device-scope cache policy (sc1, bit 4 of the buffer access's cache field):
+// the coding the compiler itself uses for relaxed device-scope atomic loads
+// and stores, so each 4-byte element is such an atomic and is coherent across
+// the XCDs without the whole-L2 writeback and invalidate of a device-scope
+// fence.  Ordering comes from waiting for the stores' completion before the
+// counting atomic, and from issuing the reads only after its result is known.
+constexpr int kCachePolicyDevice = 16;
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* slot) {   // slot: uniform over the workgroup
+  const uint64_t b = reinterpret_cast<uint64_t>(slot);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0,
+                                           kSplitSlot * static_cast<int>(sizeof(float)), 0x00020000);
+}
+__device__ __forceinline__ void slot_store(__amdgpu_buffer_rsrc_t r, int byte_off, v4f v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), r, byte_off, 0, kCachePolicyDevice);
+}
+__device__ __forceinline__ v4f slot_load(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCachePolicyDevice));
+}
 
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);

@@ -15,7 +15,7 @@ from oracle.sort import sort_by_expert
 from tests.parity import (assert_bits_equal, check_bf16, check_f32, dev_f32, dev_i32, dev_u8, gmm_allowance, host,
                           tgmm_allowance)
 from tests.mfma_model import gmm_samples, tgmm_samples
-from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate
+from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -226,7 +226,8 @@ def test_gmm_256_tiles_ragged(sizes, N, nb, static):
     _check_gmm_full(lhs, ls, mode, w, rs, gs, E, 0, E, 1, f"256 tiles {sizes} N={N} {nb}", hw=True)
 
 
-@pytest.mark.parametrize("N,nb,Kb", [(512, "block", 2), (384, "channel", 1), (256, "block", 3)])
+@pytest.mark.parametrize("N,nb,Kb", [(512, "block", 2), (384, "channel", 1), (256, "block", 3), (512, "block64", 4),
+                                     (384, "block64", 2)])
 def test_gmm_absorbing_row_blocks(N, nb, Kb):
     """Group sizes at the boundaries of the absorbing row blocks (a group of
     m rows takes ceil(m / 144) blocks of 128 rows plus up to 16 each, so
@@ -243,10 +244,52 @@ def test_gmm_absorbing_row_blocks(N, nb, Kb):
     K = 128 * Kb if Kb > 1 else 512
     lhs = rng.integers(0, 0x70, (M, K)).astype(np.uint8)
     w = rng.integers(0, 0x70, (E, K, N)).astype(np.uint8)
-    nbv = N // 128 if nb == "block" else N
+    nbv = {"block": N // 128, "block64": N // 64, "channel": N}[nb]     # 128- or 64-column scale blocks
     rs = rng.uniform(0.001, 0.1, (E, Kb, 1, nbv)).astype(np.float32)
     ls = rng.uniform(0.01, 1, M).astype(np.float32)
     _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, 0, E, 1, f"absorbing N={N} {nb} Kb={Kb}", hw=True)
+
+
+@pytest.mark.parametrize("sizes,N,blockwise", [([300, 200, 50], 1024, True), ([40, 0, 513, 7], 2048, False),
+                                                ([100], 2048, True)])
+def test_gmm_split_last_round(sizes, N, blockwise):
+    """Few tiles over many workgroups: each XCD's last (here only) round of
+    tiles is split along K (K = 2048: parts of at least four 128-deep steps),
+    whose float32 sums meet in the workspace.  Quantized gaussian operands, as
+    in the workloads: every element of both outputs under the strict rule
+    (the matrix-core model for the rare misses), the same bits on a second
+    call, and the same rule with a header-only workspace (no split)."""
+    rng = np.random.default_rng(sum(sizes) + N)
+    E = len(sizes)
+    gs = np.array(sizes, np.int32)
+    n = int(gs.sum())
+    M, K = n + 37, 2048
+    x = to_bf16_bits(rng.standard_normal((n, K)).astype(np.float32))
+    xq, xsc, _ = quantize_rows(x, SCALE_ROW_DYNAMIC)
+    w = to_bf16_bits((rng.standard_normal((E, K, N)) * 0.02).astype(np.float32))
+    kb, nb = (K // 128, N // 128) if blockwise else (1, N)
+    wq, ws_ = quantize_weights(w, kb, nb)
+    what = f"split {sizes} N={N} {'blockwise' if blockwise else 'per-channel'}"
+    _check_gmm_full(xq, xsc, SCALE_ROW_DYNAMIC, wq, ws_, gs, E, 0, E, 1, what, M=M)
+    lhs = np.zeros((M, K), np.uint8)
+    lhs[:n] = xq
+    ls = np.zeros(M, np.float32)
+    ls[:n] = xsc
+    rhs = np.ascontiguousarray(wq.transpose(0, 2, 1))
+    a, err_a = gpu_gmm(lhs, ls, SCALE_ROW_DYNAMIC, rhs, ws_, gs, E, 0, E, 1, m.MOE_BF16)
+    b, err_b = gpu_gmm(lhs, ls, SCALE_ROW_DYNAMIC, rhs, ws_, gs, E, 0, E, 1, m.MOE_BF16)
+    assert err_a == 0 and err_b == 0
+    assert_bits_equal(a, b, "split: second call")
+    # a header-only workspace: the same product without the split
+    out = torch.full((M, N), 3.0, dtype=torch.float32, device="cuda")
+    small = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    print(f"gmm header-only workspace M={M} K={K} N={N}", flush=True)
+    m.moe_gmm_fp8(dev_u8(lhs), dev_f32(ls), SCALE_ROW_DYNAMIC, dev_u8(rhs), dev_f32(ws_), kb, nb, 1, dev_i32(gs), E, 0,
+                  E, M, K, N, m.MOE_F32, out, small)
+    assert m.moe_debug_check(small) == 0
+    o = gmm(lhs, ls, wq, ws_, gs, 0, E)
+    check_f32(host(out), o["out"], o["abs_sum"], what + " header-only workspace",
+              model=lambda idx: gmm_samples(lhs, ls, wq, ws_, gs, 0, E, idx // N, idx % N))
 
 
 def test_gmm_256_tiles_local_slice():

@@ -163,6 +163,38 @@ def test_gmm_i8_integer_sums_exact(sizes, K, N, Kb, tr):
     assert not g[n:].any()
 
 
+def test_gmm_i8_split_last_round_rounds_once():
+    """Few tiles over many workgroups, K = 2048: each XCD's only round of
+    tiles is split along K (four parts of 512).  Codes of one sign push the
+    integer sums past 2^24, where float32 is no longer exact: with unit
+    scales every element must still be the exact sum rounded once, as
+    without the split -- adding the parts' sums as float32 would round up to
+    three more times, and does for some elements of these operands (checked
+    on the host, so the test cannot pass by accident)."""
+    rng = np.random.default_rng(77)
+    sizes = [300, 200, 50]
+    El, K, N = len(sizes), 2048, 1024
+    gs = np.array(sizes, np.int32)
+    n = int(gs.sum())
+    M = n + 37
+    X = rng.integers(96, 128, (n, K)).astype(np.int8)
+    W = rng.integers(96, 128, (El, K, N)).astype(np.int8)
+    ls = np.ones(M, np.float32)
+    rs = np.ones((El, 1, 1, N), np.float32)
+    o = gmm_int8(np.concatenate([X, np.zeros((M - n, K), np.int8)]), ls, W, rs, gs, 0, El)
+    want = o["out"].astype(np.float32)
+    assert np.abs(o["out"]).min(initial=2 ** 25, where=o["out"] != 0) > 2 ** 24
+    # the float32 sum of four 512-deep partial sums differs from the single rounding somewhere
+    Xg, Wg = X[:300].astype(np.int64), W[0].astype(np.int64)
+    parts = [(Xg[:, q * 512:(q + 1) * 512] @ Wg[q * 512:(q + 1) * 512]).astype(np.float32) for q in range(4)]
+    fsum = ((parts[0] + parts[1]) + parts[2]) + parts[3]
+    assert (fsum != want[:300]).any()
+    rhs = np.ascontiguousarray(W.transpose(0, 2, 1))
+    g = gpu_gmm_i8(X, ls, SCALE_ROW_DYNAMIC, rhs, rs, gs, El, 0, El, 1, m.MOE_F32, M=M)
+    assert_bits_equal(g, want, "int8 split: integer sums rounded once")
+    assert not g[n:].any()
+
+
 def test_gmm_i8_local_slice_exact():
     rng = np.random.default_rng(7)
     E, g0, El, K, N = 16, 4, 8, 384, 256

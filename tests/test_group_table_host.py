@@ -190,3 +190,58 @@ def test_absorbing_decision_on_the_workload_routings():
     sizes6 = np.bincount(generate(c6, with_weights=False)["ids"].ravel(), minlength=c6.E)
     ok, t2, t3 = absorb_decision(sizes6, c6.I // 128)
     assert not ok and (t2, t3) == (560, 544)
+
+
+def split_plan(total, grid, KT, nslots=None, per_xcd_max=128, min_steps=4):
+    """The grouped matmul's work items, replayed: for each workgroup, its list
+    of (tile, first K step, end K step, slot of a split part or None) and the
+    counter each split tile uses."""
+    nslots = grid if nslots is None else nslots
+    items = {}
+    for b in range(grid):
+        x, xj = b % 8, b // 8
+        step = (grid - x + 7) // 8
+        lo, hi = total * x // 8, total * (x + 1) // 8
+        first = lo + xj
+        rounds = (hi - lo) // step
+        lft = hi - lo - rounds * step
+        lbase = lo + rounds * step
+        s = 1
+        if lft > 0 and grid <= nslots and lft <= per_xcd_max:
+            s = max(min(step // lft, KT // min_steps), 1)
+        n_full = rounds if s >= 2 else (len(range(first, hi, step)) if first < hi else 0)
+        lst = [(first + i * step, 0, KT, None, None) for i in range(n_full)]
+        if s >= 2 and lft > 0 and xj < lft * s:
+            ul, up = xj % lft, xj // lft
+            lst.append((lbase + ul, up * KT // s, (up + 1) * KT // s, b, (x * per_xcd_max + ul, s, lft)))
+        items[b] = lst
+    return items
+
+
+@pytest.mark.parametrize("total,grid,KT", [(560, 256, 56), (24, 48, 16), (1024, 256, 56), (1200, 256, 56),
+                                           (7, 256, 16), (300, 256, 4), (33, 40, 64), (2100, 256, 16), (9, 9, 8)])
+def test_split_plan_covers_each_tile_once(total, grid, KT):
+    """Whole tiles are computed once; a split tile's parts cover its K steps
+    once, each part writes the slot of the workgroup that computes it, the
+    counter is in range, and part p of a tile is workgroup l + p * lft of the
+    XCD, as the last part's summation reads it."""
+    items = split_plan(total, grid, KT)
+    cover = {}
+    for b, lst in items.items():
+        for t, k0, k1, slot, ctr in lst:
+            assert 0 <= t < total and 0 <= k0 < k1 <= KT
+            cover.setdefault(t, []).append((k0, k1))
+            if slot is not None:
+                assert slot == b < grid
+                ci, s, lft = ctr
+                assert 0 <= ci < 8 * 128 and k1 - k0 >= 4
+                x, ul = b % 8, ci % 128
+                parts = [x + 8 * (ul + p * lft) for p in range(s)]
+                assert b in parts and all(q < grid for q in parts)
+    assert sorted(cover) == list(range(total))
+    for t, ranges in cover.items():
+        ranges.sort()
+        assert ranges[0][0] == 0 and ranges[-1][1] == KT
+        assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
+    if (total, grid) == (560, 256):          # the skewed up-projection: its third round is split
+        assert any(len(r) > 1 for r in cover.values())
