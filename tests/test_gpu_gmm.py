@@ -382,6 +382,28 @@ def test_tgmm_config5_full():
                                              idx % N))
 
 
+def test_tgmm_dy_by_rows_ends_at_the_buffer():
+    """The product reads dY by rows, a group's last K step reaching up to 127
+    rows past its end: here the buffer ends at the last group's last row, so
+    those reads are kept inside it, and the next group's rows (large codes
+    of both signs) must add nothing to a group's gradient."""
+    rng = np.random.default_rng(123)
+    gs = np.array([37, 300, 0, 91], np.int32)
+    E = len(gs)
+    M = int(gs.sum())
+    K, N = 512, 256
+    X = rng.integers(0, 0x7E, (M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)).astype(np.uint8) << 7)
+    D = rng.integers(0x60, 0x7E, (M, N)).astype(np.uint8) | (rng.integers(0, 2, (M, N)).astype(np.uint8) << 7)
+    xs = rng.uniform(0.01, 1, K).astype(np.float32)
+    ds = rng.uniform(0.001, 0.01, N).astype(np.float32)
+    o = tgmm(X, xs, D, ds, gs, 0, E)
+    g, err = gpu_tgmm(X, xs, D, ds, gs, E, 0, E)
+    assert err == 0
+    B = lambda idx: tgmm_allowance(X, xs, D, ds, gs, 0, E, idx // (K * N), (idx // N) % K, idx % N)
+    check_f32(g, o["out"], o["abs_sum"], "tgmm dY by rows, buffer end", hw_allowance=B)
+    assert not g[2].any()
+
+
 @pytest.mark.parametrize("K,small_ws", [(384, False), (256, True)])
 def test_tgmm_one_kernel_path(K, small_ws):
     """The one-kernel tgmm (operands transposed in LDS while multiplying) serves
