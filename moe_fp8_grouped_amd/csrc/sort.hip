@@ -30,7 +30,8 @@ namespace {
 
 constexpr int kTile = 2048;          // routed slots per tile (256 threads x 8), large inputs
 constexpr int kTileSmall = 512;      // routed slots per tile when the tile table fits in LDS
-constexpr int kScanLds = 15360;      // int32 entries of the tile table the scan keeps in LDS (60 KiB)
+constexpr int kScanLds = 15104;      // int32 entries of the tile table the scan keeps in LDS (59 KiB: with a
+                                     // row of counts and the kernel's own 68 bytes it stays within 64 KiB)
 constexpr int kHdr = 256;            // workspace header bytes
 // header int32 slots
 constexpr int kErr = 0, kStart = 1, kN = 2, kValid = 3;
@@ -47,13 +48,20 @@ template <int TILE>
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
                                                         int32_t* __restrict__ err, int32_t* __restrict__ tile_hist) {
   extern __shared__ int hist[];
-  for (int e = threadIdx.x; e <= E; e += 256) hist[e] = 0;
-  __syncthreads();
+  // every load of the thread's ids goes out before the first is used (one memory latency, not one per id)
   const int64_t base = static_cast<int64_t>(blockIdx.x) * TILE;
+  int idv[TILE / 256];
 #pragma unroll
   for (int i = 0; i < TILE / 256; ++i) {
     const int64_t f = base + i * 256 + threadIdx.x;
-    if (f < M) atomicAdd(&hist[key_of(ids[f], E, err)], 1);
+    idv[i] = f < M ? ids[f] : -1;
+  }
+  for (int e = threadIdx.x; e <= E; e += 256) hist[e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TILE / 256; ++i) {
+    const int64_t f = base + i * 256 + threadIdx.x;
+    if (f < M) atomicAdd(&hist[key_of(idv[i], E, err)], 1);
   }
   __syncthreads();
   int32_t* out = tile_hist + static_cast<int64_t>(blockIdx.x) * (E + 1);
@@ -61,31 +69,33 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
 }
 
 // Copy n ints from global memory to LDS with `nthreads` threads: each thread
-// issues eight independent loads before their LDS stores, so a table of many
-// cells per thread costs a few memory latencies instead of one per cell.
+// issues up to 32 independent loads before their LDS stores, so a table of
+// up to 32 cells per thread costs one memory latency instead of one per cell.
 __device__ __forceinline__ void copy_to_lds(const int32_t* __restrict__ src, int* dst, int n, int nthreads) {
-  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * nthreads) {
-    int v[8];
+  constexpr int U = 32;
+  for (int i0 = threadIdx.x; i0 < n; i0 += U * nthreads) {
+    int v[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + u * nthreads;
       v[u] = i < n ? src[i] : 0;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int i = i0 + u * nthreads;
       if (i < n) dst[i] = v[u];
     }
   }
 }
 
-// Exclusive prefix sum of a[0..n) in LDS by the first wave (n <= 1025).
-__device__ void wave0_exclusive_scan(int* a, int n) {
-  if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  int carry = 0;
-  for (int b = 0; b < n; b += 64) {
-    const int i = b + lane;
+// Exclusive prefix sum of a[0..n) in LDS by every wave of the block: each
+// 64-entry chunk is scanned by one wave with lane shuffles, then every entry
+// adds the totals of the chunks before it (wt: at least ceil(n / 64) ints).
+__device__ void block_exclusive_scan(int* a, int n, int* wt) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int nch = (n + 63) / 64;
+  for (int c = w; c < nch; c += nw) {
+    const int i = c * 64 + lane;
     const int v = i < n ? a[i] : 0;
     int incl = v;
 #pragma unroll
@@ -93,8 +103,14 @@ __device__ void wave0_exclusive_scan(int* a, int n) {
       const int t = __shfl_up(incl, o, 64);
       if (lane >= o) incl += t;
     }
-    if (i < n) a[i] = carry + incl - v;
-    carry += __shfl(incl, 63, 64);
+    if (i < n) a[i] = incl - v;
+    if (lane == 63) wt[c] = incl;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    int s = 0;
+    for (int c = 0; c < i / 64; ++c) s += wt[c];
+    a[i] += s;
   }
 }
 
@@ -105,6 +121,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
                                                          int g0, int El, int32_t* __restrict__ group_sizes,
                                                          int32_t* __restrict__ hdr, int in_lds) {
   extern __shared__ int tot[];        // [E + 1], then the table when in_lds
+  __shared__ int wt[17];              // chunk totals of the expert scan (E + 1 <= 1025)
   int* tab = tot + (E + 1);
   const int64_t cells = static_cast<int64_t>(ntiles) * (E + 1);
   int32_t* col = in_lds ? tab : tile_hist;
@@ -123,7 +140,7 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
     if (e < E) group_sizes[e] = run;
   }
   __syncthreads();
-  wave0_exclusive_scan(tot, E + 1);
+  block_exclusive_scan(tot, E + 1, wt);
   __syncthreads();
   if (in_lds) {
     for (int64_t i = threadIdx.x; i < cells; i += blockDim.x) tile_hist[i] = tab[i] + tot[i % (E + 1)];
@@ -145,40 +162,68 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ t
 // block reads the whole [ntiles][E + 1] table into LDS and derives its own
 // tile's offsets -- the counts of the earlier tiles plus the expert bases --
 // and block 0 writes group_sizes and the window header.  Otherwise tile_off
-// holds the offsets the scan kernel wrote.
-template <int TILE, bool FUSED_SCAN>
-__global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E, int nbits,
-                                                        int64_t M_cap, int32_t* __restrict__ hdr,
-                                                        int32_t* __restrict__ err,
-                                                        const int32_t* __restrict__ tile_off, int ntiles, int g0,
-                                                        int El, int32_t* __restrict__ group_sizes,
-                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv_pos) {
+// holds the offsets the scan kernel wrote.  NWV waves per block, each ranking
+// TILE / NWV slots: the phases are latency chains, so more waves per tile
+// shorten every one of them.
+template <int TILE, bool FUSED_SCAN, int NWV>
+__global__ __launch_bounds__(64 * NWV) void sort_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
+                                                             int nbits, int64_t M_cap, int32_t* __restrict__ hdr,
+                                                             int32_t* __restrict__ err,
+                                                             const int32_t* __restrict__ tile_off, int ntiles, int g0,
+                                                             int El, int32_t* __restrict__ group_sizes,
+                                                             int32_t* __restrict__ perm, int32_t* __restrict__ inv_pos) {
+  constexpr int NT = 64 * NWV, CH = TILE / NT;   // threads; 64-slot chunks per wave
+  static_assert(CH >= 1 && TILE % NT == 0, "whole chunks per wave");
   extern __shared__ int lds[];
-  int* cnt = lds;                      // [4][E + 1] running counts per wave
-  int* off = lds + 4 * (E + 1);        // [E + 1] global base of this tile
+  int* cnt = lds;                      // [NWV][E + 1] running counts per wave
+  int* off = lds + NWV * (E + 1);      // [E + 1] global base of this tile
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   __shared__ int win[2];               // start, n of the local window
+  __shared__ int wt[17];               // chunk totals of the expert scan (E + 1 <= 1025)
+  // the thread's ids, loaded first: their latency overlaps the offsets' set-up, and the ranking below
+  // never waits for memory chunk by chunk
+  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * TILE + w * (TILE / NWV);
+  int idv[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int64_t f = wbase + c * 64 + lane;
+    idv[c] = f < M ? ids[f] : 0;
+  }
   if constexpr (FUSED_SCAN) {
-    int* tab = lds + 5 * (E + 1);      // [ntiles][E + 1] counts
+    int* tab = off + (E + 1);          // [ntiles][E + 1] counts
     int* tot = tab + ntiles * (E + 1); // [E + 1] totals, then their exclusive scan
     const int cells = ntiles * (E + 1);
-    copy_to_lds(tile_off, tab, cells, 256);
+    copy_to_lds(tile_off, tab, cells, NT);
     __syncthreads();
-    for (int e = threadIdx.x; e <= E; e += 256) {
+    // each expert's counts over the earlier tiles and over all tiles, P threads per expert (P a power of
+    // two, so a group of P lanes sits in one wave), combined with lane shuffles
+    int P = 1;
+    while (P < 16 && 2 * P * (E + 1) <= NT) P *= 2;
+    const int part = threadIdx.x & (P - 1);
+    for (int e0 = 0; e0 <= E; e0 += NT / P) {
+      const int e = e0 + static_cast<int>(threadIdx.x) / P;
       int before = 0, all = 0;
-      for (int t = 0; t < ntiles; ++t) {
-        const int c = tab[t * (E + 1) + e];
-        before += t < static_cast<int>(blockIdx.x) ? c : 0;
-        all += c;
+      if (e <= E) {
+        for (int t = part; t < ntiles; t += P) {
+          const int c = tab[t * (E + 1) + e];
+          before += t < static_cast<int>(blockIdx.x) ? c : 0;
+          all += c;
+        }
       }
-      off[e] = before;
-      tot[e] = all;
-      if (blockIdx.x == 0 && e < E) group_sizes[e] = all;
+      for (int o = 1; o < P; o <<= 1) {
+        before += __shfl_xor(before, o, 64);
+        all += __shfl_xor(all, o, 64);
+      }
+      if (e <= E && part == 0) {
+        off[e] = before;
+        tot[e] = all;
+        if (blockIdx.x == 0 && e < E) group_sizes[e] = all;
+      }
     }
     __syncthreads();
-    wave0_exclusive_scan(tot, E + 1);
+    block_exclusive_scan(tot, E + 1, wt);
     __syncthreads();
-    for (int e = threadIdx.x; e <= E; e += 256) off[e] += tot[e];
+    for (int e = threadIdx.x; e <= E; e += NT) off[e] += tot[e];
     if (threadIdx.x == 0) {
       win[0] = tot[g0];
       win[1] = tot[g0 + El] - tot[g0];
@@ -188,28 +233,23 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
         hdr[kValid] = tot[E];
       }
     }
-    for (int e = threadIdx.x; e <= E; e += 256)
-      cnt[e] = cnt[(E + 1) + e] = cnt[2 * (E + 1) + e] = cnt[3 * (E + 1) + e] = 0;
   } else {
-    for (int e = threadIdx.x; e <= E; e += 256) {
-      cnt[e] = cnt[(E + 1) + e] = cnt[2 * (E + 1) + e] = cnt[3 * (E + 1) + e] = 0;
-      off[e] = tile_off[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
-    }
+    for (int e = threadIdx.x; e <= E; e += NT) off[e] = tile_off[static_cast<int64_t>(blockIdx.x) * (E + 1) + e];
     if (threadIdx.x == 0) {
       win[0] = hdr[kStart];
       win[1] = hdr[kN];
     }
   }
+  for (int i = threadIdx.x; i < NWV * (E + 1); i += NT) cnt[i] = 0;
   __syncthreads();
-  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * TILE + w * (TILE / 4);
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  int keys[TILE / 256], rank[TILE / 256];
+  int keys[CH], rank[CH];
   int* my = cnt + w * (E + 1);
 #pragma unroll
-  for (int c = 0; c < TILE / 256; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int64_t f = wbase + c * 64 + lane;
     const bool valid = f < M;
-    const int key = valid ? key_of(ids[f], E, nullptr) : 0;
+    const int key = valid ? key_of(idv[c], E, nullptr) : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (key >> b) & 1;
@@ -226,10 +266,10 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
     rank[c] = prior + r;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += 256) {
+  for (int e = threadIdx.x; e <= E; e += NT) {   // each wave's base: the counts of the waves before it
     int s = 0;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    for (int ww = 0; ww < NWV; ++ww) {
       const int t = cnt[ww * (E + 1) + e];
       cnt[ww * (E + 1) + e] = s;
       s += t;
@@ -238,7 +278,7 @@ __global__ __launch_bounds__(256) void sort_rank_kernel(const int32_t* __restric
   __syncthreads();
   const int start = win[0], n = win[1];
 #pragma unroll
-  for (int c = 0; c < TILE / 256; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int key = keys[c];
     if (key < 0) continue;
     const int64_t f = wbase + c * 64 + lane;
@@ -469,34 +509,36 @@ int sort_metadata(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E, in
     MOE_CHECK_LAUNCH();
   }
   // hist -> rank with the scan fused into every rank block when the tile
-  // table fits in LDS; hist -> scan -> rank otherwise
-  const size_t rank_lds = 6 * hist_lds + static_cast<size_t>(ntiles) * (E + 1) * sizeof(int);
-  if (ntiles > 0 && scan_in_lds && rank_lds <= 64 * 1024) {
-    if (small)
-      sort_rank_kernel<kTileSmall, true><<<ntiles, 256, rank_lds, st>>>(
-          expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-          perm, inv_pos);
-    else
-      sort_rank_kernel<kTile, true><<<ntiles, 256, rank_lds, st>>>(
-          expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts, group_sizes,
-          perm, inv_pos);
-    MOE_CHECK_LAUNCH();
-  } else {
-    const size_t scan_lds = hist_lds + (scan_in_lds ? static_cast<size_t>(ntiles) * (E + 1) * sizeof(int) : 0);
+  // table fits in LDS; hist -> scan -> rank otherwise.  Rank blocks: 16 waves
+  // on a 2048-slot tile, 8 on a 512-slot tile (two and one 64-slot chunks per
+  // wave) with a row of per-wave counts each in LDS; 4 waves where that would
+  // not fit in 64 KiB (many experts).
+  const size_t table_lds = static_cast<size_t>(ntiles) * (E + 1) * sizeof(int);
+  auto rank_lds = [&](int nwv, bool fused) { return (nwv + (fused ? 2 : 1)) * hist_lds + (fused ? table_lds : 0); };
+  constexpr size_t kMaxLds = 64 * 1024 - 256;    // dynamic LDS, leaving room for the kernel's own arrays
+  const bool fused = ntiles > 0 && scan_in_lds && rank_lds(4, true) <= kMaxLds;
+  const bool wide = rank_lds(small ? 8 : 16, fused) <= kMaxLds;
+  const size_t lds = rank_lds(wide ? (small ? 8 : 16) : 4, fused);
+  if (!fused) {
+    const size_t scan_lds = hist_lds + (scan_in_lds ? table_lds : 0);
     sort_scan_kernel<<<1, 1024, scan_lds, st>>>(tile_hist, ntiles, E, group_offset, num_local_experts,
                                                      group_sizes, hdr, scan_in_lds ? 1 : 0);
     MOE_CHECK_LAUNCH();
-    if (ntiles > 0) {
-      if (small)
-        sort_rank_kernel<kTileSmall, false><<<ntiles, 256, 5 * hist_lds, st>>>(
-            expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts,
-            group_sizes, perm, inv_pos);
-      else
-        sort_rank_kernel<kTile, false><<<ntiles, 256, 5 * hist_lds, st>>>(
-            expert_ids, M, E, nbits, M_cap, hdr, err, tile_hist, ntiles, group_offset, num_local_experts,
-            group_sizes, perm, inv_pos);
-      MOE_CHECK_LAUNCH();
+  }
+  if (ntiles > 0) {
+#define MOE_RANK(TILE, FUSED, NWV)                                                                              \
+  sort_rank_kernel<TILE, FUSED, NWV><<<ntiles, 64 * NWV, lds, st>>>(expert_ids, M, E, nbits, M_cap, hdr, err,   \
+                                                                     tile_hist, ntiles, group_offset,          \
+                                                                     num_local_experts, group_sizes, perm, inv_pos)
+    if (small) {
+      if (fused) { if (wide) MOE_RANK(kTileSmall, true, 8); else MOE_RANK(kTileSmall, true, 4); }
+      else { if (wide) MOE_RANK(kTileSmall, false, 8); else MOE_RANK(kTileSmall, false, 4); }
+    } else {
+      if (fused) { if (wide) MOE_RANK(kTile, true, 16); else MOE_RANK(kTile, true, 4); }
+      else { if (wide) MOE_RANK(kTile, false, 16); else MOE_RANK(kTile, false, 4); }
     }
+#undef MOE_RANK
+    MOE_CHECK_LAUNCH();
   }
   return MOE_OK;
 }
