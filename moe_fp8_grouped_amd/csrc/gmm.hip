@@ -99,11 +99,6 @@
 #ifndef MOE_GMM_STREAM
 #define MOE_GMM_STREAM 0
 #endif
-// 256 x 256 tiles on the 32 x 32 x 64 MFMA for the forward product with
-// [E, N, K] weights, per-channel (or coarser) scales and bf16 output.
-#ifndef MOE_GMM256
-#define MOE_GMM256 1
-#endif
 // Every forward tile of the 256 x 128 kernel as BM/2 rows x 2 BN columns (two
 // weight column blocks per stage, the two 128-row halves of a group's rows on
 // neighbouring workgroups): the same stage bytes and loads per wave, each
@@ -1452,268 +1447,6 @@ __global__ __launch_bounds__(C::THREADS) void gmm_stream_kernel(
   }
 }
 
-// ---------------------------------------------------------------- 256 x 256
-// gmm256_kernel: the grouped matmul with the weights stored [E, N, K] (both
-// operands contraction-contiguous) on 256 x 256 output tiles and the
-// 32 x 32 x 64 fp8 MFMA (v_mfma_f32_32x32x64_f8f6f4).  A K step of 64
-// stages 256 A rows and 256 B rows of 64 bytes (32 KiB); four stages, three
-// of them in flight while the waves multiply the fourth.  Per flop that is
-// two thirds of the bytes of gmm_kernel's 256 x 128 x 128 step, with one more
-// step in flight, and 25 % fewer fragment bytes read from LDS.
-//  * MFMA operands: lane l supplies row l%32 and contraction bytes
-//    32 (l/32) .. +31.  With the weight fragment as the first operand, lane l
-//    holds output row l%32 and, in accumulator register r, output column
-//    8 (r/4) + 4 (l/32) + r%4 (checked on the device).
-//  * Staged rows are 64 bytes: chunk c of row r sits at slot c ^ s(r),
-//    s(r) = ((r >> 2) & 3) ^ (r & 2) -- a 16-byte read of 8 (or 16)
-//    consecutive rows per lane group meets distinct banks, and s depends on
-//    r & 15 only, so a direct load of 16 rows needs one offset per lane.
-//  * The waves form a 2 x 4 grid of 128 x 64 wave tiles (4 x 2 MFMA blocks).
-//  * Tiles: per n-tile, the group's full 256-row m-tiles, then its
-//    remainder: at most 128 rows -> a 128 x 256 tile (64 x 64 wave tiles,
-//    3 loads per wave per step instead of 4), else a 256 x 256 tile whose
-//    rows past the group are not stored.
-//  * Epilogue: scaled in float32, rounded to bf16, staged in LDS (rows
-//    padded to 264 elements) and written with 16-byte row-contiguous stores.
-namespace g256 {
-constexpr int BM = 256, BN = 256, BK = 64, NST = 4, NW = 8, THREADS = 64 * NW;
-constexpr int STAGE = (BM + BN) * BK;                 // 32 KiB
-constexpr int OS = BN + 8;                            // staged output row, bf16 elements
-constexpr int LDS = NST * STAGE > BM * OS * 2 ? NST * STAGE : BM * OS * 2;
-__device__ __forceinline__ int swz64(int r) { return ((r >> 2) & 3) ^ (r & 2); }
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v16f mfma32(const v8i& a, const v8i& b, const v16f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-// LDS byte address of a staged byte
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  typedef const __attribute__((address_space(3))) uint8_t lds_u8;
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u8*)p));
-}
-// Fragments of 32 staged rows each (two 16-byte reads per lane at a + lo,
-// a + hi), completed before returning.  The reads are one asm block: the
-// stages are filled by direct loads whose completion the caller has already
-// waited for, and the compiler's own tracking of those loads would make it
-// wait for every load still in flight before a plain LDS read.
-__device__ __forceinline__ void frag3(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t lo, uint32_t hi, v8i& f0,
-                                      v8i& f1, v8i& f2) {
-  v4i x0, y0, x1, y1, x2, y2;
-  asm volatile(
-      "ds_read_b128 %0, %6\n\t"
-      "ds_read_b128 %1, %7\n\t"
-      "ds_read_b128 %2, %8\n\t"
-      "ds_read_b128 %3, %9\n\t"
-      "ds_read_b128 %4, %10\n\t"
-      "ds_read_b128 %5, %11\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(y0), "=&v"(x1), "=&v"(y1), "=&v"(x2), "=&v"(y2)
-      : "v"(a0 + lo), "v"(a0 + hi), "v"(a1 + lo), "v"(a1 + hi), "v"(a2 + lo), "v"(a2 + hi)
-      : "memory");
-  f0 = v8i{x0[0], x0[1], x0[2], x0[3], y0[0], y0[1], y0[2], y0[3]};
-  f1 = v8i{x1[0], x1[1], x1[2], x1[3], y1[0], y1[1], y1[2], y1[3]};
-  f2 = v8i{x2[0], x2[1], x2[2], x2[3], y2[0], y2[1], y2[2], y2[3]};
-}
-__device__ __forceinline__ v8i frag1(uint32_t a0, uint32_t lo, uint32_t hi) {
-  v4i x, y;
-  asm volatile(
-      "ds_read_b128 %0, %2\n\t"
-      "ds_read_b128 %1, %3\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x), "=&v"(y)
-      : "v"(a0 + lo), "v"(a0 + hi)
-      : "memory");
-  return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-}
-}  // namespace g256
-
-template <bool OUT_BF16>
-__global__ __launch_bounds__(g256::THREADS) void gmm256_kernel(const uint8_t* __restrict__ lhs,
-                                                             const float* __restrict__ ls, int ls_per_row,
-                                                             const uint8_t* __restrict__ rhs,
-                                                             const float* __restrict__ rs, int Kb, int Nb,
-                                                             const int32_t* __restrict__ group_sizes, int g0, int El,
-                                                             int64_t M, int64_t K, int64_t N,
-                                                             void* __restrict__ out, int32_t* __restrict__ err) {
-  using namespace g256;
-  static_assert(OUT_BF16, "bfloat16 output");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
-  __shared__ GroupTable gt;
-  __shared__ float ls_tile[BM];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int NT = static_cast<int>(N / BN);
-  build_groups(group_sizes, g0, El, M, NT, BM, err, gt, reinterpret_cast<int*>(smem), false);
-  const int total = gt.tiles_off[El];
-  const int n_rows = gt.rows_off[El];
-  const int KT = static_cast<int>(K / BK);
-  const uint32_t ncol_blk = static_cast<uint32_t>(N / Nb);
-  (void)Kb;
-  int first, last, step;
-  xcd_share(total, first, last, step);
-  // this lane's part of a direct load filling 16 staged rows: row l/4, slot l%4
-  const int sub = lane >> 2;
-  const uint32_t loff = static_cast<uint32_t>(sub * K + 16 * ((lane & 3) ^ swz64(sub)));
-  // fragment reads: row l%32 of a 32-row block, chunks 2(l/32) and 2(l/32)+1
-  const int l32 = lane & 31, h = lane >> 5;
-  const uint32_t f_lo = l32 * BK + 16 * ((2 * h) ^ swz64(l32));
-  const uint32_t f_hi = l32 * BK + 16 * ((2 * h + 1) ^ swz64(l32));
-  const int w4 = wave & 3;
-
-  for (int t = first; t < last; t += step) {
-    const int g = find_group(gt, El, t);
-    const int local = t - gt.tiles_off[g];
-    const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
-    const int full = m_g / BM, rem = m_g - full * BM;
-    const int per = full + (rem ? 1 : 0);
-    const int nt = local / per, mt = local - nt * per;
-    // a 128 x 256 tile; wave-uniform in a scalar register, so the wait counts
-    // below are chosen by a scalar branch
-    const bool half = __builtin_amdgcn_readfirstlane(mt == full && rem > 0 && rem <= BM / 2 ? 1 : 0) != 0;
-    const int64_t row0 = gt.rows_off[g] + static_cast<int64_t>(mt) * BM;
-    const int rows_here = min(BM, m_g - mt * BM);
-    const int64_t col0 = static_cast<int64_t>(nt) * BN;
-    const int bm_t = half ? BM / 2 : BM;
-    const bool tail = row0 + bm_t > M;
-    const uint8_t* wg = rhs + static_cast<int64_t>(g) * K * N;
-    const float* rs_g = rs + static_cast<int64_t>(g) * Nb;       // Kb == 1 here
-    // this wave's output block: rows rbase .., columns cbase .. +63
-    const int WM = half ? 64 : 128;
-    const int rbase = (wave >> 2) * WM, cbase = (wave & 3) * 64;
-    // this wave's load sources at contraction offset 0 and LDS destinations:
-    // plain: A rows 32w, 32w+16 and B rows 32w, 32w+16; half: A rows 16w and
-    // B rows 32w, 32w+16
-    const uint8_t* src[4];
-    int dst[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bool isA = half ? s == 0 : s < 2;
-      const int R = half ? (s == 0 ? 16 * wave : 32 * wave + 16 * (s - 1)) : 32 * wave + 16 * (s & 1);
-      if (isA) {
-        if (!tail) {
-          src[s] = lhs + (row0 + R) * K + loff;
-        } else {
-          const int64_t r = min(row0 + R + sub, M - 1);
-          src[s] = lhs + r * K + (loff - static_cast<uint32_t>(sub * K));
-        }
-        dst[s] = R * BK;
-      } else {
-        src[s] = wg + (col0 + R) * K + loff;
-        dst[s] = bm_t * BK + R * BK;
-      }
-    }
-    const int lps = half ? 3 : 4;          // direct loads per wave per K step
-
-    v16f acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
-
-    step_barrier();       // the previous tile's epilogue is done with the LDS
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s) {
-      if (s < KT) {
-        uint8_t* stg = smem + s * STAGE;
-        const int64_t kb = static_cast<int64_t>(s) * BK;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (u < lps) issue_from_dst(src[u] + kb, stg + dst[u]);
-        if (s == 0) {   // the tile's lhs row scales (rows past the tile repeat its last)
-          const int r = min(w4 * 64 + lane, rows_here - 1);
-          __builtin_amdgcn_global_load_lds(ls + (ls_per_row ? row0 + r : 0), (lds_void*)(ls_tile + w4 * 64), 4, 0, 0);
-        }
-      }
-    }
-
-    for (int kt = 0; kt < KT; ++kt) {
-      // this wave's loads of step kt have landed once at most the loads of the
-      // later stages already issued are outstanding
-      const int later = min(NST - 2, KT - 1 - kt);
-      if (later == 2) {
-        if (half) __builtin_amdgcn_s_waitcnt(waitcnt_vm(6)); else __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
-      } else if (later == 1) {
-        if (half) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3)); else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
-      } else {
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      }
-      step_barrier();
-      const int ks = kt + NST - 1;
-      const bool more = ks < KT;
-      const int64_t kb_next = static_cast<int64_t>(ks) * BK;
-      uint8_t* nxt = smem + (ks & (NST - 1)) * STAGE;
-      const uint8_t* As = smem + (kt & (NST - 1)) * STAGE;
-      const uint8_t* Bs = As + bm_t * BK;
-      const uint32_t as_addr = lds_addr(As) + rbase * BK, bs_addr = lds_addr(Bs) + cbase * BK;
-      v8i b0, b1, a_first;
-      frag3(bs_addr, bs_addr + 32 * BK, as_addr, f_lo, f_hi, b0, b1, a_first);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (half && i >= 2) break;
-        const v8i a = i == 0 ? a_first : frag1(as_addr + 32 * BK * i, f_lo, f_hi);
-        if (more) {
-          if (half) {
-            if (i == 0) { issue_from_dst(src[0] + kb_next, nxt + dst[0]); issue_from_dst(src[1] + kb_next, nxt + dst[1]); }
-            if (i == 1) issue_from_dst(src[2] + kb_next, nxt + dst[2]);
-          } else {
-            issue_from_dst(src[i] + kb_next, nxt + dst[i]);
-          }
-        }
-        acc[i][0] = mfma32(b0, a, acc[i][0]);
-        acc[i][1] = mfma32(b1, a, acc[i][1]);
-      }
-    }
-
-    // ---- epilogue: out = ls[row] * (acc * rs[col]), bf16, staged in LDS
-    __syncthreads();      // every wave is done with the operand stages
-    uint16_t* st = reinterpret_cast<uint16_t*>(smem);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = cbase + 32 * j + 8 * q + 4 * h;          // four consecutive columns
-        const int64_t cg = col0 + c;
-        float4 cs;
-        if (ncol_blk == 1)
-          cs = *reinterpret_cast<const float4*>(rs_g + cg);
-        else
-          cs = make_float4(rs_g[static_cast<uint32_t>(cg) / ncol_blk], rs_g[static_cast<uint32_t>(cg + 1) / ncol_blk],
-                           rs_g[static_cast<uint32_t>(cg + 2) / ncol_blk], rs_g[static_cast<uint32_t>(cg + 3) / ncol_blk]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (half && i >= 2) break;
-          const int r = rbase + 32 * i + l32;
-          const float l = ls_tile[r];
-          const v16f& v = acc[i][j];
-          const uint32_t lo = pack_bf16x2(l * (v[4 * q] * cs.x), l * (v[4 * q + 1] * cs.y));
-          const uint32_t hi = pack_bf16x2(l * (v[4 * q + 2] * cs.z), l * (v[4 * q + 3] * cs.w));
-          *reinterpret_cast<uint2*>(st + r * OS + c) = make_uint2(lo, hi);
-        }
-      }
-    }
-    __syncthreads();
-    uint16_t* o = static_cast<uint16_t*>(out);
-    const int chunks = bm_t * (BN / 8);
-#pragma unroll 4
-    for (int id = tid; id < chunks; id += THREADS) {
-      const int r = id >> 5, c = id & 31;
-      if (r < rows_here) {
-        const uint4 v = *reinterpret_cast<const uint4*>(st + r * OS + c * 8);
-        *reinterpret_cast<uint4*>(o + (row0 + r) * N + col0 + c * 8) = v;
-      }
-    }
-  }
-  // rows [n, M) are zero
-  const int64_t zero_rows = M - n_rows;
-  if (zero_rows > 0) {
-    const int64_t total_chunks = zero_rows * N / 8;
-    uint4* base = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + n_rows * N);
-    for (int64_t c = static_cast<int64_t>(blockIdx.x) * THREADS + tid; c < total_chunks;
-         c += static_cast<int64_t>(gridDim.x) * THREADS)
-      base[c] = make_uint4(0, 0, 0, 0);
-  }
-}
-
 // Launch one configuration: persistent grid of (workgroups per CU) x CUs.
 template <class C, bool TRANS, bool KBLOCKS, bool OUT_BF16, bool I8>
 hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const uint8_t* rhs, const float* rs, int Kb,
@@ -1725,15 +1458,6 @@ hipError_t launch_cfg(const uint8_t* lhs, const float* ls, int per_row, const ui
   int64_t grid = static_cast<int64_t>(per_cu) * tile::num_cus();
   if (ub < grid) grid = ub;
   if (grid < 8) grid = 8;
-  if constexpr (TRANS && !KBLOCKS && OUT_BF16 && !I8 && MOE_GMM256 != 0) {
-    // measured: faster from 1536 output columns on; with fewer n-tiles the
-    // 256 x 128 tiles balance better over the CUs
-    if (N % g256::BN == 0 && N >= 1536) {
-      gmm256_kernel<true><<<static_cast<unsigned>(grid), g256::THREADS, 0, st>>>(lhs, ls, per_row, rhs, rs, Kb, Nb, gs,
-                                                                                g0, El, M, K, N, out, err);
-      return hipGetLastError();
-    }
-  }
   if constexpr (MOE_GMM_STREAM != 0 && !I8) {
     if (El <= kStreamMaxLocal) {
       gmm_stream_kernel<C, TRANS, KBLOCKS, OUT_BF16, false>

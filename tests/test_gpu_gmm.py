@@ -203,12 +203,12 @@ def test_gmm_ragged_groups_and_zero_tail(sizes):
     ([2, 0, 700, 64, 255], 2048, "coarse", False),
     ([1, 1, 1, 1], 1536, "tensor", True),
 ])
-def test_gmm_256_tiles_ragged(sizes, N, nb, static):
-    """The 256 x 256-tile kernel (weights [E, N, K], N >= 1536, bf16 out):
-    empty groups, one-row groups, remainders of at most 128 rows (half
-    tiles) and of more (a full tile with rows not stored), tiles reaching
-    past the buffer, and the zero rows after the last group -- against the
-    oracle over the whole output (its float32 twin runs the 256 x 128 kernel)."""
+def test_gmm_wide_outputs_ragged(sizes, N, nb, static):
+    """Weights [E, N, K] with 1536 or more output columns, bf16 out and
+    per-channel, coarse or tensor weight scales: empty groups, one-row
+    groups, groups of 129..144 rows (one absorbing row block) and of more,
+    tiles reaching past the buffer, and the zero rows after the last group --
+    against the oracle over the whole output."""
     rng = np.random.default_rng(sum(sizes) + N)
     E = len(sizes)
     gs = np.array(sizes, np.int32)
@@ -223,7 +223,7 @@ def test_gmm_256_tiles_ragged(sizes, N, nb, static):
         ls, mode = np.array([0.25], np.float32), m.MOE_SCALE_TENSOR_STATIC
     else:
         ls, mode = rng.uniform(0.01, 1, M).astype(np.float32), m.MOE_SCALE_ROW_DYNAMIC
-    _check_gmm_full(lhs, ls, mode, w, rs, gs, E, 0, E, 1, f"256 tiles {sizes} N={N} {nb}", hw=True)
+    _check_gmm_full(lhs, ls, mode, w, rs, gs, E, 0, E, 1, f"wide outputs {sizes} N={N} {nb}", hw=True)
 
 
 @pytest.mark.parametrize("N,nb,Kb", [(512, "block", 2), (384, "channel", 1), (256, "block", 3), (512, "block64", 4),
@@ -292,7 +292,7 @@ def test_gmm_split_last_round(sizes, N, blockwise):
               model=lambda idx: gmm_samples(lhs, ls, wq, ws_, gs, 0, E, idx // N, idx % N))
 
 
-def test_gmm_256_tiles_local_slice():
+def test_gmm_wide_outputs_local_slice():
     rng = np.random.default_rng(21)
     E, g0, El = 10, 3, 4
     gs = rng.integers(0, 300, E).astype(np.int32)
@@ -302,7 +302,7 @@ def test_gmm_256_tiles_local_slice():
     w = rng.integers(0, 0x70, (El, K, N)).astype(np.uint8)
     rs = rng.uniform(0.01, 0.1, (El, 1, 1, N)).astype(np.float32)
     ls = rng.uniform(0.01, 1, n + 10).astype(np.float32)
-    _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, g0, El, 1, "256 tiles local slice", hw=True)
+    _check_gmm_full(lhs, ls, m.MOE_SCALE_ROW_DYNAMIC, w, rs, gs, E, g0, El, 1, "wide outputs local slice", hw=True)
 
 
 def test_gmm_local_slice_and_no_local_experts():
@@ -439,7 +439,7 @@ def test_gmm_group_sizes_summing_past_2_31_stay_in_bounds(N, out_dtype):
     """Three groups of 2^30 rows against a 1000-row buffer: the row table
     saturates at the buffer (group 0 gets every row, the others none), the
     rows flag is raised, and nothing past the output's last row is written
-    (256 x 128 tiles with float32 out; 256 x 256 tiles with bf16 out)."""
+    (float32 and bf16 out)."""
     rng = np.random.default_rng(N)
     M, K, E = 1000, 256, 3
     lhs = rng.integers(0, 0x70, (M, K)).astype(np.uint8)
