@@ -510,27 +510,17 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
   const int ul = lft > 0 ? xj % lft : 0, up = lft > 0 ? xj / lft : 0;   // this workgroup's leftover tile, part
   const int n_items = n_full + (split_s >= 2 && xj < lft * split_s ? 1 : 0);
 
-  // the tile loop, compiled once with a split part and once without, so the
-  // workgroups of an XCD without a split round run a loop that holds none of
-  // the split's state
-  auto tile_loop = [&](auto split_c) {
-  constexpr bool SPLIT = decltype(split_c)::value;
-  for (int item = 0; item < n_items; ++item) {
-    const bool psplit = SPLIT && item == n_full;               // a part of a split tile
-    const int t = psplit ? lbase + ul : first + item * step;
-    const int kbeg = psplit ? (up * KT) / split_s : 0;
-    const int kend = psplit ? ((up + 1) * KT) / split_s : KT;
-    // ---- decode tile t of the group table (tiles of a group: n-tile major,
-    // m-tiles fastest; a short remainder of at most BM/2 rows is covered by
-    // wide tiles of two n-tiles each, placed after the two n-tiles' full
-    // m-tiles so they reuse the same weight columns from L2)
-    const int g = BATCH ? t / (MTb * NT) : find_group(gt, El, t);
+  // decode tile t of the group table: its group, n-tile, first row, rows and kind (tiles of a group:
+  // n-tile major, m-tiles fastest; a short remainder of at most BM/2 rows is covered by wide tiles of two
+  // n-tiles each, placed after the two n-tiles' full m-tiles so they reuse the same weight columns from L2)
+  auto decode = [&](int t, int& g, int& nt, int64_t& row0, int& rows_here, bool& wide, int& m_g) {
+    g = BATCH ? t / (MTb * NT) : find_group(gt, El, t);
     const int local = BATCH ? t - g * (MTb * NT) : t - gt.tiles_off[g];
-    const int m_g = gt.rows_off[g + 1] - gt.rows_off[g];
+    m_g = gt.rows_off[g + 1] - gt.rows_off[g];
     const int full = m_g / BM, rem = m_g - full * BM;
-    int nt, roff;                 // the tile's n-tile and its first row inside the group
+    int roff;                     // the tile's first row inside the group
     int wrows = BM / 2;           // rows of a wide tile (ABS: up to BM/2 + XROWS)
-    bool wide = false;
+    wide = false;
     if (BATCH) {
       nt = local / MTb;
       roff = (local - nt * MTb) * BM;
@@ -570,8 +560,50 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
         roff = (local - npair * pairblk) * BM;
       }
     }
-    const int64_t row0 = BATCH ? static_cast<int64_t>(roff) : gt.rows_off[g] + static_cast<int64_t>(roff);
-    const int rows_here = BATCH ? BM : min(wide ? wrows : BM, m_g - roff);
+    row0 = BATCH ? static_cast<int64_t>(roff) : gt.rows_off[g] + static_cast<int64_t>(roff);
+    rows_here = BATCH ? BM : min(wide ? wrows : BM, m_g - roff);
+  };
+  // ABS: the tiles this workgroup runs, decoded up front into LDS by one thread each (a search of the
+  // group table and a few integer divisions that would otherwise sit between every two tiles); items past
+  // the table's end decode inline
+  constexpr int kDesc = ABS ? 96 : 1;
+  __shared__ int4 tdesc[kDesc];       // {first row, n-tile, group, rows | wide << 16}
+  if constexpr (ABS) {
+    for (int i = tid; i < min(n_items, kDesc); i += G_THREADS) {
+      const int t = split_s >= 2 && i == n_full ? lbase + ul : first + i * step;
+      int g, nt, rh, mg;
+      int64_t r0;
+      bool wd;
+      decode(t, g, nt, r0, rh, wd, mg);
+      tdesc[i] = make_int4(static_cast<int>(r0), nt, g, rh | (wd ? 1 << 16 : 0));
+    }
+    __syncthreads();
+  }
+
+  // the tile loop, compiled once with a split part and once without, so the
+  // workgroups of an XCD without a split round run a loop that holds none of
+  // the split's state
+  auto tile_loop = [&](auto split_c) {
+  constexpr bool SPLIT = decltype(split_c)::value;
+  for (int item = 0; item < n_items; ++item) {
+    const bool psplit = SPLIT && item == n_full;               // a part of a split tile
+    const int t = psplit ? lbase + ul : first + item * step;
+    const int kbeg = psplit ? (up * KT) / split_s : 0;
+    const int kend = psplit ? ((up + 1) * KT) / split_s : KT;
+    int g, nt, rows_here, m_g = 0;
+    int64_t row0;
+    bool wide;
+    if (ABS && item < kDesc) {    // decoded up front
+      const int4 dsc = tdesc[item];
+      row0 = __builtin_amdgcn_readfirstlane(dsc.x);
+      nt = __builtin_amdgcn_readfirstlane(dsc.y);
+      g = __builtin_amdgcn_readfirstlane(dsc.z);
+      const int f = __builtin_amdgcn_readfirstlane(dsc.w);
+      rows_here = f & 0xffff;
+      wide = (f >> 16) & 1;
+    } else {
+      decode(t, g, nt, row0, rows_here, wide, m_g);
+    }
     // ABS: this tile carries rows past BM/2 (uniform: keeps its branches scalar)
     const bool ab = ABS && __builtin_amdgcn_readfirstlane(wide && rows_here > BM / 2 ? 1 : 0) != 0;
     const int64_t col0 = static_cast<int64_t>(nt) * BN;
