@@ -403,15 +403,17 @@ def backward_path(seed=None):
     from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate
     cfg = CONFIGS[5]
     data = generate(cfg, seed=seed)
-    p = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE)
+    # X: the [T, H] codes, the sort's metadata, then the codes gathered straight into the weight-gradient
+    # product's transposed layout (no sorted rows, no transpose pass of X)
+    p = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, fused_quantize=False, transposed_x=True)
     del data
     return p
 
 
 def secondary_backward(steps, warmup, nsets=3):
     """Config 5: the backward of an up projection (T=8192 H=4096 E=64 top-4
-    I=1536, static X and W scales): dX = gmm(dY, W^T), dW = tgmm(X_sorted, dY)
-    -- eager per-call times, one graph-replayed set, then ``nsets`` rotating sets."""
+    I=1536, static X and W scales): dX = gmm(dY, W^T), dW = tgmm(X_sorted, dY) with X gathered into the
+    product's transposed layout -- eager per-call times, one graph-replayed set, then ``nsets`` rotating sets."""
     path = backward_path()
     cfg = path.cfg
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I

@@ -387,6 +387,62 @@ int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t lhs_scale_l
                  void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_tgmm_xt_cols -- columns (host out `cols`) of the transposed operand
+ * layout that moe_sort_gather_transposed writes and moe_tgmm_fp8_xt reads,
+ * for M local rows and E experts: 256 * ceil((M + 128 E) / 256).
+ * MOE_ERR_SHAPE for M < 0 or E outside 1..1024.
+ */
+int moe_tgmm_xt_cols(int64_t M, int32_t E, int64_t* cols);
+
+/*
+ * moe_sort_gather_transposed -- the sort's row gather ("Quantize activations
+ * before EP all gather": the fp8 token rows are gathered by the sorted token
+ * indices into this shard's window) written straight into the layout the
+ * weight-gradient product contracts over (tgmm2 of "Support quantization for
+ * tokamax gmm v2"): the rows of each local group become a contraction axis
+ * of their own.  For local group g with sorted rows rows_off[g] ..
+ * rows_off[g] + m_g - 1 of the window and padded start P_g = 128 *
+ * sum_{h<g} ceil(m_h / 128):
+ *   xt[c, P_g + i] = code of x[perm[start + rows_off[g] + i] / k, c]   (i < m_g)
+ *   xt[c, P_g + i] = 0                  (m_g <= i < 128 * ceil(m_g / 128))
+ * with start = sum of group_sizes[0 .. group_offset-1] (the window's first
+ * slot); columns past the last group's padded end are not written.
+ *
+ *   x        [T, H]: e4m3fn codes (x_dtype MOE_E4M3FN, e.g. from
+ *            moe_quantize_rows with a tensor scale), or bf16 rows (MOE_BF16)
+ *            quantized here with the static scale static_scale (> 0, finite)
+ *            exactly as moe_quantize_rows(MOE_SCALE_TENSOR_STATIC) codes them.
+ *   perm, group_sizes, E, group_offset, num_local_experts: as written by
+ *            moe_sort_by_expert for the same routing (T*k slots, top-k = k).
+ *   M        local rows of the weight-gradient call (rows of its dY).
+ *   xt       [H, moe_tgmm_xt_cols(M, E)] bytes, row-major.
+ *   scale_out optional device float [1]: receives static_scale (MOE_BF16).
+ *   ws       workspace of at least 256 bytes (the error word).
+ * H a multiple of 256 (MOE_ERR_UNSUPPORTED otherwise), 1 <= k <= 64.  A
+ * source index outside the buffers is clamped (no access leaves them).
+ * Errors: MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_NULL, MOE_ERR_WORKSPACE.
+ */
+int moe_sort_gather_transposed(const void* x, int x_dtype, float static_scale, int64_t T, int32_t k,
+                               int64_t H, const int32_t* perm, const int32_t* group_sizes, int32_t E,
+                               int32_t group_offset, int32_t num_local_experts, int64_t M, uint8_t* xt,
+                               float* scale_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_tgmm_fp8_xt -- moe_tgmm_fp8 with its lhs already in the transposed
+ * layout of moe_sort_gather_transposed: xt [K, moe_tgmm_xt_cols(M, E)]
+ * (column P_g + i = row rows_off[g] + i of the sorted lhs, zeros in each
+ * group's padding).  Same result as moe_tgmm_fp8 on the sorted rows, bit for
+ * bit.  rhs [M, N] as there.  K a multiple of 256 and N of 128
+ * (MOE_ERR_UNSUPPORTED otherwise).  ws: at least 256 + N * cols bytes
+ * (moe_workspace_bytes(MOE_OP_TGMM, M, K, N, E) is enough).  Other arguments
+ * and errors as in moe_tgmm_fp8.
+ */
+int moe_tgmm_fp8_xt(const uint8_t* xt, const float* lhs_scale, int32_t lhs_scale_len, const uint8_t* rhs,
+                    const float* rhs_scale, int32_t rhs_scale_len, const int32_t* group_sizes, int32_t E,
+                    int32_t group_offset, int32_t num_local_experts, int64_t M, int64_t K, int64_t N,
+                    int out_dtype, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_gather_reduce -- un-sort plus top-k weighted combine, the ragged
  * gather-reduce of "Quantize activations before EP all gather" (review
  * comments on ragged_gather_reduce_v2.py: rows are reduced over a valid-rows

@@ -50,6 +50,11 @@ SIGNATURES = {
                         ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_tgmm_fp8": (_I, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                           ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
+    "moe_tgmm_xt_cols": (_I, [_I64, ctypes.c_int32, _P]),
+    "moe_sort_gather_transposed": (_I, [_P, _I, _F, _I64, ctypes.c_int32, _I64, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, _I64, _P, _P, _P, _SZ, _P]),
+    "moe_tgmm_fp8_xt": (_I, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_gather_reduce": (_I, [_P, _I, _P, _P, _I64, ctypes.c_int32, _I64, _I, _P, _P]),
     "moe_gather_reduce_backward": (_I, [_P, _P, _P, _P, _I64, ctypes.c_int32, _I64, _P, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, _I64, _P, _P, _P, _P, _P, _P]),
@@ -214,6 +219,28 @@ def moe_gmm_i8(lhs, lhs_scale, lhs_scale_mode, rhs, rhs_scale, Kb, Nb, transpose
 def moe_tgmm_fp8(lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, group_sizes, E, group_offset,
                  num_local_experts, M, K, N, out_dtype, out, ws, stream=None):
     return _call("moe_tgmm_fp8", _ptr(lhs), _ptr(lhs_scale), lhs_scale_len, _ptr(rhs), _ptr(rhs_scale),
+                 rhs_scale_len, _ptr(group_sizes), E, group_offset, num_local_experts, M, K, N, out_dtype,
+                 _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def tgmm_xt_cols(M, E):
+    out = ctypes.c_int64(0)
+    st = load_library().moe_tgmm_xt_cols(M, E, ctypes.byref(out))
+    if st != MOE_OK:
+        raise MoeError("moe_tgmm_xt_cols", st, status_string(st))
+    return out.value
+
+
+def moe_sort_gather_transposed(x, x_dtype, static_scale, T, k, H, perm, group_sizes, E, group_offset,
+                               num_local_experts, M, xt, scale_out, ws, stream=None):
+    return _call("moe_sort_gather_transposed", _ptr(x), x_dtype, float(static_scale), T, k, H, _ptr(perm),
+                 _ptr(group_sizes), E, group_offset, num_local_experts, M, _ptr(xt), _ptr(scale_out), _ptr(ws),
+                 _nbytes(ws), _stream(stream))
+
+
+def moe_tgmm_fp8_xt(xt, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, group_sizes, E, group_offset,
+                    num_local_experts, M, K, N, out_dtype, out, ws, stream=None):
+    return _call("moe_tgmm_fp8_xt", _ptr(xt), _ptr(lhs_scale), lhs_scale_len, _ptr(rhs), _ptr(rhs_scale),
                  rhs_scale_len, _ptr(group_sizes), E, group_offset, num_local_experts, M, K, N, out_dtype,
                  _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
 

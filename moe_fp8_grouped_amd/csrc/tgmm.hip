@@ -10,6 +10,7 @@
 // tiles); persistent workgroups take tiles from an XCD-contiguous range.
 // Bound by the float32 output write (E_loc * K * N * 4 bytes).
 #include "tile_common.hpp"
+#include "quant_common.hpp"
 
 namespace moe {
 namespace {
@@ -139,15 +140,42 @@ struct TItem {
   int keep;          // bit u: this thread's load u holds data (else the piece is zero)
 };
 
+// GATHER: where row i of local group g comes from.
+//   0  A holds the sorted rows: row rows_off[g] + i of A [rows, C] (e4m3 codes).
+//   1  The sort's gather in this layout: the row is source token
+//      perm[start + rows_off[g] + i] / k of A = xq [T, C] (e4m3 codes), start
+//      = the group sizes before g0 (the window's first slot).
+//   2  As 1 from bf16 rows A = x [T, C], quantized on the way with the static
+//      scale s: e4m3(clip(x / s)), the row quantizer's codes.
+// Token indices outside [0, T) and slots outside perm are clamped (their
+// columns are those of a valid row; no access leaves a buffer).
+template <int GATHER>
 __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __restrict__ A, int64_t C,
                                                                const int32_t* __restrict__ group_sizes, int g0,
                                                                int El, int64_t max_rows, int64_t Mpad,
-                                                               uint8_t* __restrict__ AT, int32_t* __restrict__ err) {
+                                                               uint8_t* __restrict__ AT, int32_t* __restrict__ err,
+                                                               const int32_t* __restrict__ perm, int k, int64_t T,
+                                                               float static_scale) {
   constexpr int IR = 128;                     // rows per item
+  constexpr int ES = GATHER == 2 ? 2 : 1;     // source bytes per element
+  constexpr int NV = GATHER == 2 ? 8 : 4;     // 16-byte loads per thread and item
   __shared__ GroupTable gt;
   __shared__ int tmp[kMaxLocal];
   __shared__ __attribute__((aligned(16))) uint8_t tl[IR * 128];
+  __shared__ long long start_s;
   build_groups(group_sizes, g0, El, max_rows, 1, 128, err, gt, tmp, false);
+  if (GATHER) {   // the window's first slot: the sizes of the groups before g0 (negative ones count as 0)
+    if (threadIdx.x < 64) {
+      long long sum = 0;
+      for (int e = threadIdx.x; e < g0; e += 64) sum += max(group_sizes[e], 0);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (threadIdx.x == 0) start_s = sum;
+    }
+    __syncthreads();
+  }
+  const long long start = GATHER ? start_s : 0;
+  const long long nslots = static_cast<long long>(T) * k;
   const int64_t P = static_cast<int64_t>(gt.tiles_off[El]) * 128;    // padded rows
   const int64_t cblocks = C / 64;
   const int64_t cq = (cblocks + 1) / 2;
@@ -155,44 +183,93 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
   const int tid = threadIdx.x;
   const int lr = tid >> 3, pc = tid & 7;       // load: rows lr + 32 u, 16-byte piece pc of 128 bytes
   const int rg = tid & 7, cg = tid >> 3;       // transpose: 16-row group rg, 4-column group cg
+  const RowDiv div(static_scale);
 
-  // issue the loads of item `it`; every load is issued (a piece with no data
-  // reads A's first bytes and is zeroed when staged), so the loads carry no
-  // branches and stay in flight
-  auto fetch = [&](int64_t it, TItem& I, uint4 (&v)[4]) {
+  // item `it`: its first padded row and column block, and where its rows sit
+  struct Loc { int64_t p0, cb0, i0; int nb, row0, m_g; };
+  auto locate = [&](int64_t it) {
+    Loc L;
     const int64_t pb = it / cq, q = it - pb * cq;
-    I.p0 = pb * IR;
-    I.cb0 = q * 2;
-    I.nb = static_cast<int>(cblocks - I.cb0 < 2 ? cblocks - I.cb0 : 2);
+    L.p0 = pb * IR;
+    L.cb0 = q * 2;
+    L.nb = static_cast<int>(cblocks - L.cb0 < 2 ? cblocks - L.cb0 : 2);
     // the group holding padded rows p0 .. p0 + 127; the item is the
     // workgroup's, so the search runs on scalars
     int lo = 0, hi = El - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[mid])) * 128 <= I.p0) lo = mid;
+      if (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[mid])) * 128 <= L.p0) lo = mid;
       else hi = mid - 1;
     }
-    const int g = lo;
-    const int row0 = __builtin_amdgcn_readfirstlane(gt.rows_off[g]);
-    const int64_t i0 = I.p0 - static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[g])) * 128;
-    const int m_g = __builtin_amdgcn_readfirstlane(gt.rows_off[g + 1]) - row0;
+    L.row0 = __builtin_amdgcn_readfirstlane(gt.rows_off[lo]);
+    L.i0 = L.p0 - static_cast<int64_t>(__builtin_amdgcn_readfirstlane(gt.tiles_off[lo])) * 128;
+    L.m_g = __builtin_amdgcn_readfirstlane(gt.rows_off[lo + 1]) - L.row0;
+    return L;
+  };
+  // GATHER: the source tokens of the thread's four rows of item `it` (-1: past the group), loaded one item
+  // ahead of their use so that the row loads do not wait for them
+  auto load_tok = [&](int64_t it, int (&tk)[4]) {
+    if (!GATHER) return;
+    const Loc L = locate(it);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t r = L.i0 + lr + 32 * u;
+      long long slot = start + L.row0 + r;
+      slot = slot < nslots ? slot : nslots - 1;
+      tk[u] = r < L.m_g ? perm[slot] : -1;
+    }
+  };
+  // issue the loads of item `it`; every load is issued (a piece with no data
+  // reads A's first bytes and is zeroed when staged), so the loads carry no
+  // branches and stay in flight
+  auto fetch = [&](int64_t it, TItem& I, const int (&tk)[4], uint4 (&v)[NV]) {
+    const Loc L = locate(it);
+    I.p0 = L.p0;
+    I.cb0 = L.cb0;
+    I.nb = L.nb;
     const bool col_ok = (pc >> 2) < I.nb;
-    const uint8_t* src = A + (row0 + i0 + lr) * C + I.cb0 * 64 + 16 * pc;
     I.keep = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const bool ok = col_ok && i0 + lr + 32 * u < m_g;
+      const int64_t r = L.i0 + lr + 32 * u;
+      const bool ok = col_ok && r < L.m_g;
+      int64_t src_row = L.row0 + r;
+      if (GATHER) {
+        const int64_t tok = tk[u] >= 0 ? tk[u] / k : 0;
+        src_row = tok < T ? tok : T - 1;
+      }
       I.keep |= ok ? 1 << u : 0;
-      v[u] = *reinterpret_cast<const uint4*>(ok ? src + 32 * u * C : A);
+      const uint8_t* src = A + (src_row * C + I.cb0 * 64 + 16 * pc) * ES;
+      if (ES == 1) {
+        v[u] = *reinterpret_cast<const uint4*>(ok ? src : A);
+      } else {
+        v[2 * u] = *reinterpret_cast<const uint4*>(ok ? src : A);
+        v[2 * u + 1] = *reinterpret_cast<const uint4*>(ok ? src + 16 : A);
+      }
     }
   };
   // stage item I's rows in LDS, transpose, store its columns
-  auto put = [&](const TItem& I, const uint4 (&v)[4]) {
+  auto put = [&](const TItem& I, const uint4 (&v)[NV]) {
     lds_barrier();                            // the previous item's reads of tl are done
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = lr + 32 * u;
-      const uint4 w = (I.keep >> u) & 1 ? v[u] : make_uint4(0, 0, 0, 0);
+      uint4 w;
+      if (ES == 1) {
+        w = v[u];
+      } else {   // 16 bf16 values to 16 codes
+        float f[16];
+        const uint32_t ww[8] = {v[2 * u].x, v[2 * u].y, v[2 * u].z, v[2 * u].w,
+                                v[2 * u + 1].x, v[2 * u + 1].y, v[2 * u + 1].z, v[2 * u + 1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          f[2 * i] = __uint_as_float(ww[i] << 16);
+          f[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+        }
+        const uint2 c0 = codes8(f, div), c1 = codes8(f + 8, div);
+        w = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      }
+      w = (I.keep >> u) & 1 ? w : make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(tl + r * 128 + 16 * (pc ^ ((r >> 4) & 7))) = w;
     }
     lds_barrier();
@@ -205,8 +282,8 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
       for (int b = 0; b < 4; ++b) transpose4x4(d + 4 * b, e[b]);
       uint8_t* dst = AT + (I.cb0 * 64 + 4 * cg) * Mpad + I.p0 + 16 * rg;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<uint4*>(dst + k * Mpad) = make_uint4(e[0][k], e[1][k], e[2][k], e[3][k]);
+      for (int kk = 0; kk < 4; ++kk)
+        *reinterpret_cast<uint4*>(dst + kk * Mpad) = make_uint4(e[0][kk], e[1][kk], e[2][kk], e[3][kk]);
     }
   };
 
@@ -216,20 +293,28 @@ __global__ __launch_bounds__(256) void transpose_groups_kernel(const uint8_t* __
   const int64_t G = gridDim.x;
   int64_t it = blockIdx.x;
   if (it >= items) return;
+  auto next = [&](int64_t i) { return i + G < items ? i + G : items - 1; };
   TItem ia, ib;
-  uint4 va[4], vb[4];
-  fetch(it, ia, va);
+  uint4 va[NV], vb[NV];
+  int ta[4] = {0, 0, 0, 0}, tb[4] = {0, 0, 0, 0};
+  load_tok(it, ta);
+  fetch(it, ia, ta, va);
+  load_tok(next(it), tb);
   for (;;) {
-    fetch(it + G < items ? it + G : items - 1, ib, vb);
+    fetch(next(it), ib, tb, vb);
+    load_tok(next(next(it)), ta);
     put(ia, va);
     it += G;
     if (it >= items) break;
-    fetch(it + G < items ? it + G : items - 1, ia, va);
+    fetch(next(it), ia, ta, va);
+    load_tok(next(next(it)), tb);
     put(ib, vb);
     it += G;
     if (it >= items) break;
   }
 }
+
+__global__ void write_scale_kernel(float* scale, float v) { *scale = v; }
 
 }  // namespace
 
@@ -284,9 +369,11 @@ extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t 
     uint8_t* DT = XT + K * Mpad;
     const unsigned tgrid = static_cast<unsigned>(4 * moe::tile::num_cus());
     if (M > 0) {
-      moe::transpose_groups_kernel<<<tgrid, 256, 0, st>>>(lhs, K, group_sizes, group_offset, El, M, Mpad, XT, err);
+      moe::transpose_groups_kernel<0><<<tgrid, 256, 0, st>>>(lhs, K, group_sizes, group_offset, El, M, Mpad, XT, err,
+                                                             nullptr, 1, 0, 1.0f);
       MOE_CHECK_LAUNCH();
-      moe::transpose_groups_kernel<<<tgrid, 256, 0, st>>>(rhs, N, group_sizes, group_offset, El, M, Mpad, DT, err);
+      moe::transpose_groups_kernel<0><<<tgrid, 256, 0, st>>>(rhs, N, group_sizes, group_offset, El, M, Mpad, DT, err,
+                                                             nullptr, 1, 0, 1.0f);
       MOE_CHECK_LAUNCH();
     }
     return moe::gmm_batched_launch(XT, lhs_scale, lhs_scale_len, DT, rhs_scale, rhs_scale_len, group_sizes,
@@ -305,4 +392,84 @@ extern "C" int moe_tgmm_fp8(const uint8_t* lhs, const float* lhs_scale, int32_t 
         lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, group_sizes, group_offset, El, M, K, N, out, err);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
+}
+
+extern "C" int moe_tgmm_xt_cols(int64_t M, int32_t E, int64_t* cols) {
+  if (!cols) return MOE_ERR_NULL;
+  if (M < 0 || E <= 0 || E > 1024) return MOE_ERR_SHAPE;
+  *cols = moe::tgmm_mpad(M, E);
+  return MOE_OK;
+}
+
+extern "C" int moe_sort_gather_transposed(const void* x, int x_dtype, float static_scale, int64_t T, int32_t k,
+                                          int64_t H, const int32_t* perm, const int32_t* group_sizes, int32_t E,
+                                          int32_t group_offset, int32_t num_local_experts, int64_t M, uint8_t* xt,
+                                          float* scale_out, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || k <= 0 || k > 64 || H <= 0 || M < 0) return MOE_ERR_SHAPE;
+  if (H % 256) return MOE_ERR_UNSUPPORTED;
+  if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 ||
+      num_local_experts > moe::tile::kMaxLocal || group_offset + num_local_experts > E)
+    return MOE_ERR_SHAPE;
+  if (T * k > INT32_MAX - 1 || M > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (x_dtype != MOE_E4M3FN && x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (x_dtype == MOE_BF16 && !(static_scale > 0.0f && static_scale < 3.0e38f)) return MOE_ERR_SHAPE;
+  if (!group_sizes) return MOE_ERR_NULL;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe::tile::kHdr) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* err = static_cast<int32_t*>(ws);
+  if (scale_out && x_dtype == MOE_BF16) {
+    moe::write_scale_kernel<<<1, 1, 0, st>>>(scale_out, static_scale);
+    MOE_CHECK_LAUNCH();
+  }
+  const int El = num_local_experts;
+  if (El == 0 || M == 0 || T == 0) return MOE_OK;
+  if (!x || !perm || !xt) return MOE_ERR_NULL;
+  const int64_t Mpad = moe::tgmm_mpad(M, E);
+  const unsigned tgrid = static_cast<unsigned>(4 * moe::tile::num_cus());
+  const uint8_t* src = static_cast<const uint8_t*>(x);
+  if (x_dtype == MOE_E4M3FN)
+    moe::transpose_groups_kernel<1><<<tgrid, 256, 0, st>>>(src, H, group_sizes, group_offset, El, M, Mpad, xt, err,
+                                                           perm, k, T, 1.0f);
+  else
+    moe::transpose_groups_kernel<2><<<tgrid, 256, 0, st>>>(src, H, group_sizes, group_offset, El, M, Mpad, xt, err,
+                                                           perm, k, T, static_scale);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" int moe_tgmm_fp8_xt(const uint8_t* xt, const float* lhs_scale, int32_t lhs_scale_len, const uint8_t* rhs,
+                               const float* rhs_scale, int32_t rhs_scale_len, const int32_t* group_sizes, int32_t E,
+                               int32_t group_offset, int32_t num_local_experts, int64_t M, int64_t K, int64_t N,
+                               int out_dtype, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || K <= 0 || N <= 0) return MOE_ERR_SHAPE;
+  if (K % 256 || N % 128) return MOE_ERR_UNSUPPORTED;
+  if (E <= 0 || E > 1024 || group_offset < 0 || num_local_experts < 0 ||
+      num_local_experts > moe::tile::kMaxLocal || group_offset + num_local_experts > E)
+    return MOE_ERR_SHAPE;
+  if (M > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (lhs_scale_len != 1 && lhs_scale_len != K) return MOE_ERR_UNSUPPORTED;
+  if (rhs_scale_len != 1 && rhs_scale_len != N) return MOE_ERR_UNSUPPORTED;
+  if (out_dtype == MOE_DTYPE_DEFAULT) out_dtype = MOE_F32;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  const int El = num_local_experts;
+  if (El == 0) return MOE_OK;
+  if (!out || !group_sizes || !lhs_scale || !rhs_scale) return MOE_ERR_NULL;
+  if (M > 0 && (!xt || !rhs)) return MOE_ERR_NULL;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  const int64_t Mpad = moe::tgmm_mpad(M, E);
+  if (ws_bytes < static_cast<size_t>(moe::tile::kHdr + N * Mpad)) return MOE_ERR_WORKSPACE;
+  if (static_cast<int64_t>(El) * moe_cdiv(K, 64) * moe_cdiv(N, 64) > INT32_MAX) return MOE_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* err = static_cast<int32_t*>(ws);
+  uint8_t* DT = static_cast<uint8_t*>(ws) + moe::tile::kHdr;
+  if (M > 0) {
+    const unsigned tgrid = static_cast<unsigned>(4 * moe::tile::num_cus());
+    moe::transpose_groups_kernel<0><<<tgrid, 256, 0, st>>>(rhs, N, group_sizes, group_offset, El, M, Mpad, DT, err,
+                                                           nullptr, 1, 0, 1.0f);
+    MOE_CHECK_LAUNCH();
+  }
+  return moe::gmm_batched_launch(xt, lhs_scale, lhs_scale_len, DT, rhs_scale, rhs_scale_len, group_sizes,
+                                 group_offset, El, M, K, Mpad, N, out_dtype == MOE_BF16, out, err, st) == hipSuccess
+             ? MOE_OK : MOE_ERR_HIP;
 }

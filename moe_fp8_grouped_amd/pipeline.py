@@ -20,11 +20,12 @@ are quantized once at setup.
 import numpy as np
 import torch
 
-from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_F32, MOE_OP_GMM, MOE_OP_QUANTIZE_ROWS,
-               MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
-               MOE_SCALE_TENSOR_FROM_ROW_AMAX, MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gather_reduce_backward, moe_gmm_fp8, moe_quantize_rows,
-               moe_quantize_rows_strided, moe_quantize_sort_by_expert, moe_quantize_weights, moe_silu_mul_backward,
-               moe_sort_by_expert, moe_tgmm_fp8, workspace)
+from . import (MOE_ACT_NONE, MOE_ACT_SILU_MUL, MOE_BF16, MOE_E4M3FN, MOE_F32, MOE_OP_GATHER_REDUCE, MOE_OP_GMM,
+               MOE_OP_QUANTIZE_ROWS, MOE_OP_SORT_BY_EXPERT, MOE_OP_TGMM, MOE_SCALE_ROW_DYNAMIC, MOE_SCALE_TENSOR_DYNAMIC,
+               MOE_SCALE_TENSOR_FROM_ROW_AMAX, MOE_SCALE_TENSOR_STATIC, moe_gather_reduce, moe_gather_reduce_backward,
+               moe_gmm_fp8, moe_quantize_rows, moe_quantize_rows_strided, moe_quantize_sort_by_expert,
+               moe_quantize_weights, moe_silu_mul_backward, moe_sort_by_expert, moe_sort_gather_transposed,
+               moe_tgmm_fp8, moe_tgmm_fp8_xt, tgmm_xt_cols, workspace)
 
 
 def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
@@ -201,11 +202,15 @@ class ForwardPath:
 class BackwardPath:
     """Config-5 backward: dX = gmm(dY, W^T), dW = tgmm(X_sorted, dY)."""
 
-    def __init__(self, cfg, data, static_act, static_weight, device="cuda", dw_dtype=MOE_F32, fused_quantize=True):
+    def __init__(self, cfg, data, static_act, static_weight, device="cuda", dw_dtype=MOE_F32, fused_quantize=True,
+                 transposed_x=False):
         self.cfg, self.dev = cfg, device
         # X quantized with its static scale inside the sort's gather (True), or
         # to [T, H] codes by a pass of its own first
         self.fused_quantize = bool(fused_quantize)
+        # transposed_x: no sorted X rows at all -- the sort's metadata, then X quantized on its way into the
+        # weight-gradient product's transposed layout (moe_sort_gather_transposed), read by moe_tgmm_fp8_xt
+        self.transposed_x = bool(transposed_x)
         T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
         self.T, self.H, self.E, self.k, self.I = T, H, E, k, I
         self.M = T * k
@@ -224,7 +229,11 @@ class BackwardPath:
         self.perm = torch.empty(self.M, dtype=i32, device=device)
         self.inv_pos = torch.empty(self.M, dtype=i32, device=device)
         self.group_sizes = torch.empty(E, dtype=i32, device=device)
-        self.xs = torch.empty((self.M, H), dtype=u8, device=device)
+        if self.transposed_x:
+            self.xt = torch.empty((H, tgmm_xt_cols(self.M, E)), dtype=u8, device=device)
+            self.ws_xt = workspace(MOE_OP_GATHER_REDUCE, device=device)
+        else:
+            self.xs = torch.empty((self.M, H), dtype=u8, device=device)
         self.dyq_r = torch.empty((self.M, I), dtype=u8, device=device)
         self.dys_r = torch.empty(self.M, dtype=f32, device=device)
         self.dyq_t = torch.empty((self.M, I), dtype=u8, device=device)
@@ -239,6 +248,22 @@ class BackwardPath:
         self.ws_tgmm = workspace(MOE_OP_TGMM, self.M, H, I, E, device=device)
 
     def quantize_and_sort(self):
+        if self.transposed_x:
+            # (fused_quantize: the bf16 rows are quantized on their way into the layout; otherwise the [T, H]
+            # codes come first and the gather moves bytes)
+            moe_sort_by_expert(self.ids, self.T, self.k, self.E, self.g0, self.El, None, None, MOE_SCALE_TENSOR_STATIC,
+                               self.H, self.M, self.perm, self.inv_pos, self.group_sizes, None, None, self.ws_sort)
+            if self.fused_quantize:
+                moe_sort_gather_transposed(self.x, MOE_BF16, self.static_act, self.T, self.k, self.H, self.perm,
+                                           self.group_sizes, self.E, self.g0, self.El, self.M, self.xt, self.xscale,
+                                           self.ws_xt)
+            else:
+                moe_quantize_rows(self.x, None, MOE_ACT_NONE, self.T, self.H, MOE_SCALE_TENSOR_STATIC,
+                                  self.static_act, self.xq, self.xscale, None, None)
+                moe_sort_gather_transposed(self.xq, MOE_E4M3FN, 1.0, self.T, self.k, self.H, self.perm,
+                                           self.group_sizes, self.E, self.g0, self.El, self.M, self.xt, None,
+                                           self.ws_xt)
+            return
         if self.fused_quantize:
             moe_quantize_sort_by_expert(self.x, self.T, self.H, MOE_SCALE_TENSOR_STATIC, self.static_act, self.ids,
                                         self.k, self.E, self.g0, self.El, self.M, self.perm, self.inv_pos,
@@ -263,6 +288,10 @@ class BackwardPath:
                     self.ws_gmm)
 
     def grad_weight(self):
+        if self.transposed_x:
+            moe_tgmm_fp8_xt(self.xt, self.xscale, 1, self.dyq_t, self.dys_t, 1, self.group_sizes, self.E, self.g0,
+                            self.El, self.M, self.H, self.I, self.dw_dtype, self.dw, self.ws_tgmm)
+            return
         moe_tgmm_fp8(self.xs, self.xscale, 1, self.dyq_t, self.dys_t, 1, self.group_sizes, self.E, self.g0,
                      self.El, self.M, self.H, self.I, self.dw_dtype, self.dw, self.ws_tgmm)
 
@@ -274,9 +303,9 @@ class BackwardPath:
 
     @property
     def OUTPUTS(self):
-        return ((() if self.fused_quantize else ("xq",)) +
-                ("xscale", "perm", "inv_pos", "group_sizes", "xs", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax",
-                 "dx", "dw"))
+        x_out = (() if self.fused_quantize else ("xq",)) + (("xt",) if self.transposed_x else ("xs",))
+        return (x_out + ("xscale", "perm", "inv_pos", "group_sizes", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax",
+                         "dx", "dw"))
 
     def capture_graph(self, warmup=1):
         """Record one backward step into a HIP graph (every buffer it writes is

@@ -36,8 +36,8 @@ def test_header_declares_the_path_calls():
     names = _declared_functions()
     for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_sort_by_expert_noalloc", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
                "moe_gather_reduce_backward", "moe_silu_mul_backward", "moe_quantize_weights", "moe_quantize_rows_i8",
-               "moe_quantize_weights_i8", "moe_gmm_i8", "moe_workspace_bytes", "moe_debug_check", "moe_status_string",
-               "moe_version"]:
+               "moe_quantize_weights_i8", "moe_gmm_i8", "moe_tgmm_xt_cols", "moe_sort_gather_transposed",
+               "moe_tgmm_fp8_xt", "moe_workspace_bytes", "moe_debug_check", "moe_status_string", "moe_version"]:
         assert fn in names
 
 
@@ -196,6 +196,33 @@ def test_tgmm_and_gather_reduce_validation(lib):
     assert g(one, 0, one, one, 4, 0, 16, 0, one, None) == m.MOE_ERR_SHAPE
     assert g(None, 0, one, one, 4, 2, 16, 0, one, None) == m.MOE_ERR_NULL
     assert g(None, 0, None, None, 0, 2, 16, 0, None, None) == m.MOE_OK             # T = 0
+
+
+def test_transposed_gather_and_product_validation(lib):
+    """The transposed row gather and the weight-gradient product on its layout: the column count, and every
+    argument check that returns before a launch."""
+    assert m.tgmm_xt_cols(1000, 8) == 256 * ((1000 + 128 * 8 + 255) // 256)
+    assert m.tgmm_xt_cols(0, 1) == 256
+    with pytest.raises(m.MoeError):
+        m.tgmm_xt_cols(10, 0)
+    one = 1
+    g = lambda *a: _c(lib, "moe_sort_gather_transposed", *a)
+    # x, x_dtype, static_scale, T, k, H, perm, group_sizes, E, g0, El, M, xt, scale_out, ws, ws_bytes, stream
+    assert g(one, m.MOE_E4M3FN, 1.0, 8, 2, 384, one, one, 4, 0, 4, 16, one, None, one, 256, None) == m.MOE_ERR_UNSUPPORTED
+    assert g(one, m.MOE_E4M3FN, 1.0, 8, 0, 512, one, one, 4, 0, 4, 16, one, None, one, 256, None) == m.MOE_ERR_SHAPE
+    assert g(one, m.MOE_F32, 1.0, 8, 2, 512, one, one, 4, 0, 4, 16, one, None, one, 256, None) == m.MOE_ERR_UNSUPPORTED
+    assert g(one, m.MOE_BF16, 0.0, 8, 2, 512, one, one, 4, 0, 4, 16, one, None, one, 256, None) == m.MOE_ERR_SHAPE
+    assert g(one, m.MOE_E4M3FN, 1.0, 8, 2, 512, one, one, 4, 2, 4, 16, one, None, one, 256, None) == m.MOE_ERR_SHAPE
+    assert g(one, m.MOE_E4M3FN, 1.0, 8, 2, 512, one, None, 4, 0, 4, 16, one, None, one, 256, None) == m.MOE_ERR_NULL
+    assert g(one, m.MOE_E4M3FN, 1.0, 8, 2, 512, one, one, 4, 0, 4, 16, one, None, None, 0, None) == m.MOE_ERR_WORKSPACE
+    assert g(one, m.MOE_E4M3FN, 1.0, 8, 2, 512, one, one, 4, 0, 0, 16, one, None, one, 256, None) == m.MOE_OK  # no experts
+    t = lambda *a: _c(lib, "moe_tgmm_fp8_xt", *a)
+    # xt, ls, ls_len, rhs, rs, rs_len, group_sizes, E, g0, El, M, K, N, out_dtype, out, ws, ws_bytes, stream
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 384, 256, 1, one, one, 1 << 20, None) == m.MOE_ERR_UNSUPPORTED
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 512, 200, 1, one, one, 1 << 20, None) == m.MOE_ERR_UNSUPPORTED
+    assert t(one, one, 3, one, one, 1, one, 8, 0, 8, 100, 512, 256, 1, one, one, 1 << 20, None) == m.MOE_ERR_UNSUPPORTED
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 512, 256, 1, one, one, 256, None) == m.MOE_ERR_WORKSPACE
+    assert t(one, one, 1, one, one, 1, one, 8, 0, 0, 100, 512, 256, 1, one, one, 256, None) == m.MOE_OK  # no experts
 
 
 def test_gather_reduce_backward_validation(lib):

@@ -15,6 +15,7 @@ from oracle.quantize import (SCALE_ROW_DYNAMIC, SCALE_TENSOR_DYNAMIC, SCALE_TENS
                              quantize_weights, silu_mul_backward)
 from oracle.sort import sort_by_expert
 from tests.golden import accuracy_tables
+from tests.test_gpu_tgmm_xt import expected_xt
 from tests.mfma_model import gmm_samples, tgmm_samples
 from tests.parity import assert_bits_equal, check_bf16, check_f32, dev_bf16, dev_f32, dev_i32, host
 from workloads import CONFIGS, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, generate, scaled_config, to_bf16_bits
@@ -257,12 +258,13 @@ def test_expert_slice_pipeline_config4_stagewise():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("fused", [True, False])
-def test_backward_pipeline_config5_stagewise(fused):
+@pytest.mark.parametrize("fused,transposed", [(True, False), (False, False), (True, True)])
+def test_backward_pipeline_config5_stagewise(fused, transposed):
     cfg = CONFIGS[5]
     data = generate(cfg)
-    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, fused_quantize=fused)
-    print(f"pipeline config 5 backward fused={fused}", flush=True)
+    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, fused_quantize=fused,
+                        transposed_x=transposed)
+    print(f"pipeline config 5 backward fused={fused} transposed={transposed}", flush=True)
     path.step()
     torch.cuda.synchronize()
     # the weights: the GPU quantizer's first experts against the oracle's; the later stages take the GPU's
@@ -275,7 +277,14 @@ def test_backward_pipeline_config5_stagewise(fused):
         assert_bits_equal(host(path.xq), xq, "xq")
     assert_bits_equal(host(path.xscale), xsc, "xscale")
     srt = sort_by_expert(data["ids"], cfg.E, 0, cfg.E, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_STATIC)
-    assert_bits_equal(host(path.xs), srt["xs"], "xs")
+    if transposed:                     # X only in the weight-gradient product's layout (its padded columns)
+        want = expected_xt(srt["xs"], srt["group_sizes"], 0, cfg.E, path.M, cfg.E)
+        used = int(np.sum((srt["group_sizes"] + 127) // 128)) * 128
+        assert_bits_equal(host(path.xt)[:, :used], want[:, :used], "xt")
+        for key in ("perm", "inv_pos", "group_sizes"):
+            assert_bits_equal(host(getattr(path, key)), srt[key], key)
+    else:
+        assert_bits_equal(host(path.xs), srt["xs"], "xs")
     dq_r, ds_r, _ = quantize_rows(data["dy"], SCALE_ROW_DYNAMIC)
     dq_t, ds_t, _ = quantize_rows(data["dy"], SCALE_TENSOR_DYNAMIC)
     assert_bits_equal(host(path.dyq_r), dq_r, "dy row q")
@@ -457,17 +466,21 @@ def test_gated_ffn_backward_hip_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
-def test_backward_config5_hip_graph_replays_match_eager():
+@pytest.mark.parametrize("transposed", [False, True])
+def test_backward_config5_hip_graph_replays_match_eager(transposed):
     """The up-projection backward (reduced config-5 shape) as a HIP graph: every
     replay, with scribbled outputs and eager steps between, leaves the eager
-    step's bits in every buffer the step writes."""
+    step's bits in every buffer the step writes (of the transposed X layout:
+    the columns up to the last group's padded end, all the product reads)."""
     cfg = scaled_config(5, T=512, H=512, E=8, k=4, I=256)
     data = generate(cfg)
-    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE)
-    print("config 5 backward graph replays", flush=True)
+    path = BackwardPath(cfg, data, STATIC_ACT_SCALE, STATIC_WEIGHT_SCALE, transposed_x=transposed)
+    print(f"config 5 backward graph replays transposed={transposed}", flush=True)
     path.step()
     torch.cuda.synchronize()
-    ref = {k: getattr(path, k).clone() for k in path.OUTPUTS}
+    used = int(((host(path.group_sizes).astype(np.int64) + 127) // 128).sum()) * 128
+    view = lambda k: getattr(path, k)[:, :used] if k == "xt" else getattr(path, k)
+    ref = {k: view(k).clone() for k in path.OUTPUTS}
     path.capture_graph(warmup=1)
     for rep in range(3):
         for k in path.OUTPUTS:
@@ -476,7 +489,7 @@ def test_backward_config5_hip_graph_replays_match_eager():
         path.replay()
         torch.cuda.synchronize()
         for k in path.OUTPUTS:
-            assert torch.equal(getattr(path, k).view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+            assert torch.equal(view(k).view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
         path.step()
         torch.cuda.synchronize()
 
