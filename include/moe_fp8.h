@@ -227,6 +227,22 @@ int moe_sort_by_expert(const int32_t* expert_ids, int64_t T, int32_t k, int32_t 
                        int32_t* perm, int32_t* inv_pos, int32_t* group_sizes, uint8_t* xs,
                        float* ss, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_sort_gather_rows -- the row gather of moe_sort_by_expert alone, on the
+ * metadata an earlier moe_sort_by_expert call (with xq NULL) wrote: its
+ * inv_pos and the window header in its workspace ws.  The same bytes as the
+ * one-call sort; lets the metadata run while the token rows are still being
+ * quantized ("Quantize activations before EP all gather": the sort's order
+ * depends on the routing only, the gathered rows on the quantized tokens).
+ *   xq, xscale, xscale_mode, H, M_cap, xs, ss: as in moe_sort_by_expert.
+ *   inv_pos  [T*k] from that call; ws: that call's workspace, unchanged
+ *            since (the call must be ordered before this one on the device).
+ * Errors: MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_NULL, MOE_ERR_WORKSPACE.
+ */
+int moe_sort_gather_rows(const uint8_t* xq, const float* xscale, int xscale_mode, const int32_t* inv_pos,
+                         int64_t T, int32_t k, int64_t H, int64_t M_cap, uint8_t* xs, float* ss, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Bytes of the device array that moe_sort_by_expert_noalloc uses in place of
  * a workspace (one per GPU). */
 #define MOE_SORT_NOALLOC_SCRATCH_BYTES (2u << 20)

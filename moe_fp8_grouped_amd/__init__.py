@@ -50,6 +50,7 @@ SIGNATURES = {
                         ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
     "moe_tgmm_fp8": (_I, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                           ctypes.c_int32, _I64, _I64, _I64, _I, _P, _P, _SZ, _P]),
+    "moe_sort_gather_rows": (_I, [_P, _P, _I, _P, _I64, ctypes.c_int32, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "moe_tgmm_xt_cols": (_I, [_I64, ctypes.c_int32, _P]),
     "moe_sort_gather_transposed": (_I, [_P, _I, _F, _I64, ctypes.c_int32, _I64, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _I64, _P, _P, _P, _SZ, _P]),
@@ -221,6 +222,11 @@ def moe_tgmm_fp8(lhs, lhs_scale, lhs_scale_len, rhs, rhs_scale, rhs_scale_len, g
     return _call("moe_tgmm_fp8", _ptr(lhs), _ptr(lhs_scale), lhs_scale_len, _ptr(rhs), _ptr(rhs_scale),
                  rhs_scale_len, _ptr(group_sizes), E, group_offset, num_local_experts, M, K, N, out_dtype,
                  _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_sort_gather_rows(xq, xscale, xscale_mode, inv_pos, T, k, H, M_cap, xs, ss, ws, stream=None):
+    return _call("moe_sort_gather_rows", _ptr(xq), _ptr(xscale), xscale_mode, _ptr(inv_pos), T, k, H, M_cap,
+                 _ptr(xs), _ptr(ss), _ptr(ws), _nbytes(ws), _stream(stream))
 
 
 def tgmm_xt_cols(M, E):

@@ -710,3 +710,30 @@ extern "C" int moe_sort_by_expert_noalloc(const int32_t* expert_ids, int64_t T, 
                        perm, inv_pos, group_sizes, xs, ss, hdr, tile_hist, device_error,
                        static_cast<hipStream_t>(stream));
 }
+
+// The row gather alone, on the metadata a moe_sort_by_expert call without
+// rows left in the same workspace (its window header) and in inv_pos.
+extern "C" int moe_sort_gather_rows(const uint8_t* xq, const float* xscale, int xscale_mode, const int32_t* inv_pos,
+                                    int64_t T, int32_t k, int64_t H, int64_t M_cap, uint8_t* xs, float* ss, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  if (T < 0 || k <= 0 || k > 64 || M_cap < 0 || T * k > INT32_MAX - 1) return MOE_ERR_SHAPE;
+  if (xscale_mode != MOE_SCALE_ROW_DYNAMIC && xscale_mode != MOE_SCALE_TENSOR_DYNAMIC &&
+      xscale_mode != MOE_SCALE_TENSOR_STATIC)
+    return MOE_ERR_UNSUPPORTED;
+  if (H <= 0 || H % 16) return MOE_ERR_SHAPE;
+  const bool row_scale = xscale_mode == MOE_SCALE_ROW_DYNAMIC;
+  if (!xs && !(row_scale && ss)) return MOE_ERR_NULL;           // nothing to gather into
+  if (T > 0 && (!xq || !inv_pos)) return MOE_ERR_NULL;
+  if (row_scale && ss && T > 0 && !xscale) return MOE_ERR_NULL;
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < static_cast<size_t>(moe::kHdr)) return MOE_ERR_WORKSPACE;
+  if (M_cap == 0 && T == 0) return MOE_OK;
+  int64_t waves = T > M_cap / 4 ? T : M_cap / 4;
+  if (waves < 4) waves = 4;
+  if (waves > 65536) waves = 65536;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  moe::sort_scatter_kernel<<<static_cast<unsigned>(moe_cdiv(waves, 4)), 256, 0, st>>>(
+      xq, xscale, row_scale ? 1 : 0, inv_pos, T, k, H, M_cap, static_cast<const int32_t*>(ws), xs, ss);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

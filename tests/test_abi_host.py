@@ -36,7 +36,7 @@ def test_header_declares_the_path_calls():
     names = _declared_functions()
     for fn in ["moe_quantize_rows", "moe_quantize_rows_strided", "moe_sort_by_expert", "moe_sort_by_expert_noalloc", "moe_quantize_sort_by_expert", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gather_reduce",
                "moe_gather_reduce_backward", "moe_silu_mul_backward", "moe_quantize_weights", "moe_quantize_rows_i8",
-               "moe_quantize_weights_i8", "moe_gmm_i8", "moe_tgmm_xt_cols", "moe_sort_gather_transposed",
+               "moe_quantize_weights_i8", "moe_gmm_i8", "moe_tgmm_xt_cols", "moe_sort_gather_transposed", "moe_sort_gather_rows",
                "moe_tgmm_fp8_xt", "moe_workspace_bytes", "moe_debug_check", "moe_status_string", "moe_version"]:
         assert fn in names
 
@@ -223,6 +223,19 @@ def test_transposed_gather_and_product_validation(lib):
     assert t(one, one, 3, one, one, 1, one, 8, 0, 8, 100, 512, 256, 1, one, one, 1 << 20, None) == m.MOE_ERR_UNSUPPORTED
     assert t(one, one, 1, one, one, 1, one, 8, 0, 8, 100, 512, 256, 1, one, one, 256, None) == m.MOE_ERR_WORKSPACE
     assert t(one, one, 1, one, one, 1, one, 8, 0, 0, 100, 512, 256, 1, one, one, 256, None) == m.MOE_OK  # no experts
+
+
+def test_sort_gather_rows_validation(lib):
+    g = lambda *a: _c(lib, "moe_sort_gather_rows", *a)
+    one = 1
+    # xq, xscale, mode, inv_pos, T, k, H, M_cap, xs, ss, ws, ws_bytes, stream
+    assert g(one, one, m.MOE_SCALE_TENSOR_STATIC, one, 8, 0, 64, 16, one, None, one, 256, None) == m.MOE_ERR_SHAPE
+    assert g(one, one, m.MOE_SCALE_TENSOR_STATIC, one, 8, 2, 60, 16, one, None, one, 256, None) == m.MOE_ERR_SHAPE
+    assert g(one, one, 9, one, 8, 2, 64, 16, one, None, one, 256, None) == m.MOE_ERR_UNSUPPORTED
+    assert g(one, one, m.MOE_SCALE_TENSOR_STATIC, one, 8, 2, 64, 16, None, None, one, 256, None) == m.MOE_ERR_NULL
+    assert g(None, one, m.MOE_SCALE_TENSOR_STATIC, one, 8, 2, 64, 16, one, None, one, 256, None) == m.MOE_ERR_NULL
+    assert g(one, one, m.MOE_SCALE_TENSOR_STATIC, one, 8, 2, 64, 16, one, None, one, 8, None) == m.MOE_ERR_WORKSPACE
+    assert g(None, None, m.MOE_SCALE_TENSOR_STATIC, None, 0, 2, 64, 0, one, None, one, 256, None) == m.MOE_OK
 
 
 def test_gather_reduce_backward_validation(lib):

@@ -387,3 +387,35 @@ def test_sort_flags_rows_beyond_capacity():
     g = gpu_sort(ids, 2, 0, 2, xq, np.ones(20, np.float32), m_cap=10)
     assert g["err"] & m.MOE_DEVERR_ROWS
     assert (g["inv_pos"] >= 10).sum() == 0
+
+
+@pytest.mark.parametrize("mode", [m.MOE_SCALE_ROW_DYNAMIC, m.MOE_SCALE_TENSOR_STATIC])
+def test_sort_metadata_then_gather_rows_equals_one_call(mode):
+    """The sort's metadata (no rows) and then moe_sort_gather_rows on its
+    workspace: the rows, scales and zero tail of the one-call sort, bit for
+    bit, and the oracle's."""
+    rng = np.random.default_rng(31 + mode)
+    T, k, E, g0, El, H = 700, 4, 40, 6, 20, 512
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    xq = rng.integers(0, 256, (T, H)).astype(np.uint8)
+    xscale = (rng.uniform(0.01, 1, T) if mode == m.MOE_SCALE_ROW_DYNAMIC else np.array([0.3])).astype(np.float32)
+    M_cap = sort_by_expert(ids, E, g0, El)["n"] + 37      # the local rows and a zero tail
+    one = gpu_sort(ids, E, g0, El, xq=xq, xscale=xscale, mode=mode, m_cap=M_cap)
+    perm = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    gs = torch.empty(E, dtype=torch.int32, device="cuda")
+    xs = torch.full((M_cap, H), 0xAB, dtype=torch.uint8, device="cuda")
+    row = mode == m.MOE_SCALE_ROW_DYNAMIC
+    ss = torch.full((M_cap,), 7.0, dtype=torch.float32, device="cuda") if row else None
+    ws = m.workspace(m.MOE_OP_SORT_BY_EXPERT, T * k, 0, 0, E)
+    print(f"sort metadata then gather rows T={T} mode={mode}", flush=True)
+    m.moe_sort_by_expert(dev_i32(ids), T, k, E, g0, El, None, None, mode, H, M_cap, perm, inv, gs, None, None, ws)
+    m.moe_sort_gather_rows(dev_u8(xq), dev_f32(xscale), mode, inv, T, k, H, M_cap, xs, ss, ws)
+    assert m.moe_debug_check(ws) == 0 and one["err"] == 0
+    assert_bits_equal(host(xs), one["xs"], "gathered rows")
+    if row:
+        assert_bits_equal(host(ss), one["ss"], "gathered scales")
+    for key, v in (("perm", perm), ("inv_pos", inv), ("group_sizes", gs)):
+        assert_bits_equal(host(v), one[key], key)
+    o = sort_by_expert(ids, E, g0, El, xq=xq, xscale=xscale, xscale_mode=mode, m_cap=M_cap)
+    assert_bits_equal(host(xs), o["xs"], "oracle rows")
