@@ -610,6 +610,9 @@ def main():
                     help="seconds of untimed steps before each timed region (clock ramp; 0 to skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (profiler byte-counter calibration)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated names of the other workloads to run alone (no line of record), "
+                         "e.g. moe_backward; for profiling one workload")
     a = ap.parse_args()
     SETTLE_S = a.settle_s
     if a.gpus != 1:
@@ -626,6 +629,28 @@ def main():
             torch.add(src, 0.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    secondaries = (("gated_ffn_fwd", lambda: secondary_forward(2, a.steps, a.warmup)),
+                   ("gated_ffn_fwd_cold", lambda: rotating_forward(2, a.steps, a.warmup)),
+                   ("moe_backward", lambda: secondary_backward(min(a.steps, 50), a.warmup)),
+                   ("gated_ffn_backward", lambda: secondary_ffn_backward(a.steps, a.warmup)),
+                   ("tiny_up_proj", lambda: secondary_forward(1, a.steps, a.warmup)),
+                   ("tiny_zipf_blockwise", lambda: secondary_forward(3, a.steps, a.warmup)),
+                   ("tiny_zipf_blockwise_static", lambda: secondary_forward(3, a.steps, a.warmup, True)),
+                   ("skewed_large_blockwise", lambda: secondary_forward(6, a.steps, a.warmup)),
+                   ("skewed_large_blockwise_static", lambda: secondary_forward(6, a.steps, a.warmup, True)))
+    if a.only:
+        names = a.only.split(",")
+        unknown = sorted(set(names) - {k for k, _ in secondaries})
+        if unknown:
+            print(f"bench.py: unknown workload(s) {unknown}", file=sys.stderr)
+            sys.exit(2)
+        sec = {}
+        for key, fn in secondaries:
+            if key in names:
+                print(f"bench: {key} alone", file=sys.stderr, flush=True)
+                sec[key] = fn()
+        print(json.dumps({"only": names, "steps": a.steps, "warmup": a.warmup, "secondary": sec}), flush=True)
+        return
     print(f"bench: config {a.config}, {a.steps} timed steps after {a.warmup}", file=sys.stderr, flush=True)
     path, data = forward_path(a.config)
     cfg = path.cfg
@@ -634,6 +659,8 @@ def main():
     head, durs, acc = measure_forward(path, a.steps, a.warmup)
     dominant = "gmm_wi_01" if cfg.pipeline == "ffn" else "gmm_w_up"
     roof = roofline(durs[dominant], acc[dominant])
+    if a.config != 4:
+        roof["traffic"] = None     # the committed counter summary covers config 4's dominant launch
     int8 = None
     if not a.no_secondary and cfg.pipeline == "ffn" and cfg.weight_block_k and cfg.weight_block_n > 1:
         print("bench: int8 grouped matmuls", file=sys.stderr, flush=True)
@@ -660,15 +687,7 @@ def main():
     }
     if not a.no_secondary:
         sec = {}
-        for key, fn in (("gated_ffn_fwd", lambda: secondary_forward(2, a.steps, a.warmup)),
-                        ("gated_ffn_fwd_cold", lambda: rotating_forward(2, a.steps, a.warmup)),
-                        ("moe_backward", lambda: secondary_backward(min(a.steps, 50), a.warmup)),
-                        ("gated_ffn_backward", lambda: secondary_ffn_backward(a.steps, a.warmup)),
-                        ("tiny_up_proj", lambda: secondary_forward(1, a.steps, a.warmup)),
-                        ("tiny_zipf_blockwise", lambda: secondary_forward(3, a.steps, a.warmup)),
-                        ("tiny_zipf_blockwise_static", lambda: secondary_forward(3, a.steps, a.warmup, True)),
-                        ("skewed_large_blockwise", lambda: secondary_forward(6, a.steps, a.warmup)),
-                        ("skewed_large_blockwise_static", lambda: secondary_forward(6, a.steps, a.warmup, True))):
+        for key, fn in secondaries:
             print(f"bench: secondary {key}", file=sys.stderr, flush=True)
             sec[key] = fn()
         if int8 is not None:
