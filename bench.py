@@ -451,7 +451,9 @@ def secondary_backward(steps, warmup, nsets=3):
 
 def secondary_ffn_backward(steps, warmup):
     """The gated FFN's whole backward after a config-2 forward step: every
-    call timed eagerly with HIP events, then the backward step as a graph."""
+    call timed eagerly with HIP events, then the backward step as a graph.
+    dW01's x is gathered by the forward's sort into the weight-gradient
+    product's transposed layout."""
     from moe_fp8_grouped_amd.pipeline import FFNBackwardPath
     path, data = forward_path(2)
     weights = dict(data["weights"])
@@ -461,7 +463,7 @@ def secondary_ffn_backward(steps, warmup):
     path.step()
     g = torch.Generator(device="cuda").manual_seed(99)
     dout = (torch.randn((T, H), generator=g, device="cuda") * 1e-2).to(torch.bfloat16)
-    b = FFNBackwardPath(path, {"weights": weights}, dout)
+    b = FFNBackwardPath(path, {"weights": weights}, dout, transposed_x=True)
     del weights
     names = ("combine_backward", "quantize_dy", "grad_h", "grad_wo", "silu_backward", "quantize_dab",
              "grad_x_sorted", "grad_w01", "grad_x")

@@ -344,11 +344,14 @@ class FFNBackwardPath:
     scales serve the gmm inputs).  Weight gradients come out in float32
     ([E, I, H] for wo, [E, H, 2I] for [W0 | W1])."""
 
-    def __init__(self, fwd, data, dout: torch.Tensor, device="cuda", fuse_dy_quant=True):
+    def __init__(self, fwd, data, dout: torch.Tensor, device="cuda", fuse_dy_quant=True, transposed_x=False):
         cfg = fwd.cfg
         assert cfg.pipeline == "ffn"
         # dy's per-row quantization formed by the combine backward (True) or as a pass of its own
         self.fuse_dy_quant = fuse_dy_quant
+        # transposed_x: dW01's x as [T, H] codes with one tensor scale, gathered by the forward's sort
+        # straight into the weight-gradient product's transposed layout (no second sort, no sorted x rows)
+        self.transposed_x = bool(transposed_x)
         T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
         self.fwd, self.cfg = fwd, cfg
         self.T, self.H, self.E, self.k, self.I = T, H, E, k, I
@@ -385,10 +388,14 @@ class FFNBackwardPath:
         self.dxs = torch.empty((Mc, H), dtype=bf, device=device)
         self.xq_t = torch.empty((T, H), dtype=u8, device=device)
         self.xs_scale = torch.empty((1,), dtype=f32, device=device)
-        self.perm = torch.empty(T * k, dtype=torch.int32, device=device)
-        self.inv_pos = torch.empty(T * k, dtype=torch.int32, device=device)
-        self.group_sizes = torch.empty(E, dtype=torch.int32, device=device)
-        self.xs_t = torch.empty((Mc, H), dtype=u8, device=device)
+        if self.transposed_x:
+            self.xt = torch.empty((H, tgmm_xt_cols(Mc, E)), dtype=u8, device=device)
+            self.ws_xt = workspace(MOE_OP_GATHER_REDUCE, device=device)
+        else:
+            self.perm = torch.empty(T * k, dtype=torch.int32, device=device)
+            self.inv_pos = torch.empty(T * k, dtype=torch.int32, device=device)
+            self.group_sizes = torch.empty(E, dtype=torch.int32, device=device)
+            self.xs_t = torch.empty((Mc, H), dtype=u8, device=device)
         self.dw01 = torch.empty((cfg.E_loc, H, 2 * I), dtype=f32, device=device)
         self.dx = torch.empty((T, H), dtype=bf, device=device)
         C = max(H, 2 * I)
@@ -456,6 +463,18 @@ class FFNBackwardPath:
 
     def grad_w01(self):
         f, T, H = self.fwd, self.T, self.H
+        if self.transposed_x:
+            if f.fused_quantize and f.act_mode == MOE_SCALE_ROW_DYNAMIC:   # the scale from the forward's maxima
+                moe_quantize_rows(f.x, None, MOE_ACT_NONE, T, H, MOE_SCALE_TENSOR_FROM_ROW_AMAX, 0.0, self.xq_t,
+                                  self.xs_scale, f.xamax)
+            else:
+                moe_quantize_rows(f.x, None, MOE_ACT_NONE, T, H, MOE_SCALE_TENSOR_DYNAMIC, 0.0, self.xq_t,
+                                  self.xs_scale, None, self.ws_qx)
+            moe_sort_gather_transposed(self.xq_t, MOE_E4M3FN, 1.0, T, self.k, H, f.perm, f.group_sizes, self.E,
+                                       f.g0, f.El, self.m_cap, self.xt, None, self.ws_xt)
+            moe_tgmm_fp8_xt(self.xt, self.xs_scale, 1, self.dabq_t, self.dabs_t, 1, f.group_sizes, self.E, f.g0,
+                            f.El, self.m_cap, H, 2 * self.I, MOE_F32, self.dw01, self.ws_tgmm_01)
+            return
         if f.fused_quantize and f.act_mode == MOE_SCALE_ROW_DYNAMIC:
             # x with one tensor scale (from the token maxima the forward's fused pass wrote), quantized
             # straight into the sorted rows
@@ -484,9 +503,11 @@ class FFNBackwardPath:
         self.grad_w01()
         self.grad_x()
 
-    OUTPUTS = ("dy", "dw_router", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax", "dh", "hq_t", "hs_t", "dwo", "dab",
-               "dabq_r", "dabs_r", "dabq_t", "dabs_t", "dab_amax", "dxs", "xs_scale", "perm", "inv_pos",
-               "group_sizes", "xs_t", "dw01", "dx")
+    @property
+    def OUTPUTS(self):
+        x_out = ("xq_t", "xt") if self.transposed_x else ("perm", "inv_pos", "group_sizes", "xs_t")
+        return (("dy", "dw_router", "dyq_r", "dys_r", "dyq_t", "dys_t", "dy_amax", "dh", "hq_t", "hs_t", "dwo", "dab",
+                 "dabq_r", "dabs_r", "dabq_t", "dabs_t", "dab_amax", "dxs", "xs_scale") + x_out + ("dw01", "dx"))
 
     def capture_graph(self, warmup=1):
         """Record one backward step into a HIP graph (every buffer it writes is

@@ -304,8 +304,10 @@ def _full_tgmm(x, xs, d, ds, gs, El, got, what):
               model=lambda idx: tgmm_samples(x, xs, d, ds, gs, 0, El, idx // (K * N), (idx // N) % K, idx % N))
 
 
-@pytest.mark.parametrize("shape,fuse", [("small", True), ("small", False), ("config2", True)])
-def test_gated_ffn_backward_stagewise(shape, fuse):
+@pytest.mark.parametrize("shape,fuse,transposed", [("small", True, False), ("small", False, False),
+                                                   ("small", True, True), ("config2", True, False),
+                                                   ("config2", True, True)])
+def test_gated_ffn_backward_stagewise(shape, fuse, transposed):
     """The gated FFN's backward after a forward step, every stage against the
     oracle fed the GPU's own inputs for that stage: the combine backward, the
     quantizations and the activation backward bit-exact, the grouped matmuls
@@ -316,12 +318,14 @@ def test_gated_ffn_backward_stagewise(shape, fuse):
     fwd = ForwardPath(cfg, data)
     rng = np.random.default_rng(77)
     dout_bits = to_bf16_bits((rng.standard_normal((T, H)) * 1e-2).astype(np.float32))
-    bwd = FFNBackwardPath(fwd, data, dev_bf16(dout_bits), fuse_dy_quant=fuse)
-    print(f"gated ffn backward {shape} fuse_dy_quant={fuse} T={T} H={H} E={E} k={k} I={I}", flush=True)
+    bwd = FFNBackwardPath(fwd, data, dev_bf16(dout_bits), fuse_dy_quant=fuse, transposed_x=transposed)
+    print(f"gated ffn backward {shape} fuse_dy_quant={fuse} transposed_x={transposed} T={T} H={H} E={E} k={k} I={I}",
+          flush=True)
     fwd.step()
     bwd.step()
     torch.cuda.synchronize()
-    for ws in (bwd.ws_q, bwd.ws_qx, bwd.ws_sort, bwd.ws_gmm_h, bwd.ws_gmm_x, bwd.ws_tgmm_o, bwd.ws_tgmm_01):
+    for ws in (bwd.ws_q, bwd.ws_qx, bwd.ws_sort, bwd.ws_gmm_h, bwd.ws_gmm_x, bwd.ws_tgmm_o, bwd.ws_tgmm_01) + \
+            ((bwd.ws_xt,) if transposed else ()):
         assert m.moe_debug_check(ws) == 0
     inv = host(fwd.inv_pos).reshape(T, k)
     gs = host(fwd.group_sizes)
@@ -380,7 +384,13 @@ def test_gated_ffn_backward_stagewise(shape, fuse):
     assert_bits_equal(host(fwd.xamax), xam, "x token maxima (forward's fused pass)")
     assert_bits_equal(host(bwd.xs_scale), xsc, "x tensor scale")
     srt = sort_by_expert(data["ids"], E, 0, E, xq=xq, xscale=xsc, xscale_mode=SCALE_TENSOR_DYNAMIC, m_cap=Mc)
-    assert_bits_equal(host(bwd.xs_t), srt["xs"], "x sorted")
+    if transposed:   # [T, H] codes, then the forward's sort gathers them into the product's layout
+        assert_bits_equal(host(bwd.xq_t), xq, "x tensor codes")
+        used = int(np.sum((gs.astype(np.int64) + 127) // 128)) * 128
+        want = expected_xt(srt["xs"], gs, 0, E, Mc, E)
+        assert_bits_equal(host(bwd.xt)[:, :used], want[:, :used], "x in the product's layout")
+    else:
+        assert_bits_equal(host(bwd.xs_t), srt["xs"], "x sorted")
     _full_tgmm(srt["xs"], xsc, q2t, s2t, gs, E, host(bwd.dw01), f"{shape} dw01")
     # dx: unit-weight un-sort of dxs
     o = gather_reduce(dxs, True, inv, np.ones((T, k), np.float32))
@@ -425,11 +435,13 @@ def test_expert_slice_with_no_routed_rows_forward_and_backward():
     assert_bits_equal(host(fwd.hs), hs, "hs")
     assert (hs == 1.0).all()
     dout = dev_bf16(to_bf16_bits(rng.standard_normal((cfg.T, cfg.H)).astype(np.float32)))
-    bwd = FFNBackwardPath(fwd, data, dout)
-    bwd.step()
-    torch.cuda.synchronize()
-    for name in ("dy", "dw_router", "dh", "dwo", "dab", "dxs", "dw01", "dx"):
-        assert not host(getattr(bwd, name)).any(), name
+    for transposed in (False, True):
+        bwd = FFNBackwardPath(fwd, data, dout, transposed_x=transposed)
+        bwd.dw01.fill_(7.0)
+        bwd.step()
+        torch.cuda.synchronize()
+        for name in ("dy", "dw_router", "dh", "dwo", "dab", "dxs", "dw01", "dx"):
+            assert not host(getattr(bwd, name)).any(), (name, transposed)
     q2, s2, _ = quantize_rows(host(bwd.dab), SCALE_ROW_DYNAMIC)
     assert_bits_equal(host(bwd.dabq_r), q2, "[da|db] row q")
     assert_bits_equal(host(bwd.dabs_r), s2, "[da|db] row scale")
@@ -438,21 +450,25 @@ def test_expert_slice_with_no_routed_rows_forward_and_backward():
     assert_bits_equal(host(bwd.dabs_t), s2t, "[da|db] tensor scale")
 
 
-def test_gated_ffn_backward_hip_graph_replays_match_eager():
+@pytest.mark.parametrize("transposed", [False, True])
+def test_gated_ffn_backward_hip_graph_replays_match_eager(transposed):
     """The backward step as a HIP graph: every replay, with scribbled outputs
     and eager steps between replays, leaves the eager step's bits in every
-    buffer the step writes."""
+    buffer the step writes (of the transposed x layout: the columns up to the
+    last group's padded end, all the product reads)."""
     cfg = scaled_config(2, T=384, H=512, E=8, k=2, I=256)
     data = generate(cfg)
     fwd = ForwardPath(cfg, data)
     rng = np.random.default_rng(5)
     dout = dev_bf16(to_bf16_bits((rng.standard_normal((cfg.T, cfg.H)) * 1e-2).astype(np.float32)))
-    bwd = FFNBackwardPath(fwd, data, dout)
-    print("gated ffn backward graph replays", flush=True)
+    bwd = FFNBackwardPath(fwd, data, dout, transposed_x=transposed)
+    print(f"gated ffn backward graph replays transposed_x={transposed}", flush=True)
     fwd.step()
     bwd.step()
     torch.cuda.synchronize()
-    ref = {k: getattr(bwd, k).clone() for k in bwd.OUTPUTS}
+    used = int(((host(fwd.group_sizes).astype(np.int64) + 127) // 128).sum()) * 128
+    view = lambda k: getattr(bwd, k)[:, :used] if k == "xt" else getattr(bwd, k)
+    ref = {k: view(k).clone() for k in bwd.OUTPUTS}
     bwd.capture_graph(warmup=1)
     for rep in range(3):
         for k in bwd.OUTPUTS:
@@ -461,7 +477,7 @@ def test_gated_ffn_backward_hip_graph_replays_match_eager():
         bwd.replay()
         torch.cuda.synchronize()
         for k in bwd.OUTPUTS:
-            assert torch.equal(getattr(bwd, k).view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+            assert torch.equal(view(k).view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
         bwd.step()
         torch.cuda.synchronize()
 
