@@ -714,6 +714,7 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
           else
             b[j] = frag_tr_swz(Bs + (n0 >> 7) * (128 * G_BK), n0 & 127, lane);
         }
+        v4f pp[JN];          // KBLOCKS: the previous round's block products
         // MI rounds: an A fragment, this round's share of the loads of step ks,
         // then the round's MFMAs -- so memory back-pressure on the loads never
         // holds up a long run of MFMA issue
@@ -741,23 +742,46 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
               __builtin_amdgcn_global_load_lds(rs_lane + static_cast<int64_t>((kofs + ks) / steps_per_block) * Nb,
                                                (lds_void*)(nxt + C::SC_OFF + w4 * 256), 4, 0, 0);
           }
+          v4f pc[JN];
 #pragma unroll
           for (int j = 0; j < JN; ++j) {
             if (KBLOCKS) {
-              v4f p;
               if constexpr (I8)
-                p = __builtin_convertvector(mfma_i8x2(b[j], a, v4i32{0, 0, 0, 0}), v4f);   // exact: |p| < 2^24
+                pc[j] = __builtin_convertvector(mfma_i8x2(b[j], a, v4i32{0, 0, 0, 0}), v4f);   // exact: |p| < 2^24
               else
-                p = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
-              acc[i][j][0] = fmaf(s_col[j].x, p[0], acc[i][j][0]);
-              acc[i][j][1] = fmaf(s_col[j].y, p[1], acc[i][j][1]);
-              acc[i][j][2] = fmaf(s_col[j].z, p[2], acc[i][j][2]);
-              acc[i][j][3] = fmaf(s_col[j].w, p[3], acc[i][j][3]);
+                pc[j] = mfma_f8(b[j], a, v4f{0.f, 0.f, 0.f, 0.f});
             } else if constexpr (I8) {      // the int32 sums live in the accumulator's registers
               acc[i][j] = __builtin_bit_cast(v4f, mfma_i8x2(b[j], a, __builtin_bit_cast(v4i32, acc[i][j])));
             } else {
               acc[i][j] = mfma_f8(b[j], a, acc[i][j]);
             }
+          }
+          // Blockwise scales: the previous round's block products are folded while this round's MFMAs run.
+          // The empty asm reads the folded accumulators, so the fold stays in this round (it is ordered
+          // against the round's direct loads); left free, the compiler moves every fold to the end of the
+          // step, which keeps all sixteen products live (a spill) and leaves the matrix cores idle there.
+          if (KBLOCKS) {
+            if (i > 0) {
+#pragma unroll
+              for (int j = 0; j < JN; ++j) {
+                acc[i - 1][j][0] = fmaf(s_col[j].x, pp[j][0], acc[i - 1][j][0]);
+                acc[i - 1][j][1] = fmaf(s_col[j].y, pp[j][1], acc[i - 1][j][1]);
+                acc[i - 1][j][2] = fmaf(s_col[j].z, pp[j][2], acc[i - 1][j][2]);
+                acc[i - 1][j][3] = fmaf(s_col[j].w, pp[j][3], acc[i - 1][j][3]);
+              }
+              asm volatile("" ::"v"(acc[i - 1][0]), "v"(acc[i - 1][1]), "v"(acc[i - 1][2]), "v"(acc[i - 1][3]));
+            }
+#pragma unroll
+            for (int j = 0; j < JN; ++j) pp[j] = pc[j];
+          }
+        }
+        if (KBLOCKS) {
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            acc[MI - 1][j][0] = fmaf(s_col[j].x, pp[j][0], acc[MI - 1][j][0]);
+            acc[MI - 1][j][1] = fmaf(s_col[j].y, pp[j][1], acc[MI - 1][j][1]);
+            acc[MI - 1][j][2] = fmaf(s_col[j].z, pp[j][2], acc[MI - 1][j][2]);
+            acc[MI - 1][j][3] = fmaf(s_col[j].w, pp[j][3], acc[MI - 1][j][3]);
           }
         }
         if constexpr (AB) {
