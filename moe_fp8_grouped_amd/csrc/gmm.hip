@@ -700,11 +700,8 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
         const uint8_t* As = smem + (kt % NST) * STAGE;
         const uint8_t* Bs = As + bm_t * G_BK;
         float4 s_col[JN];    // scales of this lane's output columns 16j + 4(l/16) .. +3
-        if (KBLOCKS) {
-          const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + 4 * (lane >> 4);
-          static_assert(JN == 4, "four column groups per scale read");
-          lds_read_4x16f(sc, s_col);
-        }
+        const float* sc = reinterpret_cast<const float*>(As + C::SC_OFF) + cbase + 4 * (lane >> 4);
+        static_assert(JN == 4, "four column groups per scale read");
         v8i b[JN];
 #pragma unroll
         for (int j = 0; j < JN; ++j) {
@@ -760,6 +757,12 @@ __global__ __launch_bounds__(C::THREADS) void gmm_kernel(const uint8_t* __restri
           // The empty asm reads the folded accumulators, so the fold stays in this round (it is ordered
           // against the round's direct loads); left free, the compiler moves every fold to the end of the
           // step, which keeps all sixteen products live (a spill) and leaves the matrix cores idle there.
+          // the scales are read once round 0's MFMAs are issued: the first fold needs them only in round 1,
+          // so the step's start waits for one LDS round trip (the fragments), not two
+          if (KBLOCKS && i == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            lds_read_4x16f(sc, s_col);
+          }
           if (KBLOCKS) {
             if (i > 0) {
 #pragma unroll
